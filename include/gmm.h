@@ -1,0 +1,131 @@
+/*
+ * gmm.h — C-ABI of libgmm_mi355x.so: the fused Gaussian-mixture EM E-step for
+ * MI355X (gfx950), with its M-step, EM loop and top-2 assignment.
+ *
+ * The operation (pages: "Turbo-GMM: FlashAttention-Inspired GPU-Accelerated
+ * Gaussian Mixture Model", abstract; "Flash-GMM: a memory-efficient kernel for
+ * scalable soft clustering", abstract): EM for a Gaussian mixture scores N
+ * points against K components, normalises each point's responsibilities with
+ * a log-sum-exp, and accumulates the sufficient statistics, without writing
+ * the N x K responsibility matrix to memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array pointer is a DEVICE pointer owned by the caller. The library
+ *   allocates no device memory of its own: scratch comes from `workspace`,
+ *   which must hold at least gmm_workspace_bytes(N, d, K) bytes and be
+ *   256-byte aligned (any hipMalloc / torch allocation is).
+ * - Layouts are row-major and dense: X is N x d (x_dtype GMM_F32 = float,
+ *   GMM_F16 = IEEE half), mu and var are K x d float, logw is K float,
+ *   Sx and Sxx are K x d float, Nk is K float.
+ * - The mixture is diagonal: component k has mean mu[k], variance var[k]
+ *   (per feature, > 0) and log mixing weight logw[k] (-inf allowed; at least
+ *   one component must be finite).
+ * - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *   enqueues work on it and never synchronises; outputs are valid once the
+ *   stream has completed. Calls that share a workspace must be ordered on
+ *   one stream.
+ * - Return value: GMM_OK (0) or a negative GMM_E* code. Arguments are checked
+ *   on the host before anything is enqueued: a rejected call enqueues nothing
+ *   and touches no device memory. gmm_error_string() names each code.
+ * - Limits: 1 <= d <= 128, 1 <= K <= 65536, 0 <= N < 2^40.
+ * - Non-finite inputs (NaN X, var <= 0) are not checked on the device; they
+ *   propagate into the outputs as NaN/Inf.
+ */
+#ifndef GMM_MI355X_H
+#define GMM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gmm_status {
+  GMM_OK = 0,
+  GMM_EINVAL = -1,        /* null pointer, negative size, bad dtype or regime */
+  GMM_EUNSUPPORTED = -2,  /* shape beyond the limits above, or regime not possible */
+  GMM_EWORKSPACE = -3,    /* workspace NULL, too small or misaligned */
+  GMM_EHIP = -4           /* a HIP launch failed (see hipGetLastError) */
+};
+
+enum gmm_dtype { GMM_F32 = 0, GMM_F16 = 1 };
+
+/* Regime of the E-step (Turbo-GMM abstract: a single sweep over the component
+ * axis kept on chip when it fits, a two-pass fallback otherwise). AUTO takes
+ * the single sweep for K <= 256 and two passes above. */
+enum gmm_regime { GMM_REGIME_AUTO = 0, GMM_REGIME_SINGLE = 1, GMM_REGIME_TWOPASS = 2 };
+
+/* Library version, major*10000 + minor*100 + patch. */
+int gmm_version(void);
+
+/* Static text for a status code. */
+const char* gmm_error_string(int code);
+
+/* Workspace bytes needed by every entry point below for this (N, d, K).
+ * Returns 0 for arguments outside the limits. */
+size_t gmm_workspace_bytes(int64_t N, int32_t d, int32_t K);
+
+/* E-step with sufficient statistics (Turbo-GMM abstract: responsibility
+ * normalisation and sufficient-statistic accumulation; Flash-GMM abstract:
+ * no materialised responsibility matrix).
+ *   s_nk = logw_k + log N(x_n | mu_k, diag var_k)
+ *   l_n  = log sum_k exp(s_nk)          (per-point log-likelihood)
+ *   r_nk = exp(s_nk - l_n)
+ *   Nk[k] = sum_n r_nk,  Sx[k][j] = sum_n r_nk x_nj,  Sxx[k][j] = sum_n r_nk x_nj^2
+ *   *loglik_total = sum_n l_n (device double)
+ * loglik_point (nullable) receives l_n as N floats. N = 0 gives zero stats and
+ * a zero log-likelihood. Outputs are fully overwritten. */
+int gmm_estep_stats(const void* X, int32_t x_dtype, int64_t N, int32_t d,
+                    const float* mu, const float* var, const float* logw, int32_t K,
+                    float* Nk, float* Sx, float* Sxx,
+                    double* loglik_total, float* loglik_point,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/* gmm_estep_stats with the regime forced (GMM_REGIME_SINGLE needs K <= 256). */
+int gmm_estep_stats_regime(const void* X, int32_t x_dtype, int64_t N, int32_t d,
+                           const float* mu, const float* var, const float* logw, int32_t K,
+                           float* Nk, float* Sx, float* Sxx,
+                           double* loglik_total, float* loglik_point,
+                           void* workspace, size_t ws_bytes, int32_t regime, void* stream);
+
+/* Testing aid: materialises R (N x K floats, row-major) through the same
+ * scoring and normalisation code as gmm_estep_stats in the given regime, so
+ * responsibilities can be checked element by element on small N. The
+ * statistics are computed too and discarded; loglik_point is nullable. */
+int gmm_estep_resp(const void* X, int32_t x_dtype, int64_t N, int32_t d,
+                   const float* mu, const float* var, const float* logw, int32_t K,
+                   float* R, float* loglik_point,
+                   void* workspace, size_t ws_bytes, int32_t regime, void* stream);
+
+/* M-step for diagonal covariance (the EM update the Turbo-GMM abstract
+ * alternates with the E-step), in double precision:
+ *   w_k = Nk/N,  mu_k = Sx_k/Nk,  var_k = max(Sxx_k/Nk - mu_k^2, var_floor)
+ * mu, var, logw are in/out. A component with Nk < 1e-12*N keeps its mu and
+ * var; its logw becomes log(max(Nk, 1e-300)/N). Needs N >= 1, var_floor >= 0. */
+int gmm_mstep(const float* Nk, const float* Sx, const float* Sxx, int64_t N, int32_t d, int32_t K,
+              float var_floor, float* mu, float* var, float* logw, void* stream);
+
+/* `iters` EM iterations on the device: E-step (AUTO regime) then M-step, all
+ * enqueued on `stream` with nothing read back. loglik_hist (device, `iters`
+ * doubles) receives the log-likelihood of the parameters before each M-step.
+ * mu, var, logw are in/out. Needs N >= 1, iters >= 0. */
+int gmm_em_iterate(const void* X, int32_t x_dtype, int64_t N, int32_t d, int32_t K, int32_t iters,
+                   float var_floor, float* mu, float* var, float* logw, double* loglik_hist,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Top-2 assignment for border-vector multi-assignment (Flash-GMM abstract:
+ * responsibilities assign border vectors to several clusters). For each point:
+ * idx[n][0], idx[n][1] = the two components with the largest s_nk (ties go to
+ * the lower index) and resp[n][.] = their r_nk, normalised over all K. With
+ * K = 1, idx[n][1] = -1 and resp[n][1] = 0. idx is N x 2 int32, resp N x 2 float. */
+int gmm_assign_top2(const void* X, int32_t x_dtype, int64_t N, int32_t d,
+                    const float* mu, const float* var, const float* logw, int32_t K,
+                    int32_t* idx, float* resp, void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GMM_MI355X_H */

@@ -1,0 +1,231 @@
+// C-ABI of libgmm_mi355x.so: argument checks, workspace planning and dispatch.
+// Every check runs on the host before anything is enqueued; a rejected call
+// touches neither the device nor the caller's buffers.
+#include "../../include/gmm.h"
+
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "gmm_internal.hpp"
+
+namespace gmm {
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static int pow2_waves(int K) {
+  int w = 1;
+  while (w * 32 < K) w <<= 1;
+  return w;
+}
+
+int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
+  if (N < 0 || d < 1 || K < 1) return GMM_EINVAL;
+  if (d > kMaxD || K > kMaxK || N >= ((int64_t)1 << 40)) return GMM_EUNSUPPORTED;
+  if (regime < GMM_REGIME_AUTO || regime > GMM_REGIME_TWOPASS) return GMM_EINVAL;
+  if (regime == GMM_REGIME_AUTO) regime = K <= kSingleMaxK ? GMM_REGIME_SINGLE : GMM_REGIME_TWOPASS;
+  if (regime == GMM_REGIME_SINGLE && K > kSingleMaxK) return GMM_EUNSUPPORTED;
+
+  Plan p{};
+  p.N = N;
+  p.d = d;
+  p.K = K;
+  p.DT = (d + 31) / 32;
+  p.DP = 32 * p.DT;
+  p.regime = regime;
+  if (K <= kSingleMaxK) {
+    p.waves = pow2_waves(K);
+    p.kslabs = 1;
+  } else {
+    p.waves = kSlabWaves;
+    p.kslabs = (int)ceil_div(K, 32 * kSlabWaves);
+  }
+  p.Kp = 32 * p.waves * p.kslabs;
+  p.Kp16 = (int)ceil_div(K, 16) * 16;
+  p.E = 1 + 2 * p.DP;
+  p.tiles = ceil_div(N, kTileN);
+  // Row chunks: one statistics partial per chunk. Aim for one resident block
+  // per SIMD-set (8 waves per CU) across 256 CUs.
+  int64_t target = p.kslabs > 1 ? std::max<int64_t>(1, 256 / p.kslabs)
+                                 : 256 * std::max(1, 8 / p.waves);
+  target = std::max<int64_t>(1, std::min<int64_t>(target, p.tiles));
+  p.rows_per_chunk = ceil_div(std::max<int64_t>(p.tiles, 1), target) * kTileN;
+  p.P = N == 0 ? 0 : ceil_div(N, p.rows_per_chunk);
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_W32p = take((size_t)p.Kp * 2 * p.DP * sizeof(float));
+  const size_t o_c32 = take((size_t)p.Kp * sizeof(float));
+  const size_t o_W64p = take((size_t)p.Kp16 * 2 * p.DP * sizeof(double));
+  const size_t o_c64e = take((size_t)p.Kp16 * sizeof(double));
+  const size_t o_iv64 = take((size_t)K * d * sizeof(double));
+  const size_t o_c64d = take((size_t)K * sizeof(double));
+  const size_t o_cmax = take((size_t)K * 3 * sizeof(float));
+  const size_t o_errc = take(4 * sizeof(float));
+  const size_t o_rowref = take((size_t)std::max<int64_t>(N, 1) * sizeof(float2));
+  const size_t o_part = take((size_t)std::max<int64_t>(p.P, 1) * p.Kp * p.E * sizeof(float));
+  const size_t o_ll = take((size_t)std::max<int64_t>(std::max(p.P, p.tiles), 1) * sizeof(double));
+  const size_t o_stats = take((size_t)K * (1 + 2 * d) * sizeof(float));
+  p.bytes = off;
+  if (base) {
+    char* b = static_cast<char*>(base);
+    p.ws.W32p = reinterpret_cast<float*>(b + o_W32p);
+    p.ws.c32 = reinterpret_cast<float*>(b + o_c32);
+    p.ws.W64p = reinterpret_cast<double*>(b + o_W64p);
+    p.ws.c64e = reinterpret_cast<double*>(b + o_c64e);
+    p.ws.iv64 = reinterpret_cast<double*>(b + o_iv64);
+    p.ws.c64d = reinterpret_cast<double*>(b + o_c64d);
+    p.ws.compmax = reinterpret_cast<float*>(b + o_cmax);
+    p.ws.errc = reinterpret_cast<float*>(b + o_errc);
+    p.ws.rowref = reinterpret_cast<float2*>(b + o_rowref);
+    p.ws.partials = reinterpret_cast<float*>(b + o_part);
+    p.ws.llpart = reinterpret_cast<double*>(b + o_ll);
+    p.ws.stats = reinterpret_cast<float*>(b + o_stats);
+  }
+  *plan = p;
+  return GMM_OK;
+}
+
+static size_t workspace_bytes(int64_t N, int d, int K) {
+  size_t best = 0;
+  for (int r = GMM_REGIME_SINGLE; r <= GMM_REGIME_TWOPASS; ++r) {
+    Plan p;
+    if (make_plan(N, d, K, r, nullptr, &p) == GMM_OK) best = std::max(best, p.bytes);
+  }
+  return best;
+}
+
+static int check_ws(void* ws, size_t ws_bytes, int64_t N, int d, int K) {
+  if (!ws) return GMM_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return GMM_EWORKSPACE;
+  if (ws_bytes < workspace_bytes(N, d, K)) return GMM_EWORKSPACE;
+  return GMM_OK;
+}
+
+static int check_common(const void* X, int32_t xt, int64_t N, int32_t d, int32_t K, const float* mu,
+                        const float* var, const float* logw) {
+  if (xt != GMM_F32 && xt != GMM_F16) return GMM_EINVAL;
+  if (N < 0 || d < 1 || K < 1) return GMM_EINVAL;
+  if (d > kMaxD || K > kMaxK || N >= ((int64_t)1 << 40)) return GMM_EUNSUPPORTED;
+  if ((N > 0 && !X) || !mu || !var || !logw) return GMM_EINVAL;
+  return GMM_OK;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? GMM_OK : GMM_EHIP; }
+
+}  // namespace gmm
+
+using namespace gmm;
+
+extern "C" {
+
+int gmm_version(void) { return 10000; }
+
+const char* gmm_error_string(int code) {
+  switch (code) {
+    case GMM_OK: return "ok";
+    case GMM_EINVAL: return "invalid argument (null pointer, negative size, bad dtype or regime)";
+    case GMM_EUNSUPPORTED: return "unsupported shape or regime (1<=d<=128, 1<=K<=65536; single sweep needs K<=256)";
+    case GMM_EWORKSPACE: return "workspace missing, misaligned (256 B) or smaller than gmm_workspace_bytes()";
+    case GMM_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t gmm_workspace_bytes(int64_t N, int32_t d, int32_t K) {
+  if (N < 0 || d < 1 || K < 1 || d > kMaxD || K > kMaxK || N >= ((int64_t)1 << 40)) return 0;
+  return workspace_bytes(N, d, K);
+}
+
+int gmm_estep_stats_regime(const void* X, int32_t x_dtype, int64_t N, int32_t d, const float* mu,
+                           const float* var, const float* logw, int32_t K, float* Nk, float* Sx, float* Sxx,
+                           double* loglik_total, float* loglik_point, void* workspace, size_t ws_bytes,
+                           int32_t regime, void* stream) {
+  int st = check_common(X, x_dtype, N, d, K, mu, var, logw);
+  if (st) return st;
+  if (!Nk || !Sx || !Sxx || !loglik_total) return GMM_EINVAL;
+  if ((st = check_ws(workspace, ws_bytes, N, d, K))) return st;
+  Plan p;
+  if ((st = make_plan(N, d, K, regime, workspace, &p))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) return hip_status(launch_zero_outputs(Nk, Sx, Sxx, d, K, loglik_total, s));
+  hipError_t e = launch_precompute(p, mu, var, logw, s);
+  if (e == hipSuccess) e = launch_estep(p, X, x_dtype, mu, Nk, Sx, Sxx, loglik_total, loglik_point, nullptr, s);
+  return hip_status(e);
+}
+
+int gmm_estep_stats(const void* X, int32_t x_dtype, int64_t N, int32_t d, const float* mu, const float* var,
+                    const float* logw, int32_t K, float* Nk, float* Sx, float* Sxx, double* loglik_total,
+                    float* loglik_point, void* workspace, size_t ws_bytes, void* stream) {
+  return gmm_estep_stats_regime(X, x_dtype, N, d, mu, var, logw, K, Nk, Sx, Sxx, loglik_total, loglik_point,
+                                workspace, ws_bytes, GMM_REGIME_AUTO, stream);
+}
+
+int gmm_estep_resp(const void* X, int32_t x_dtype, int64_t N, int32_t d, const float* mu, const float* var,
+                   const float* logw, int32_t K, float* R, float* loglik_point, void* workspace, size_t ws_bytes,
+                   int32_t regime, void* stream) {
+  int st = check_common(X, x_dtype, N, d, K, mu, var, logw);
+  if (st) return st;
+  if (N > 0 && !R) return GMM_EINVAL;
+  if ((st = check_ws(workspace, ws_bytes, N, d, K))) return st;
+  Plan p;
+  if ((st = make_plan(N, d, K, regime, workspace, &p))) return st;
+  if (N == 0) return GMM_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_precompute(p, mu, var, logw, s);
+  if (e == hipSuccess) e = launch_estep(p, X, x_dtype, mu, nullptr, nullptr, nullptr, nullptr, loglik_point, R, s);
+  return hip_status(e);
+}
+
+int gmm_mstep(const float* Nk, const float* Sx, const float* Sxx, int64_t N, int32_t d, int32_t K,
+              float var_floor, float* mu, float* var, float* logw, void* stream) {
+  if (!Nk || !Sx || !Sxx || !mu || !var || !logw) return GMM_EINVAL;
+  if (N < 1 || d < 1 || K < 1 || !(var_floor >= 0.f)) return GMM_EINVAL;
+  if (d > kMaxD || K > kMaxK) return GMM_EUNSUPPORTED;
+  return hip_status(launch_mstep(Nk, Sx, Sxx, N, d, K, var_floor, mu, var, logw, static_cast<hipStream_t>(stream)));
+}
+
+int gmm_em_iterate(const void* X, int32_t x_dtype, int64_t N, int32_t d, int32_t K, int32_t iters,
+                   float var_floor, float* mu, float* var, float* logw, double* loglik_hist, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  int st = check_common(X, x_dtype, N, d, K, mu, var, logw);
+  if (st) return st;
+  if (N < 1 || iters < 0 || !(var_floor >= 0.f)) return GMM_EINVAL;
+  if (iters > 0 && !loglik_hist) return GMM_EINVAL;
+  if ((st = check_ws(workspace, ws_bytes, N, d, K))) return st;
+  Plan p;
+  if ((st = make_plan(N, d, K, GMM_REGIME_AUTO, workspace, &p))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* Nk = p.ws.stats;
+  float* Sx = Nk + K;
+  float* Sxx = Sx + (size_t)K * d;
+  for (int it = 0; it < iters; ++it) {
+    hipError_t e = launch_precompute(p, mu, var, logw, s);
+    if (e == hipSuccess) e = launch_estep(p, X, x_dtype, mu, Nk, Sx, Sxx, loglik_hist + it, nullptr, nullptr, s);
+    if (e == hipSuccess) e = launch_mstep(Nk, Sx, Sxx, N, d, K, var_floor, mu, var, logw, s);
+    if (e != hipSuccess) return GMM_EHIP;
+  }
+  return GMM_OK;
+}
+
+int gmm_assign_top2(const void* X, int32_t x_dtype, int64_t N, int32_t d, const float* mu, const float* var,
+                    const float* logw, int32_t K, int32_t* idx, float* resp, void* workspace, size_t ws_bytes,
+                    void* stream) {
+  int st = check_common(X, x_dtype, N, d, K, mu, var, logw);
+  if (st) return st;
+  if (N > 0 && (!idx || !resp)) return GMM_EINVAL;
+  if ((st = check_ws(workspace, ws_bytes, N, d, K))) return st;
+  Plan p;
+  if ((st = make_plan(N, d, K, GMM_REGIME_TWOPASS, workspace, &p))) return st;
+  if (N == 0) return GMM_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_precompute(p, mu, var, logw, s);
+  if (e == hipSuccess) e = launch_top2(p, X, x_dtype, idx, resp, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal declarations shared by the host API and the kernel translation unit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gmm {
+
+constexpr int kTileN = 64;           // points per tile (two 32-row MFMA blocks)
+constexpr int kCompTile = 32;        // components per wave in the fp32 kernels
+constexpr int kCompTile64 = 16;      // components per fp64 MFMA tile
+constexpr int kMaxD = 128;
+constexpr int kMaxK = 65536;
+constexpr int kSlabWaves = 8;        // waves (x32 components) per two-pass slab
+constexpr int kSingleMaxK = 256;     // largest K the single sweep keeps on chip
+constexpr int kLseWaves = 4;         // waves per block in the fp64 normaliser pass
+
+// Device pointers into the caller's workspace, filled by gmm::plan().
+struct Workspace {
+  float* W32p;      // fp32 score operands, packed for the 32x32x2 MFMA B operand
+  float* c32;       // [Kp32] expanded-form score constant (fp32), -inf for padding
+  double* W64p;     // fp64 score operands, packed for the 16x16x4 f64 MFMA A operand
+  double* c64e;     // [Kp16] expanded-form constant (fp64), -inf for padding
+  double* iv64;     // [K][d] 1/var in fp64 (exact re-score)
+  double* c64d;     // [K] difference-form constant (fp64)
+  float* compmax;   // [K][3] per-component max|A|, max|B|, |c| (error bound inputs)
+  float* errc;      // [4] a_max, b_max, c_max, 0
+  float2* rowref;   // [N] per-row (m_ref, lZ) from the fp64 pass
+  float* partials;  // [P][Kp][E] per-chunk statistics
+  double* llpart;   // [max(P, tiles)] per-block log-likelihood sums
+  float* stats;     // [K][1 + 2d] Nk | Sx | Sxx scratch for the EM loop
+};
+
+struct Plan {
+  int64_t N;
+  int d, K;
+  int DT, DP;       // DP = 32*DT >= d: padded feature count
+  int regime;       // 1 single, 2 two-pass
+  int waves;        // waves per block in the statistics kernel
+  int kslabs;       // component slabs (1 for the single sweep)
+  int Kp;           // padded K of the statistics kernel = 32*waves*kslabs
+  int Kp16;         // K rounded up to 16 (fp64 pass)
+  int64_t P;        // row chunks of the statistics kernel
+  int64_t rows_per_chunk;
+  int64_t tiles;    // ceil(N / 64)
+  int E;            // 1 + 2*DP floats per component in a partial
+  size_t bytes;     // workspace bytes this plan uses
+  Workspace ws;
+};
+
+// Fills `plan` (and the workspace pointers when base != nullptr). Returns a
+// gmm_status code; does not touch the GPU.
+int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan);
+
+// Kernel launchers (gmm_kernels.hip). All enqueue on `stream` and return a
+// hipError_t from hipGetLastError().
+hipError_t launch_precompute(const Plan& p, const float* mu, const float* var, const float* logw,
+                             hipStream_t stream);
+hipError_t launch_estep(const Plan& p, const void* X, int x_dtype, const float* mu,
+                        float* Nk, float* Sx, float* Sxx, double* loglik_total,
+                        float* loglik_point, float* R, hipStream_t stream);
+hipError_t launch_top2(const Plan& p, const void* X, int x_dtype, int32_t* idx, float* resp,
+                       hipStream_t stream);
+hipError_t launch_mstep(const float* Nk, const float* Sx, const float* Sxx, int64_t N, int d, int K,
+                        float var_floor, float* mu, float* var, float* logw, hipStream_t stream);
+hipError_t launch_zero_outputs(float* Nk, float* Sx, float* Sxx, int d, int K,
+                               double* loglik_total, hipStream_t stream);
+
+}  // namespace gmm

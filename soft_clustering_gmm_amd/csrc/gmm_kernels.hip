@@ -1,0 +1,794 @@
+// HIP kernels for the fused Gaussian-mixture EM E-step on gfx950 (MI355X).
+//
+// What is computed (Turbo-GMM abstract; Flash-GMM abstract): for N points and
+// K diagonal Gaussian components, the score s_nk = log w_k + log N(x_n|mu_k,
+// var_k), the row normaliser l_n = logsumexp_k s_nk, the responsibilities
+// r_nk = exp(s_nk - l_n) and the statistics Nk, Sx = sum r x, Sxx = sum r x^2,
+// with r kept on chip (never written to HBM).
+//
+// Score contraction. With A_kj = -1/(2 var_kj), B_kj = mu_kj/var_kj and
+// c_k = log w_k - 1/2 (d log 2pi + sum_j log var_kj + sum_j mu_kj^2/var_kj),
+//     s_nk = sum_j (A_kj x_nj^2 + B_kj x_nj) + c_k,
+// a dense (N x 2d) . (2d x K) product that runs on MFMA tiles. The inner
+// dimension interleaves x^2 and x feature by feature, so one LDS read of x
+// feeds both halves of an MFMA step.
+//
+// Precision. FP32 accumulation of the expanded form loses ~1e-4 absolute on
+// scores of magnitude ~10^2, which is too coarse for responsibilities near
+// 0.5. Each row therefore carries an a-priori bound E_n on the fp32 score
+// error; when 2 E_n / Z_n (Z_n = sum_k exp(s_nk - max)) could exceed a small
+// threshold, every component within kWindow of the row maximum is re-scored
+// exactly (fp64, difference form) before the normalisation. Components
+// outside the window have r < e^-20, so their fp32 error cannot matter.
+//
+// Regimes (Turbo-GMM abstract): the single sweep keeps the whole component
+// axis of a 64-point tile on chip (K <= 256) and does max, log-sum-exp and
+// statistics in one traversal. The two-pass fallback computes l_n first in a
+// fp64-MFMA pass (exact, so it needs no re-score), then recomputes the fp32
+// scores per 256-component slab and accumulates the statistics.
+#include "gmm_internal.hpp"
+
+#include <math.h>
+
+namespace gmm {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+constexpr double kLog2Pi = 1.83787706640934548356065947281;
+constexpr float kWindow = 20.0f;   // re-score components with s >= max - kWindow
+constexpr float kGateTau = 5e-7f;  // re-score a row when 2 E_n * r_max could exceed this
+constexpr float kUnitRound = 5.9604644775390625e-8f;  // 2^-24
+
+// Row of the 32x32 MFMA accumulator held in slot j by lanes of half h:
+// D[row][col] with col = lane % 32 and row = 8*(j/4) + 4*h + j%4.
+__device__ __forceinline__ int acc_row(int h, int j) { return ((j >> 2) << 3) + (h << 2) + (j & 3); }
+
+__device__ __forceinline__ float group_max(float v, int tpr) {
+  for (int o = 1; o < tpr; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float group_sum(float v, int tpr) {
+  for (int o = 1; o < tpr; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ double group_sum_d(double v, int tpr) {
+  for (int o = 1; o < tpr; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <typename XT>
+__device__ __forceinline__ float load_x(const XT* X, int64_t i) { return (float)X[i]; }
+
+// ---------------------------------------------------------------------------
+// Parameter precompute (fp64 arithmetic)
+// ---------------------------------------------------------------------------
+
+// One thread per (padded) component: the score constants and the inputs of
+// the fp32 error bound.
+__global__ void comp_consts_kernel(const float* __restrict__ mu, const float* __restrict__ var,
+                                   const float* __restrict__ logw, int K, int d, int Kp, int Kp16,
+                                   float* __restrict__ c32, double* __restrict__ c64e,
+                                   double* __restrict__ c64d, float* __restrict__ compmax) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= Kp) return;
+  if (k >= K) {
+    c32[k] = -INFINITY;
+    if (k < Kp16) c64e[k] = -INFINITY;
+    return;
+  }
+  double slv = 0.0, sm2 = 0.0, amax = 0.0, bmax = 0.0;
+  for (int j = 0; j < d; ++j) {
+    const double v = var[(size_t)k * d + j], m = mu[(size_t)k * d + j];
+    const double iv = 1.0 / v;
+    slv += log(v);
+    sm2 += m * m * iv;
+    amax = fmax(amax, 0.5 * iv);
+    bmax = fmax(bmax, fabs(m * iv));
+  }
+  const double cd = (double)logw[k] - 0.5 * ((double)d * kLog2Pi + slv);
+  const double ce = cd - 0.5 * sm2;
+  c64d[k] = cd;
+  c64e[k] = ce;
+  c32[k] = (float)ce;
+  compmax[3 * k + 0] = (float)amax;
+  compmax[3 * k + 1] = (float)bmax;
+  compmax[3 * k + 2] = isfinite(ce) ? (float)fabs(ce) : 0.0f;
+}
+
+// One thread per (component, feature) over Kp x DP: packed MFMA operands.
+//  W32p: float4 index (kt*Q + q)*64 + lane, lane = 32*h + c, holds features
+//        4q..4q+3 of component 32*kt + c; h = 0 -> A, h = 1 -> B.
+//  W64p: double index ((kt*S + s)*4 + g)*16 + c holds feature 2s + g/2 of
+//        component 16*kt + c; g even -> A, g odd -> B.
+__global__ void pack_kernel(const float* __restrict__ mu, const float* __restrict__ var, int K, int d,
+                            int Kp, int Kp16, int DP, float* __restrict__ W32p,
+                            double* __restrict__ W64p, double* __restrict__ iv64) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= (int64_t)Kp * DP) return;
+  const int k = (int)(t / DP), f = (int)(t - (int64_t)k * DP);
+  double A = 0.0, B = 0.0;
+  if (k < K && f < d) {
+    const double iv = 1.0 / (double)var[(size_t)k * d + f];
+    A = -0.5 * iv;
+    B = (double)mu[(size_t)k * d + f] * iv;
+    iv64[(size_t)k * d + f] = iv;
+  }
+  {
+    const int kt = k >> 5, c = k & 31, q = f >> 2, u = f & 3, Q = DP >> 2;
+    const size_t base = (((size_t)kt * Q + q) * 64 + c) * 4 + u;
+    W32p[base] = (float)A;
+    W32p[base + 32 * 4] = (float)B;
+  }
+  if (k < Kp16) {
+    const int kt = k >> 4, c = k & 15, s = f >> 1, S = DP >> 1, g0 = 2 * (f & 1);
+    const size_t base = (((size_t)kt * S + s) * 4 + g0) * 16 + c;
+    W64p[base] = A;
+    W64p[base + 16] = B;
+  }
+}
+
+// One block: global maxima of the per-component error-bound inputs.
+__global__ void errc_kernel(const float* __restrict__ compmax, int K, float* __restrict__ errc) {
+  __shared__ float s[3][256];
+  float a = 0.f, b = 0.f, c = 0.f;
+  for (int k = threadIdx.x; k < K; k += blockDim.x) {
+    a = fmaxf(a, compmax[3 * k]);
+    b = fmaxf(b, compmax[3 * k + 1]);
+    c = fmaxf(c, compmax[3 * k + 2]);
+  }
+  s[0][threadIdx.x] = a;
+  s[1][threadIdx.x] = b;
+  s[2][threadIdx.x] = c;
+  __syncthreads();
+  for (int o = blockDim.x / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o)
+      for (int i = 0; i < 3; ++i) s[i][threadIdx.x] = fmaxf(s[i][threadIdx.x], s[i][threadIdx.x + o]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    errc[0] = s[0][0];
+    errc[1] = s[1][0];
+    errc[2] = s[2][0];
+    errc[3] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Statistics kernel: single sweep (MODE 0) or the second pass (MODE 1)
+// ---------------------------------------------------------------------------
+//
+// Block = `waves` waves; wave w owns components kw = k0 + 32w .. kw + 31 of
+// its slab. The block walks the 64-point tiles of its row chunk:
+//   1. X tile -> LDS (zero padded to DP features and 64 rows)
+//   2. scores: two 32x32 fp32 MFMA accumulators per wave -> LDS score tile
+//   3. row phase (`waves` threads per row): max, log-sum-exp (MODE 0) or the
+//      first pass's (m, lZ) (MODE 1), gated exact re-score, r in place
+//   4. statistics: r (re-read in accumulator layout) is the A operand and
+//      [x | x^2] from the LDS tile the B operand of 32x32x2 MFMAs that
+//      accumulate Sx, Sxx for the wave's 32 components in registers.
+// At the end each block writes its statistics partial; a separate kernel
+// sums the partials in a fixed order (no atomics anywhere).
+template <int DT, int MODE, typename XT>
+__global__ void __launch_bounds__(512)
+estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, int waves, int kslabs,
+                   int64_t rows_per_chunk, const float4* __restrict__ W32p, const float* __restrict__ c32,
+                   const float* __restrict__ mu, const double* __restrict__ iv64,
+                   const double* __restrict__ c64d, const float* __restrict__ errc,
+                   const float2* __restrict__ rowref, float* __restrict__ partials,
+                   double* __restrict__ llpart, float* __restrict__ ll_point, float* __restrict__ R) {
+  constexpr int DP = 32 * DT, Q = DP / 4, XS = DP + 4, E = 1 + 2 * DP;
+  extern __shared__ __align__(16) float smem[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int nthr = blockDim.x;
+  const int KS = waves * 32, SCS = KS + 8;
+  const int64_t chunk = blockIdx.x / kslabs;
+  const int slab = blockIdx.x - (int)(chunk * kslabs);
+  const int k0 = slab * KS;
+  const int kw = k0 + wave * 32;
+  float* xs = smem;              // [64][XS]
+  float* sc = xs + 64 * XS;      // [64][SCS]
+  float* rv = sc + 64 * SCS;     // [64][2]
+  double* lls = reinterpret_cast<double*>(rv + 128);  // [nthr]
+
+  const int tpr = waves;  // threads per row in the row phase
+  const int prow = tid / tpr, psub = tid - prow * tpr;
+  const int lane_base = lane - psub;
+  const float a_max = errc[0], b_max = errc[1], c_max = errc[2];
+  const float gam = (float)(2 * DP + 8) * kUnitRound;
+
+  v16f SX[DT], SXX[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      SX[t][j] = 0.f;
+      SXX[t][j] = 0.f;
+    }
+  float nk = 0.f;
+  double ll_acc = 0.0;
+
+  const int64_t lo = chunk * rows_per_chunk;
+  const int64_t hi = min(N, lo + rows_per_chunk);
+  const float4* Wt = W32p + (size_t)(kw >> 5) * Q * 64 + lane;
+  const float ck = c32[kw + c];
+
+  for (int64_t r0 = lo; r0 < hi; r0 += 64) {
+    __syncthreads();
+    // 1. X tile
+    for (int e = tid; e < 64 * DP; e += nthr) {
+      const int row = e / DP, f = e - row * DP;
+      const int64_t gr = r0 + row;
+      xs[row * XS + f] = (gr < hi && f < d) ? load_x(X, gr * d + f) : 0.f;
+    }
+    if (MODE == 1 && tid < 64) {
+      const int64_t gr = r0 + tid;
+      const float2 mr = gr < hi ? rowref[gr] : make_float2(0.f, 0.f);
+      rv[2 * tid] = mr.x;
+      rv[2 * tid + 1] = mr.y;
+    }
+    __syncthreads();
+
+    // 2. scores
+    {
+      v16f acc0, acc1;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        acc0[j] = 0.f;
+        acc1[j] = 0.f;
+      }
+      // one-ahead register prefetch of the (L2-resident) score operands
+      float4 w = Wt[0];
+#pragma unroll 1
+      for (int q = 0; q < Q; ++q) {
+        const float4 wn = Wt[(q + 1 < Q ? q + 1 : q) * 64];
+        const float4 x0 = *reinterpret_cast<const float4*>(xs + c * XS + 4 * q);
+        const float4 x1 = *reinterpret_cast<const float4*>(xs + (c + 32) * XS + 4 * q);
+        const float wv[4] = {w.x, w.y, w.z, w.w};
+        const float xv0[4] = {x0.x, x0.y, x0.z, x0.w};
+        const float xv1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float a0 = h ? xv0[u] : xv0[u] * xv0[u];
+          const float a1 = h ? xv1[u] : xv1[u] * xv1[u];
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, wv[u], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, wv[u], acc1, 0, 0, 0);
+        }
+        w = wn;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = acc_row(h, j);
+        sc[r * SCS + wave * 32 + c] = acc0[j] + ck;
+        sc[(r + 32) * SCS + wave * 32 + c] = acc1[j] + ck;
+      }
+    }
+    __syncthreads();
+
+    // 3. row phase
+    {
+      const int row = prow;
+      const int64_t grow = r0 + row;
+      const bool valid = grow < hi;
+      float* srow = sc + row * SCS;
+      const float* xrow = xs + row * XS;
+      float sq = 0.f, ab = 0.f;
+      for (int f = psub; f < d; f += tpr) {
+        const float x = xrow[f];
+        sq += x * x;
+        ab += fabsf(x);
+      }
+      sq = group_sum(sq, tpr);
+      ab = group_sum(ab, tpr);
+      const float Ebound = gam * (a_max * sq + b_max * ab + c_max);
+
+      float m;
+      double z = 0.0, lZd = 0.0;
+      if (MODE == 0) {
+        m = -INFINITY;
+#pragma unroll 1
+        for (int i = 0; i < 32; ++i) m = fmaxf(m, srow[psub + tpr * i]);
+        m = group_max(m, tpr);
+#pragma unroll 1
+        for (int i = 0; i < 32; ++i) {
+          const float dl = srow[psub + tpr * i] - m;
+          srow[psub + tpr * i] = dl;
+          z += (double)expf(dl);
+        }
+        z = group_sum_d(z, tpr);
+      } else {
+        m = rv[2 * row];
+        lZd = (double)rv[2 * row + 1];
+#pragma unroll 1
+        for (int i = 0; i < 32; ++i) srow[psub + tpr * i] -= m;
+      }
+      const float rmax = MODE == 0 ? (float)(1.0 / z) : expf(-(float)lZd);
+      const bool refine = valid && (2.f * Ebound * rmax > kGateTau);
+      uint32_t mask = 0;
+      if (refine)
+#pragma unroll 1
+        for (int i = 0; i < 32; ++i)
+          if (srow[psub + tpr * i] >= -kWindow) mask |= 1u << i;
+      // Exact re-score of the window, one component at a time per row group;
+      // the group's threads split the features.
+      for (;;) {
+        const uint64_t bal = __ballot(mask != 0);
+        if (bal == 0) break;
+        const uint32_t gb = (uint32_t)(bal >> lane_base) & ((1u << tpr) - 1u);
+        const int owner = gb ? __ffs(gb) - 1 : 0;
+        const int myfirst = mask ? __ffs(mask) - 1 : 0;
+        const int oi = __shfl(myfirst, lane_base + owner, 64);
+        const int kl = owner + tpr * oi;
+        const int kg = k0 + kl;
+        double acc = 0.0;
+        if (gb) {
+          const float* mk = mu + (size_t)kg * d;
+          const double* ivk = iv64 + (size_t)kg * d;
+          for (int f = psub; f < d; f += tpr) {
+            const double t = (double)xrow[f] - (double)mk[f];
+            acc += t * t * ivk[f];
+          }
+        }
+        acc = group_sum_d(acc, tpr);
+        if (gb && psub == owner) {
+          const double s64 = c64d[kg] - 0.5 * acc;
+          srow[kl] = (float)(s64 - (double)m);
+          mask &= mask - 1u;
+        }
+      }
+      if (MODE == 0) {
+        double z2 = 0.0;
+        if (refine)
+#pragma unroll 1
+          for (int i = 0; i < 32; ++i) z2 += (double)expf(srow[psub + tpr * i]);
+        z2 = group_sum_d(z2, tpr);
+        if (refine) z = z2;
+        lZd = log(z);
+        if (valid && psub == 0) {
+          const double l = (double)m + lZd;
+          ll_acc += l;
+          if (ll_point) ll_point[grow] = (float)l;
+        }
+      }
+      const float lZ = (float)lZd;
+#pragma unroll 1
+      for (int i = 0; i < 32; ++i) {
+        const int kl = psub + tpr * i;
+        const float r = valid ? expf(srow[kl] - lZ) : 0.f;
+        srow[kl] = r;
+        if (R && valid && k0 + kl < K) R[grow * K + k0 + kl] = r;
+      }
+    }
+    __syncthreads();
+
+    // 4. statistics
+#pragma unroll 1
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll 2
+      for (int j = 0; j < 16; ++j) {
+        const int row = g * 32 + acc_row(h, j);
+        const float r = sc[row * SCS + wave * 32 + c];
+        nk += r;
+        const float* xr = xs + row * XS + DT * c;
+        float xv[DT];
+#pragma unroll
+        for (int t = 0; t < DT; ++t) xv[t] = xr[t];
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          SX[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(r, xv[t], SX[t], 0, 0, 0);
+          SXX[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(r, xv[t] * xv[t], SXX[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // statistics partial of this (chunk, slab)
+  float* part = partials + (size_t)chunk * Kp * E;
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int comp = kw + acc_row(h, j);
+      const int f = DT * c + t;
+      part[(size_t)comp * E + 1 + f] = SX[t][j];
+      part[(size_t)comp * E + 1 + DP + f] = SXX[t][j];
+    }
+  nk += __shfl_xor(nk, 32, 64);
+  if (h == 0) part[(size_t)(kw + c) * E] = nk;
+
+  if (MODE == 0) {
+    lls[tid] = ll_acc;
+    __syncthreads();
+    if (tid == 0) {
+      double s = 0.0;
+      for (int i = 0; i < nthr; ++i) s += lls[i];
+      llpart[chunk] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// First pass of the two-pass regime (also the top-2 kernel): fp64 MFMA scores
+// ---------------------------------------------------------------------------
+//
+// Block = 4 waves, one 64-point tile; wave w takes the 16-component tiles
+// w, w+4, ... . Scores come from 16x16x4 f64 MFMAs (layout: D[comp][point]),
+// so each lane holds four components of one point per accumulator and keeps
+// an online (max, sum of exp) per point; lanes and waves are merged at the
+// end in a fixed order. Output per row: (m_ref, lZ) with m_ref = fp32 of the
+// row max and lZ = l - m_ref, the per-point l, and optionally the top-2.
+__device__ __forceinline__ bool better(double v, int i, double w, int j) {
+  return v > w || (v == w && i < j);
+}
+__device__ __forceinline__ void lse_merge(double& m, double& z, double mo, double zo) {
+  const double mn = fmax(m, mo);
+  if (mn == -INFINITY) return;
+  z = (m == -INFINITY ? 0.0 : z * exp(m - mn)) + (mo == -INFINITY ? 0.0 : zo * exp(mo - mn));
+  m = mn;
+}
+__device__ __forceinline__ void top2_insert(double v, int i, double& v1, int& i1, double& v2, int& i2) {
+  if (better(v, i, v1, i1)) {
+    v2 = v1;
+    i2 = i1;
+    v1 = v;
+    i1 = i;
+  } else if (better(v, i, v2, i2)) {
+    v2 = v;
+    i2 = i;
+  }
+}
+
+template <int DT, bool TOP2, typename XT>
+__global__ void __launch_bounds__(256)
+estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
+                 const double* __restrict__ W64p, const double* __restrict__ c64e,
+                 float2* __restrict__ rowref, float* __restrict__ ll_point, double* __restrict__ llpart,
+                 int32_t* __restrict__ tidx, float* __restrict__ tresp) {
+  constexpr int DP = 32 * DT, S = DP / 2, XS = DP + 1;
+  __shared__ float xs[64 * XS];
+  __shared__ double sm[kLseWaves][64], sz[kLseWaves][64], sv1[kLseWaves][64], sv2[kLseWaves][64];
+  __shared__ int si1[kLseWaves][64], si2[kLseWaves][64];
+  __shared__ double sl[64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+
+  for (int e = tid; e < 64 * DP; e += blockDim.x) {
+    const int row = e / DP, f = e - row * DP;
+    const int64_t gr = r0 + row;
+    xs[row * XS + f] = (gr < N && f < d) ? load_x(X, gr * d + f) : 0.f;
+  }
+  __syncthreads();
+
+  double m[4], z[4], v1[4], v2[4];
+  int i1[4], i2[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    m[p] = -INFINITY;
+    z[p] = 0.0;
+    v1[p] = v2[p] = -INFINITY;
+    i1[p] = i2[p] = 0x7fffffff;
+  }
+  const int Kt = Kp16 / 16;
+  for (int kt = wave; kt < Kt; kt += kLseWaves) {
+    v4d D[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) D[p] = (v4d){0.0, 0.0, 0.0, 0.0};
+    const double* Wk = W64p + (size_t)kt * S * 64 + lane;
+#pragma unroll 4
+    for (int s = 0; s < S; ++s) {
+      const double a = Wk[(size_t)s * 64];
+      const int f = 2 * s + (g >> 1);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const double x = (double)xs[(p * 16 + c) * XS + f];
+        const double b = (g & 1) ? x : x * x;
+        D[p] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, D[p], 0, 0, 0);
+      }
+    }
+    double ce[4];
+    int comp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      comp[j] = kt * 16 + 4 * j + g;
+      ce[j] = c64e[comp[j]];
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      double s[4];
+      double mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[j] = D[p][j] + ce[j];
+        mx = fmax(mx, s[j]);
+      }
+      if (mx > m[p]) {
+        z[p] = (m[p] == -INFINITY) ? 0.0 : z[p] * exp(m[p] - mx);
+        m[p] = mx;
+      }
+      if (m[p] > -INFINITY)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[p] += (double)expf((float)(s[j] - m[p]));
+      if (TOP2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (comp[j] < K) top2_insert(s[j], comp[j], v1[p], i1[p], v2[p], i2[p]);
+    }
+  }
+  // merge the four lane groups that hold the same points
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const double mo = __shfl_xor(m[p], o, 64), zo = __shfl_xor(z[p], o, 64);
+      lse_merge(m[p], z[p], mo, zo);
+      if (TOP2) {
+        const double w1 = __shfl_xor(v1[p], o, 64), w2 = __shfl_xor(v2[p], o, 64);
+        const int j1 = __shfl_xor(i1[p], o, 64), j2 = __shfl_xor(i2[p], o, 64);
+        top2_insert(w1, j1, v1[p], i1[p], v2[p], i2[p]);
+        top2_insert(w2, j2, v1[p], i1[p], v2[p], i2[p]);
+      }
+    }
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      sm[wave][p * 16 + c] = m[p];
+      sz[wave][p * 16 + c] = z[p];
+      if (TOP2) {
+        sv1[wave][p * 16 + c] = v1[p];
+        sv2[wave][p * 16 + c] = v2[p];
+        si1[wave][p * 16 + c] = i1[p];
+        si2[wave][p * 16 + c] = i2[p];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    double mm = sm[0][tid], zz = sz[0][tid];
+    double a1 = TOP2 ? sv1[0][tid] : 0.0, a2 = TOP2 ? sv2[0][tid] : 0.0;
+    int b1 = TOP2 ? si1[0][tid] : 0, b2 = TOP2 ? si2[0][tid] : 0;
+    for (int w = 1; w < kLseWaves; ++w) {
+      lse_merge(mm, zz, sm[w][tid], sz[w][tid]);
+      if (TOP2) {
+        top2_insert(sv1[w][tid], si1[w][tid], a1, b1, a2, b2);
+        top2_insert(sv2[w][tid], si2[w][tid], a1, b1, a2, b2);
+      }
+    }
+    const double l = mm + log(zz);
+    const int64_t gr = r0 + tid;
+    sl[tid] = gr < N ? l : 0.0;
+    if (gr < N) {
+      const float mref = (float)mm;
+      if (rowref) rowref[gr] = make_float2(mref, (float)(l - (double)mref));
+      if (ll_point) ll_point[gr] = (float)l;
+      if (TOP2) {
+        tidx[2 * gr] = b1;
+        tresp[2 * gr] = (float)exp(a1 - l);
+        const bool has2 = b2 != 0x7fffffff;
+        tidx[2 * gr + 1] = has2 ? b2 : -1;
+        tresp[2 * gr + 1] = has2 ? (float)exp(a2 - l) : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0 && llpart) {
+    double s = 0.0;
+    for (int i = 0; i < 64; ++i) s += sl[i];
+    llpart[blockIdx.x] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reductions, M-step, fills
+// ---------------------------------------------------------------------------
+
+// out element (k, e) of [Nk | Sx | Sxx] = sum over chunks p in order 0..P-1.
+__global__ void reduce_stats_kernel(const float* __restrict__ partials, int64_t P, int Kp, int E, int DP,
+                                    int K, int d, float* __restrict__ Nk, float* __restrict__ Sx,
+                                    float* __restrict__ Sxx) {
+  const int W = 1 + 2 * d;
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= (int64_t)K * W) return;
+  const int k = (int)(t / W), e = (int)(t - (int64_t)k * W);
+  const int src = e == 0 ? 0 : (e <= d ? e : DP + (e - d));
+  const float* p0 = partials + (size_t)k * E + src;
+  const size_t stride = (size_t)Kp * E;
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  int64_t p = 0;
+  for (; p + 4 <= P; p += 4) {
+    s0 += p0[(p + 0) * stride];
+    s1 += p0[(p + 1) * stride];
+    s2 += p0[(p + 2) * stride];
+    s3 += p0[(p + 3) * stride];
+  }
+  for (; p < P; ++p) s0 += p0[p * stride];
+  const float s = (float)((s0 + s1) + (s2 + s3));
+  if (e == 0)
+    Nk[k] = s;
+  else if (e <= d)
+    Sx[(size_t)k * d + e - 1] = s;
+  else
+    Sxx[(size_t)k * d + e - 1 - d] = s;
+}
+
+// One block of 256: fixed-order sum of n doubles.
+__global__ void reduce_ll_kernel(const double* __restrict__ part, int64_t n, double* __restrict__ out) {
+  __shared__ double s[256];
+  const int64_t per = (n + 255) / 256;
+  const int64_t lo = threadIdx.x * per, hi = min(n, lo + per);
+  double a = 0.0;
+  for (int64_t i = lo; i < hi; ++i) a += part[i];
+  s[threadIdx.x] = a;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = s[0];
+}
+
+__global__ void zero_outputs_kernel(float* __restrict__ Nk, float* __restrict__ Sx, float* __restrict__ Sxx,
+                                    int d, int K, double* __restrict__ ll) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t Kd = (int64_t)K * d;
+  if (t < K && Nk) Nk[t] = 0.f;
+  if (t < Kd) {
+    if (Sx) Sx[t] = 0.f;
+    if (Sxx) Sxx[t] = 0.f;
+  }
+  if (t == 0 && ll) ll[0] = 0.0;
+}
+
+// One thread per (k, j): w = Nk/N, mu = Sx/Nk, var = max(Sxx/Nk - mu^2, floor).
+__global__ void mstep_kernel(const float* __restrict__ Nk, const float* __restrict__ Sx,
+                             const float* __restrict__ Sxx, double Nd, int d, int K, float var_floor,
+                             float* __restrict__ mu, float* __restrict__ var, float* __restrict__ logw) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= (int64_t)K * d) return;
+  const int k = (int)(t / d), j = (int)(t - (int64_t)k * d);
+  const double nk = (double)Nk[k];
+  if (j == 0) {
+    const double nkc = nk < 1e-300 ? 1e-300 : nk;
+    logw[k] = (float)log(nkc / Nd);
+  }
+  if (nk >= 1e-12 * Nd) {
+    const double m = (double)Sx[t] / nk;
+    double v = (double)Sxx[t] / nk - m * m;
+    if (v < (double)var_floor) v = (double)var_floor;
+    mu[t] = (float)m;
+    var[t] = (float)v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+
+static inline unsigned nblocks(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
+
+hipError_t launch_precompute(const Plan& p, const float* mu, const float* var, const float* logw,
+                             hipStream_t stream) {
+  const Workspace& w = p.ws;
+  comp_consts_kernel<<<nblocks(p.Kp, 256), 256, 0, stream>>>(mu, var, logw, p.K, p.d, p.Kp, p.Kp16, w.c32,
+                                                               w.c64e, w.c64d, w.compmax);
+  pack_kernel<<<nblocks((int64_t)p.Kp * p.DP, 256), 256, 0, stream>>>(mu, var, p.K, p.d, p.Kp, p.Kp16, p.DP,
+                                                                        w.W32p, w.W64p, w.iv64);
+  errc_kernel<<<1, 256, 0, stream>>>(w.compmax, p.K, w.errc);
+  return hipGetLastError();
+}
+
+template <int DT, int MODE, typename XT>
+static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* ll_point, float* R,
+                            hipStream_t stream) {
+  const Workspace& w = p.ws;
+  const int nthr = p.waves * 64;
+  const int KS = p.waves * 32;
+  const size_t lds = (size_t)(64 * (32 * DT + 4) + 64 * (KS + 8) + 128) * sizeof(float) + (size_t)nthr * sizeof(double);
+  auto fn = estep_stats_kernel<DT, MODE, XT>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)(p.P * p.kslabs);
+  fn<<<grid, nthr, lds, stream>>>(X, p.N, p.d, p.K, p.Kp, p.waves, p.kslabs, p.rows_per_chunk,
+                                  reinterpret_cast<const float4*>(w.W32p), w.c32, mu, w.iv64, w.c64d, w.errc,
+                                  w.rowref, w.partials, w.llpart, ll_point, R);
+  return hipGetLastError();
+}
+
+template <int DT, bool TOP2, typename XT>
+static hipError_t run_lse(const Plan& p, const XT* X, float* ll_point, int32_t* idx, float* resp,
+                          hipStream_t stream) {
+  const Workspace& w = p.ws;
+  estep_lse_kernel<DT, TOP2, XT><<<(unsigned)p.tiles, 256, 0, stream>>>(
+      X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp);
+  return hipGetLastError();
+}
+
+template <typename XT>
+static hipError_t estep_typed(const Plan& p, const XT* X, const float* mu, float* ll_point, float* R,
+                              hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  if (p.regime == 1) {
+    switch (p.DT) {
+      case 1: e = run_stats<1, 0>(p, X, mu, ll_point, R, stream); break;
+      case 2: e = run_stats<2, 0>(p, X, mu, ll_point, R, stream); break;
+      case 3: e = run_stats<3, 0>(p, X, mu, ll_point, R, stream); break;
+      default: e = run_stats<4, 0>(p, X, mu, ll_point, R, stream); break;
+    }
+    return e;
+  }
+  switch (p.DT) {
+    case 1: e = run_lse<1, false>(p, X, ll_point, nullptr, nullptr, stream); break;
+    case 2: e = run_lse<2, false>(p, X, ll_point, nullptr, nullptr, stream); break;
+    case 3: e = run_lse<3, false>(p, X, ll_point, nullptr, nullptr, stream); break;
+    default: e = run_lse<4, false>(p, X, ll_point, nullptr, nullptr, stream); break;
+  }
+  if (e != hipSuccess) return e;
+  switch (p.DT) {
+    case 1: e = run_stats<1, 1>(p, X, mu, nullptr, R, stream); break;
+    case 2: e = run_stats<2, 1>(p, X, mu, nullptr, R, stream); break;
+    case 3: e = run_stats<3, 1>(p, X, mu, nullptr, R, stream); break;
+    default: e = run_stats<4, 1>(p, X, mu, nullptr, R, stream); break;
+  }
+  return e;
+}
+
+hipError_t launch_estep(const Plan& p, const void* X, int x_dtype, const float* mu, float* Nk, float* Sx,
+                        float* Sxx, double* loglik_total, float* loglik_point, float* R, hipStream_t stream) {
+  if (p.N == 0) return launch_zero_outputs(Nk, Sx, Sxx, p.d, p.K, loglik_total, stream);
+  hipError_t e = x_dtype == 1
+                     ? estep_typed(p, reinterpret_cast<const _Float16*>(X), mu, loglik_point, R, stream)
+                     : estep_typed(p, reinterpret_cast<const float*>(X), mu, loglik_point, R, stream);
+  if (e != hipSuccess) return e;
+  const Workspace& w = p.ws;
+  if (Nk && Sx && Sxx) {
+    const int64_t n = (int64_t)p.K * (1 + 2 * p.d);
+    reduce_stats_kernel<<<nblocks(n, 256), 256, 0, stream>>>(w.partials, p.P, p.Kp, p.E, p.DP, p.K, p.d, Nk,
+                                                               Sx, Sxx);
+  }
+  if (loglik_total) {
+    const int64_t nll = p.regime == 1 ? p.P : p.tiles;
+    reduce_ll_kernel<<<1, 256, 0, stream>>>(w.llpart, nll, loglik_total);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_top2(const Plan& p, const void* X, int x_dtype, int32_t* idx, float* resp,
+                       hipStream_t stream) {
+  if (p.N == 0) return hipSuccess;
+  hipError_t e = hipSuccess;
+  if (x_dtype == 1) {
+    const _Float16* x = reinterpret_cast<const _Float16*>(X);
+    switch (p.DT) {
+      case 1: e = run_lse<1, true>(p, x, nullptr, idx, resp, stream); break;
+      case 2: e = run_lse<2, true>(p, x, nullptr, idx, resp, stream); break;
+      case 3: e = run_lse<3, true>(p, x, nullptr, idx, resp, stream); break;
+      default: e = run_lse<4, true>(p, x, nullptr, idx, resp, stream); break;
+    }
+  } else {
+    const float* x = reinterpret_cast<const float*>(X);
+    switch (p.DT) {
+      case 1: e = run_lse<1, true>(p, x, nullptr, idx, resp, stream); break;
+      case 2: e = run_lse<2, true>(p, x, nullptr, idx, resp, stream); break;
+      case 3: e = run_lse<3, true>(p, x, nullptr, idx, resp, stream); break;
+      default: e = run_lse<4, true>(p, x, nullptr, idx, resp, stream); break;
+    }
+  }
+  return e;
+}
+
+hipError_t launch_mstep(const float* Nk, const float* Sx, const float* Sxx, int64_t N, int d, int K,
+                        float var_floor, float* mu, float* var, float* logw, hipStream_t stream) {
+  const int64_t n = (int64_t)K * d;
+  mstep_kernel<<<nblocks(n, 256), 256, 0, stream>>>(Nk, Sx, Sxx, (double)N, d, K, var_floor, mu, var, logw);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_outputs(float* Nk, float* Sx, float* Sxx, int d, int K, double* loglik_total,
+                               hipStream_t stream) {
+  const int64_t n = (int64_t)K * d > K ? (int64_t)K * d : K;
+  zero_outputs_kernel<<<nblocks(n, 256), 256, 0, stream>>>(Nk, Sx, Sxx, d, K, loglik_total);
+  return hipGetLastError();
+}
+
+}  // namespace gmm

@@ -1,0 +1,197 @@
+"""Thin ctypes binding of libgmm_mi355x.so (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU, passes their
+device pointers and torch's current HIP stream to the C-ABI, and returns
+tensors the library wrote. All computation happens in the HIP kernels; there
+is no CPU path. The library must have been built (``build.py``); importing
+this module on a machine without it raises immediately.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgmm_mi355x.so")
+
+GMM_F32, GMM_F16 = 0, 1
+REGIME_AUTO, REGIME_SINGLE, REGIME_TWOPASS = 0, 1, 2
+
+EXPORTS = (
+    "gmm_version", "gmm_error_string", "gmm_workspace_bytes", "gmm_estep_stats",
+    "gmm_estep_stats_regime", "gmm_estep_resp", "gmm_mstep", "gmm_em_iterate", "gmm_assign_top2",
+)
+
+
+class GmmError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {code} ({error_string(code)})")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with soft_clustering_gmm_amd/build.py "
+                           "(or __graft_entry__.build()); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    L.gmm_version.restype = ctypes.c_int
+    L.gmm_version.argtypes = []
+    L.gmm_error_string.restype = ctypes.c_char_p
+    L.gmm_error_string.argtypes = [ctypes.c_int]
+    L.gmm_workspace_bytes.restype = SZ
+    L.gmm_workspace_bytes.argtypes = [I64, I32, I32]
+    L.gmm_estep_stats.restype = ctypes.c_int
+    L.gmm_estep_stats.argtypes = [P, I32, I64, I32, P, P, P, I32, P, P, P, P, P, P, SZ, P]
+    L.gmm_estep_stats_regime.restype = ctypes.c_int
+    L.gmm_estep_stats_regime.argtypes = [P, I32, I64, I32, P, P, P, I32, P, P, P, P, P, P, SZ, I32, P]
+    L.gmm_estep_resp.restype = ctypes.c_int
+    L.gmm_estep_resp.argtypes = [P, I32, I64, I32, P, P, P, I32, P, P, P, SZ, I32, P]
+    L.gmm_mstep.restype = ctypes.c_int
+    L.gmm_mstep.argtypes = [P, P, P, I64, I32, I32, F32, P, P, P, P]
+    L.gmm_em_iterate.restype = ctypes.c_int
+    L.gmm_em_iterate.argtypes = [P, I32, I64, I32, I32, I32, F32, P, P, P, P, P, SZ, P]
+    L.gmm_assign_top2.restype = ctypes.c_int
+    L.gmm_assign_top2.argtypes = [P, I32, I64, I32, P, P, P, I32, P, P, P, SZ, P]
+    return L
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def error_string(code: int) -> str:
+    return lib().gmm_error_string(code).decode()
+
+
+def _check(fn: str, code: int) -> None:
+    if code != 0:
+        raise GmmError(fn, code)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _xtype(X: torch.Tensor) -> int:
+    if X.dtype == torch.float32:
+        return GMM_F32
+    if X.dtype == torch.float16:
+        return GMM_F16
+    raise ValueError(f"X must be float32 or float16, got {X.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, device):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _params(X, mu, var, logw):
+    if X.dim() != 2:
+        raise ValueError("X must be N x d")
+    N, d = X.shape
+    K = mu.shape[0]
+    dev = X.device
+    if dev.type != "cuda":
+        raise ValueError("X must be on the GPU")
+    _xtype(X)
+    if not X.is_contiguous():
+        raise ValueError("X must be contiguous")
+    _need(mu, "mu", torch.float32, (K, d), dev)
+    _need(var, "var", torch.float32, (K, d), dev)
+    _need(logw, "logw", torch.float32, (K,), dev)
+    return N, d, K, dev
+
+
+def workspace_bytes(N: int, d: int, K: int) -> int:
+    return int(lib().gmm_workspace_bytes(N, d, K))
+
+
+def workspace(N: int, d: int, K: int, device) -> torch.Tensor:
+    """A device workspace large enough for every entry point at (N, d, K)."""
+    nb = workspace_bytes(N, d, K)
+    if nb == 0:
+        raise ValueError(f"unsupported shape N={N} d={d} K={K}")
+    return torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+def _ws(ws, N, d, K, dev):
+    if ws is None:
+        ws = workspace(N, d, K, dev)
+    return ws
+
+
+def estep_stats(X, mu, var, logw, *, regime: int = REGIME_AUTO, want_point_loglik: bool = False, ws=None):
+    """Fused E-step: returns (Nk[K], Sx[K,d], Sxx[K,d], L (0-d float64), l_n[N] or None)."""
+    N, d, K, dev = _params(X, mu, var, logw)
+    Nk = torch.empty(K, dtype=torch.float32, device=dev)
+    Sx = torch.empty(K, d, dtype=torch.float32, device=dev)
+    Sxx = torch.empty(K, d, dtype=torch.float32, device=dev)
+    L = torch.empty((), dtype=torch.float64, device=dev)
+    lp = torch.empty(N, dtype=torch.float32, device=dev) if want_point_loglik else None
+    ws = _ws(ws, N, d, K, dev)
+    _check("gmm_estep_stats_regime", lib().gmm_estep_stats_regime(
+        _ptr(X), _xtype(X), N, d, _ptr(mu), _ptr(var), _ptr(logw), K, _ptr(Nk), _ptr(Sx), _ptr(Sxx),
+        _ptr(L), _ptr(lp), _ptr(ws), ws.numel(), regime, _stream(dev)))
+    return Nk, Sx, Sxx, L, lp
+
+
+def estep_resp(X, mu, var, logw, *, regime: int = REGIME_AUTO, ws=None):
+    """Testing aid: the responsibilities R[N,K] and l_n[N] from the same kernels."""
+    N, d, K, dev = _params(X, mu, var, logw)
+    R = torch.empty(N, K, dtype=torch.float32, device=dev)
+    lp = torch.empty(N, dtype=torch.float32, device=dev)
+    ws = _ws(ws, N, d, K, dev)
+    _check("gmm_estep_resp", lib().gmm_estep_resp(
+        _ptr(X), _xtype(X), N, d, _ptr(mu), _ptr(var), _ptr(logw), K, _ptr(R), _ptr(lp), _ptr(ws),
+        ws.numel(), regime, _stream(dev)))
+    return R, lp
+
+
+def mstep(Nk, Sx, Sxx, N: int, var_floor: float, mu, var, logw):
+    """In-place M-step on (mu, var, logw) from the statistics."""
+    K, d = mu.shape
+    dev = mu.device
+    _need(Nk, "Nk", torch.float32, (K,), dev)
+    _need(Sx, "Sx", torch.float32, (K, d), dev)
+    _need(Sxx, "Sxx", torch.float32, (K, d), dev)
+    _need(var, "var", torch.float32, (K, d), dev)
+    _need(logw, "logw", torch.float32, (K,), dev)
+    _check("gmm_mstep", lib().gmm_mstep(_ptr(Nk), _ptr(Sx), _ptr(Sxx), N, d, K, float(var_floor),
+                                        _ptr(mu), _ptr(var), _ptr(logw), _stream(dev)))
+
+
+def em_iterate(X, mu, var, logw, iters: int, var_floor: float, *, ws=None):
+    """`iters` EM iterations in place; returns the log-likelihood history (device float64)."""
+    N, d, K, dev = _params(X, mu, var, logw)
+    hist = torch.empty(max(iters, 1), dtype=torch.float64, device=dev)
+    ws = _ws(ws, N, d, K, dev)
+    _check("gmm_em_iterate", lib().gmm_em_iterate(
+        _ptr(X), _xtype(X), N, d, K, iters, float(var_floor), _ptr(mu), _ptr(var), _ptr(logw),
+        _ptr(hist), _ptr(ws), ws.numel(), _stream(dev)))
+    return hist[:iters]
+
+
+def assign_top2(X, mu, var, logw, *, ws=None):
+    """Top-2 components per point: (idx[N,2] int32, resp[N,2] float32)."""
+    N, d, K, dev = _params(X, mu, var, logw)
+    idx = torch.empty(N, 2, dtype=torch.int32, device=dev)
+    resp = torch.empty(N, 2, dtype=torch.float32, device=dev)
+    ws = _ws(ws, N, d, K, dev)
+    _check("gmm_assign_top2", lib().gmm_assign_top2(
+        _ptr(X), _xtype(X), N, d, _ptr(mu), _ptr(var), _ptr(logw), K, _ptr(idx), _ptr(resp),
+        _ptr(ws), ws.numel(), _stream(dev)))
+    return idx, resp

@@ -1,0 +1,96 @@
+"""The C-ABI library loads, exports every symbol gmm.h declares, and rejects bad
+arguments on the host before touching any GPU (these tests need no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gmm.h")
+LIB = os.path.join(ROOT, "soft_clustering_gmm_amd", "libgmm_mi355x.so")
+
+P = ctypes.c_void_p
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gmm_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built: run __graft_entry__.build()")
+    from soft_clustering_gmm_amd import gmm
+    return gmm.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    from soft_clustering_gmm_amd import gmm
+    assert set(gmm.EXPORTS) == set(names)
+
+
+def test_version_and_error_strings(L):
+    assert L.gmm_version() == 10000
+    for code in (0, -1, -2, -3, -4):
+        assert len(L.gmm_error_string(code)) >= 2
+    assert L.gmm_error_string(-99) == b"unknown status"
+
+
+def test_workspace_bytes(L):
+    assert L.gmm_workspace_bytes(0, 0, 8) == 0
+    assert L.gmm_workspace_bytes(10, 129, 8) == 0
+    assert L.gmm_workspace_bytes(10, 4, 70000) == 0
+    small = L.gmm_workspace_bytes(4096, 16, 8)
+    big = L.gmm_workspace_bytes(1 << 20, 128, 256)
+    assert 0 < small < big
+    assert L.gmm_workspace_bytes(1 << 20, 128, 256) % 256 == 0
+
+
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation first
+
+
+def _estep(L, X=FAKE, xt=0, N=100, d=4, K=3, ws=FAKE, wsb=1 << 40, regime=0, nk=FAKE):
+    return L.gmm_estep_stats_regime(X, xt, N, d, FAKE, FAKE, FAKE, K, nk, FAKE, FAKE, FAKE, None,
+                                    ws, wsb, regime, None)
+
+
+def test_estep_argument_validation(L):
+    assert _estep(L, d=0) == -1
+    assert _estep(L, N=-1) == -1
+    assert _estep(L, K=0) == -1
+    assert _estep(L, xt=7) == -1
+    assert _estep(L, X=None) == -1
+    assert _estep(L, nk=None) == -1
+    assert _estep(L, d=129) == -2
+    assert _estep(L, K=70000) == -2
+    assert _estep(L, ws=None) == -3
+    assert _estep(L, ws=ctypes.c_void_p(0x100010)) == -3   # misaligned
+    assert _estep(L, wsb=16) == -3                         # too small
+    assert _estep(L, K=300, regime=1) == -2                # single sweep needs K <= 256
+    assert _estep(L, regime=5) == -1
+
+
+def test_other_entry_points_validate(L):
+    # mstep: N must be >= 1, floor >= 0
+    assert L.gmm_mstep(FAKE, FAKE, FAKE, 0, 4, 3, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, None) == -1
+    assert L.gmm_mstep(FAKE, FAKE, FAKE, 10, 4, 3, ctypes.c_float(-1.0), FAKE, FAKE, FAKE, None) == -1
+    assert L.gmm_mstep(None, FAKE, FAKE, 10, 4, 3, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, None) == -1
+    # em_iterate: N >= 1, iters >= 0, history pointer needed
+    assert L.gmm_em_iterate(FAKE, 0, 0, 4, 3, 2, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, FAKE, FAKE,
+                            1 << 40, None) == -1
+    assert L.gmm_em_iterate(FAKE, 0, 10, 4, 3, -1, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, FAKE, FAKE,
+                            1 << 40, None) == -1
+    assert L.gmm_em_iterate(FAKE, 0, 10, 4, 3, 2, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, None, FAKE,
+                            1 << 40, None) == -1
+    # top2 / resp: outputs needed, workspace checked
+    assert L.gmm_assign_top2(FAKE, 0, 10, 4, FAKE, FAKE, FAKE, 3, None, FAKE, FAKE, 1 << 40, None) == -1
+    assert L.gmm_assign_top2(FAKE, 0, 10, 4, FAKE, FAKE, FAKE, 3, FAKE, FAKE, FAKE, 8, None) == -3
+    assert L.gmm_estep_resp(FAKE, 0, 10, 4, FAKE, FAKE, FAKE, 3, None, None, FAKE, 1 << 40, 0, None) == -1
+    assert L.gmm_estep_resp(FAKE, 1, 10, 4, FAKE, FAKE, FAKE, 3, FAKE, None, FAKE, 1 << 40, 9, None) == -1
