@@ -1,0 +1,161 @@
+"""Benchmark: fused GMM E-step + sufficient statistics on one MI355X.
+
+A step is one EM iteration through the C-ABI (gmm_em_iterate with iters=1):
+parameter precompute, the fused E-step with statistics, the deterministic
+partial reduction and the M-step, on the "ref" blob workload
+(N=1,048,576 points, d=128, K=256 diagonal components, fp32) with X resident
+in HBM. Every step (warm-up and timed) starts from the same initial
+parameters (K data points as means, unit variances, equal weights), restored
+by three small device copies inside the step, so that all steps do identical
+work. `value` = N*K / (wall-clock seconds per step).
+
+Prints one JSON line with, besides the required keys,
+  roofline     - the fused E-step kernel's flops per launch / its average
+                 duration (HIP events recorded around the kernel on its own
+                 stream), against the FP32 MFMA peak, plus its algorithmic
+                 HBM rate; `traffic` comes from committed rocprofv3 counter
+                 readings when they were taken on the current kernel source
+  cpu_baseline - the float64 oracle's E-step on a bounded row sample of the
+                 same workload, on this host, single-threaded
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "E-step+stats points×components/s (N=1M,d=128,K=256); % of MFMA/HBM peak"
+UNIT = "points×components/s"
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+VAR_FLOOR = 1e-6
+KERNEL_SRC = os.path.join(ROOT, "soft_clustering_gmm_amd", "csrc", "gmm_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ref_estep_stats.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, if still current."""
+    if workload != "ref" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(X, mu, var, logw, rows: int):
+    """The oracle's E-step (as it stands) on the first `rows` rows, one thread."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    x = np.ascontiguousarray(X[:rows])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.estep(x, mu, var, logw)
+        dt = time.perf_counter() - t0
+    K = mu.shape[0]
+    return {"value": rows * K / dt, "unit": UNIT, "cores": 1, "kind": "oracle",
+            "sample": f"float64 oracle E-step + statistics (difference form, materialised R) on the first "
+                      f"{rows} of {X.shape[0]} rows, same parameters; {dt:.2f} s on 1 host thread"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ref", choices=["tiny", "ref", "smallk", "largek", "ivf"])
+    ap.add_argument("--cpu-rows", type=int, default=32768, help="row sample for the oracle baseline (0: skip)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this E-step build runs on a "
+              f"single MI355X; see the design notes for how it would shard over N.", file=sys.stderr)
+        return 2
+
+    import torch
+    from soft_clustering_gmm_amd import datagen, gmm
+    gmm.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+
+    w = datagen.WORKLOADS[args.workload]
+    X, mu, var, logw = datagen.make_workload(args.workload)
+    N, d, K = X.shape[0], X.shape[1], mu.shape[0]
+    Xd = torch.from_numpy(X).to(dev)
+    mu0, var0, lw0 = (torch.from_numpy(a.copy()).to(dev) for a in (mu, var, logw))
+    mud, vard, lwd = mu0.clone(), var0.clone(), lw0.clone()
+    ws = gmm.workspace(N, d, K, dev)
+    torch.cuda.synchronize()
+
+    def step():
+        mud.copy_(mu0)
+        vard.copy_(var0)
+        lwd.copy_(lw0)
+        gmm.em_iterate(Xd, mud, vard, lwd, 1, VAR_FLOOR, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:  # materialise the events
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        gmm.set_timing_events(*evs[i])
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = 1e3 * wall / args.steps
+    k_ms = [a.elapsed_time(b) for a, b in evs]
+    k_avg = float(np.mean(k_ms))
+    flops = 8.0 * N * K * d
+    xbytes = N * d * X.itemsize + K * (2 * d + 1) * 4
+    achieved = flops / (k_avg * 1e-3) / 1e12
+    single = K <= 256
+    roof = {
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": committed_traffic(args.workload),
+        "kernel": "estep_stats_kernel<4,0,float> (single sweep)" if single
+        else "estep_lse_kernel + estep_stats_kernel (two-pass)",
+        "flops_per_launch": flops, "avg_launch_ms": round(k_avg, 4),
+        "p90_launch_ms": round(float(np.percentile(k_ms, 90)), 4),
+        "hbm_algorithmic_bytes_per_launch": xbytes,
+        "hbm_achieved_GBps": round(xbytes / (k_avg * 1e-3) / 1e9, 1),
+        "hbm_frac": round(xbytes / (k_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+    }
+    out = {
+        "metric": METRIC, "value": N * K / (ms_step * 1e-3), "unit": UNIT, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: N={N} d={d} K={K} {w.x_dtype} Gaussian blobs (seed {w.seed}); "
+                               f"step = one EM iteration from the initial parameters (precompute, fused E-step+stats, "
+                               f"reduction, M-step)",
+                   "N": N, "d": d, "K": K, "x_dtype": w.x_dtype,
+                   "regime": "single-sweep" if single else "two-pass"},
+        "roofline": roof,
+    }
+    if args.cpu_rows > 0:
+        out["cpu_baseline"] = cpu_baseline(X, mu, var, logw, min(args.cpu_rows, N))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -115,6 +115,15 @@ int gmm_em_iterate(const void* X, int32_t x_dtype, int64_t N, int32_t d, int32_t
                    float var_floor, float* mu, float* var, float* logw, double* loglik_hist,
                    void* workspace, size_t ws_bytes, void* stream);
 
+/* Measurement aid (one-shot, per host thread): the next E-step enqueued by
+ * this thread through gmm_estep_stats, gmm_estep_stats_regime or
+ * gmm_em_iterate records `start` (a hipEvent_t) on its stream immediately
+ * before its fused E-step kernel(s) and `stop` immediately after them (before
+ * the small reduction kernels), then forgets both. Passing NULLs cancels a
+ * pending request. The events are the caller's; the library only records
+ * them. Always returns GMM_OK. */
+int gmm_set_timing_events(void* start, void* stop);
+
 /* Top-2 assignment for border-vector multi-assignment (Flash-GMM abstract:
  * responsibilities assign border vectors to several clusters). For each point:
  * idx[n][0], idx[n][1] = the two components with the largest s_nk (ties go to

@@ -212,6 +212,11 @@ int gmm_em_iterate(const void* X, int32_t x_dtype, int64_t N, int32_t d, int32_t
   return GMM_OK;
 }
 
+int gmm_set_timing_events(void* start, void* stop) {
+  set_timing_events(static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
+  return GMM_OK;
+}
+
 int gmm_assign_top2(const void* X, int32_t x_dtype, int64_t N, int32_t d, const float* mu, const float* var,
                     const float* logw, int32_t K, int32_t* idx, float* resp, void* workspace, size_t ws_bytes,
                     void* stream) {

@@ -57,6 +57,10 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan);
 // hipError_t from hipGetLastError().
 hipError_t launch_precompute(const Plan& p, const float* mu, const float* var, const float* logw,
                              hipStream_t stream);
+// One-shot timing events recorded around the fused E-step kernel(s) of the
+// next launch_estep on this thread (see gmm_set_timing_events).
+void set_timing_events(hipEvent_t start, hipEvent_t stop);
+
 hipError_t launch_estep(const Plan& p, const void* X, int x_dtype, const float* mu,
                         float* Nk, float* Sx, float* Sxx, double* loglik_total,
                         float* loglik_point, float* R, hipStream_t stream);

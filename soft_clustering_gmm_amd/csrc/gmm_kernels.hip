@@ -37,8 +37,10 @@ typedef double v4d __attribute__((ext_vector_type(4)));
 
 constexpr double kLog2Pi = 1.83787706640934548356065947281;
 constexpr float kWindow = 20.0f;   // re-score components with s >= max - kWindow
+constexpr float kExpWindow = 2.0611536e-9f;  // exp(-kWindow)
 constexpr float kGateTau = 5e-7f;  // re-score a row when 2 E_n * r_max could exceed this
 constexpr float kUnitRound = 5.9604644775390625e-8f;  // 2^-24
+constexpr int kRefCap = 128;       // re-score list entries per wave and pass
 
 // Row of the 32x32 MFMA accumulator held in slot j by lanes of half h:
 // D[row][col] with col = lane % 32 and row = 8*(j/4) + 4*h + j%4.
@@ -57,8 +59,60 @@ __device__ __forceinline__ double group_sum_d(double v, int tpr) {
   return v;
 }
 
+// Orders this wave's LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <typename XT>
 __device__ __forceinline__ float load_x(const XT* X, int64_t i) { return (float)X[i]; }
+
+// Asynchronous fp32 tile load: rows [r0, r0 + 64) of X -> LDS tile [64][XS]
+// with 16-byte global->LDS loads. One wave instruction fills 1 KB of LDS, i.e.
+// 64 consecutive 16-byte chunks of the padded row-major tile, so the tile is
+// XS/4 instructions spread over the waves. Chunks outside the data (the row
+// padding, features d..DP-1, rows past `hi`) receive finite filler copied
+// from a valid row: they only ever meet zero weights or r = 0.
+template <int XS>
+__device__ __forceinline__ void async_x_tile(float* xn, const float* X, int64_t r0, int64_t hi, int d,
+                                             int wave, int waves, int lane) {
+  constexpr int CPR = XS / 4;  // 16-byte chunks per LDS row
+  for (int j = wave; j < CPR; j += waves) {
+    const int ch = 64 * j + lane;
+    const int row = ch / CPR, slot = ch - row * CPR;
+    const int64_t gr = r0 + row < hi ? r0 + row : hi - 1;
+    const int q = 4 * slot < d ? slot : 0;
+    __builtin_amdgcn_global_load_lds(X + gr * d + 4 * q,
+                                     reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                         reinterpret_cast<uintptr_t>(xn + 256 * j)),
+                                     16, 0, 0);
+  }
+}
+
+// Rows [r0, r0 + 64) of X -> LDS tile [64][XS], zero padded to DP features
+// and past `hi`. `vec`: X rows are 16-byte aligned float rows (d % 4 == 0).
+template <int XS, typename XT>
+__device__ __forceinline__ void load_x_tile(float* xs, const XT* X, int64_t r0, int64_t hi, int d, int DP,
+                                            int tid, int nthr, int vec) {
+  if (vec && sizeof(XT) == 4) {
+    const float* Xf = reinterpret_cast<const float*>(X);
+    for (int ch = tid; ch < 16 * DP; ch += nthr) {
+      const int row = ch / (DP / 4), q = ch - row * (DP / 4);
+      const int64_t gr = r0 + row;
+      *reinterpret_cast<float4*>(xs + row * XS + 4 * q) =
+          (gr < hi && 4 * q < d) ? *reinterpret_cast<const float4*>(Xf + gr * d + 4 * q)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  } else {
+    for (int e = tid; e < 64 * DP; e += nthr) {
+      const int row = e / DP, f = e - row * DP;
+      const int64_t gr = r0 + row;
+      xs[row * XS + f] = (gr < hi && f < d) ? load_x(X, gr * d + f) : 0.f;
+    }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Parameter precompute (fp64 arithmetic)
@@ -176,7 +230,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
                    const float* __restrict__ mu, const double* __restrict__ iv64,
                    const double* __restrict__ c64d, const float* __restrict__ errc,
                    const float2* __restrict__ rowref, float* __restrict__ partials,
-                   double* __restrict__ llpart, float* __restrict__ ll_point, float* __restrict__ R) {
+                   double* __restrict__ llpart, float* __restrict__ ll_point, float* __restrict__ R,
+                   int vec) {
   constexpr int DP = 32 * DT, Q = DP / 4, XS = DP + 4, E = 1 + 2 * DP;
   extern __shared__ __align__(16) float smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
@@ -186,14 +241,14 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   const int slab = blockIdx.x - (int)(chunk * kslabs);
   const int k0 = slab * KS;
   const int kw = k0 + wave * 32;
-  float* xs = smem;              // [64][XS]
-  float* sc = xs + 64 * XS;      // [64][SCS]
+  float* xsb = smem;             // [2][64][XS]: current and next X tile
+  float* sc = xsb + 2 * 64 * XS; // [64][SCS]
   float* rv = sc + 64 * SCS;     // [64][2]
   double* lls = reinterpret_cast<double*>(rv + 128);  // [nthr]
+  uint32_t* reflist = reinterpret_cast<uint32_t*>(lls + nthr);  // [waves][kRefCap]
 
   const int tpr = waves;  // threads per row in the row phase
   const int prow = tid / tpr, psub = tid - prow * tpr;
-  const int lane_base = lane - psub;
   const float a_max = errc[0], b_max = errc[1], c_max = errc[2];
   const float gam = (float)(2 * DP + 8) * kUnitRound;
 
@@ -213,21 +268,20 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   const float4* Wt = W32p + (size_t)(kw >> 5) * Q * 64 + lane;
   const float ck = c32[kw + c];
 
+  // The next tile's X streams straight into the other LDS buffer (16-byte
+  // global->LDS loads) while the statistics MFMAs run.
+  const bool async_x = vec && sizeof(XT) == 4;
+  load_x_tile<XS>(xsb, X, lo, hi, d, DP, tid, nthr, vec);
+  int cur = 0;
   for (int64_t r0 = lo; r0 < hi; r0 += 64) {
+    float* xs = xsb + cur * 64 * XS;
     __syncthreads();
-    // 1. X tile
-    for (int e = tid; e < 64 * DP; e += nthr) {
-      const int row = e / DP, f = e - row * DP;
-      const int64_t gr = r0 + row;
-      xs[row * XS + f] = (gr < hi && f < d) ? load_x(X, gr * d + f) : 0.f;
-    }
     if (MODE == 1 && tid < 64) {
       const int64_t gr = r0 + tid;
       const float2 mr = gr < hi ? rowref[gr] : make_float2(0.f, 0.f);
       rv[2 * tid] = mr.x;
       rv[2 * tid + 1] = mr.y;
     }
-    __syncthreads();
 
     // 2. scores
     {
@@ -265,7 +319,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     }
     __syncthreads();
 
-    // 3. row phase
+    // 3. row phase. The score tile is rewritten in place: first to
+    //    e = exp(s - m) (MODE 0) or directly to r (MODE 1), then to r.
     {
       const int row = prow;
       const int64_t grow = r0 + row;
@@ -273,6 +328,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       float* srow = sc + row * SCS;
       const float* xrow = xs + row * XS;
       float sq = 0.f, ab = 0.f;
+#pragma unroll 4
       for (int f = psub; f < d; f += tpr) {
         const float x = xrow[f];
         sq += x * x;
@@ -282,86 +338,127 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       ab = group_sum(ab, tpr);
       const float Ebound = gam * (a_max * sq + b_max * ab + c_max);
 
-      float m;
-      double z = 0.0, lZd = 0.0;
+      float m, lZ = 0.f, thr;
+      double z = 0.0;
       if (MODE == 0) {
-        m = -INFINITY;
-#pragma unroll 1
-        for (int i = 0; i < 32; ++i) m = fmaxf(m, srow[psub + tpr * i]);
-        m = group_max(m, tpr);
-#pragma unroll 1
+        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll 4
+        for (int i = 0; i < 32; ++i) m4[i & 3] = fmaxf(m4[i & 3], srow[psub + tpr * i]);
+        m = group_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])), tpr);
+#pragma unroll 4
         for (int i = 0; i < 32; ++i) {
-          const float dl = srow[psub + tpr * i] - m;
-          srow[psub + tpr * i] = dl;
-          z += (double)expf(dl);
+          const float e = expf(srow[psub + tpr * i] - m);
+          srow[psub + tpr * i] = e;
+          z += (double)e;
         }
         z = group_sum_d(z, tpr);
+        thr = kExpWindow;  // e >= exp(-kWindow)
       } else {
         m = rv[2 * row];
-        lZd = (double)rv[2 * row + 1];
-#pragma unroll 1
-        for (int i = 0; i < 32; ++i) srow[psub + tpr * i] -= m;
+        lZ = rv[2 * row + 1];
+#pragma unroll 4
+        for (int i = 0; i < 32; ++i) srow[psub + tpr * i] = expf((srow[psub + tpr * i] - m) - lZ);
+        thr = kExpWindow * expf(-lZ);  // r >= exp(-kWindow - lZ)
       }
-      const float rmax = MODE == 0 ? (float)(1.0 / z) : expf(-(float)lZd);
+      const float rmax = MODE == 0 ? (float)(1.0 / z) : expf(-lZ);
       const bool refine = valid && (2.f * Ebound * rmax > kGateTau);
       uint32_t mask = 0;
       if (refine)
-#pragma unroll 1
+#pragma unroll 4
         for (int i = 0; i < 32; ++i)
-          if (srow[psub + tpr * i] >= -kWindow) mask |= 1u << i;
-      // Exact re-score of the window, one component at a time per row group;
-      // the group's threads split the features.
-      for (;;) {
-        const uint64_t bal = __ballot(mask != 0);
-        if (bal == 0) break;
-        const uint32_t gb = (uint32_t)(bal >> lane_base) & ((1u << tpr) - 1u);
-        const int owner = gb ? __ffs(gb) - 1 : 0;
-        const int myfirst = mask ? __ffs(mask) - 1 : 0;
-        const int oi = __shfl(myfirst, lane_base + owner, 64);
-        const int kl = owner + tpr * oi;
-        const int kg = k0 + kl;
-        double acc = 0.0;
-        if (gb) {
-          const float* mk = mu + (size_t)kg * d;
-          const double* ivk = iv64 + (size_t)kg * d;
-          for (int f = psub; f < d; f += tpr) {
-            const double t = (double)xrow[f] - (double)mk[f];
-            acc += t * t * ivk[f];
-          }
+          if (srow[psub + tpr * i] >= thr) mask |= 1u << i;
+      // Exact re-score of the window entries. Each wave pools the entries of
+      // its rows into an LDS list and re-scores four at a time, sixteen lanes
+      // per entry splitting the features (fp64, difference form).
+      if (MODE == 0 && psub == 0) rv[2 * row] = m;
+      {
+        const int cnt = __popc(mask);
+        int incl = cnt;
+        for (int o = 1; o < 64; o <<= 1) {
+          const int t = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += t;
         }
-        acc = group_sum_d(acc, tpr);
-        if (gb && psub == owner) {
-          const double s64 = c64d[kg] - 0.5 * acc;
-          srow[kl] = (float)(s64 - (double)m);
-          mask &= mask - 1u;
+        const int total = __shfl(incl, 63, 64);
+        const int base = incl - cnt;
+        uint32_t* wl = reflist + wave * kRefCap;
+        for (int p0 = 0; p0 < total; p0 += kRefCap) {
+          uint32_t m2 = mask;
+          int pos = base;
+          while (m2) {
+            const int i = __ffs(m2) - 1;
+            m2 &= m2 - 1u;
+            if (pos >= p0 && pos < p0 + kRefCap) wl[pos - p0] = ((uint32_t)row << 16) | (uint32_t)(psub + tpr * i);
+            ++pos;
+          }
+          wave_lds_sync();
+          const int n = min(total - p0, kRefCap);
+          for (int e0 = 0; e0 < n; e0 += 4) {
+            const int e = e0 + (lane >> 4), sl = lane & 15;
+            const bool act = e < n;
+            const uint32_t ent = act ? wl[e] : 0u;
+            const int er = (int)(ent >> 16), ek = (int)(ent & 0xffffu), kg = k0 + ek;
+            double acc = 0.0;
+            if (act) {
+              const float* xr = xs + er * XS;
+              const float* mk = mu + (size_t)kg * d;
+              const double* ivk = iv64 + (size_t)kg * d;
+              // unconditional (clamped) loads so that all of them are in flight at once
+#pragma unroll
+              for (int i = 0; i < DP / 16; ++i) {
+                const int f = sl + 16 * i;
+                const int fc = f < d ? f : d - 1;
+                const double t = (double)xr[fc] - (double)mk[fc];
+                const double w = f < d ? ivk[fc] : 0.0;
+                acc += t * t * w;
+              }
+            }
+            acc += __shfl_xor(acc, 1, 64);
+            acc += __shfl_xor(acc, 2, 64);
+            acc += __shfl_xor(acc, 4, 64);
+            acc += __shfl_xor(acc, 8, 64);
+            if (act && sl == 0) {
+              const double dl = (c64d[kg] - 0.5 * acc) - (double)rv[2 * er];  // exact s - m
+              sc[er * SCS + ek] = MODE == 0 ? expf((float)dl) : expf((float)(dl - (double)rv[2 * er + 1]));
+            }
+          }
+          wave_lds_sync();
         }
       }
       if (MODE == 0) {
         double z2 = 0.0;
         if (refine)
-#pragma unroll 1
-          for (int i = 0; i < 32; ++i) z2 += (double)expf(srow[psub + tpr * i]);
+#pragma unroll 4
+          for (int i = 0; i < 32; ++i) z2 += (double)srow[psub + tpr * i];
         z2 = group_sum_d(z2, tpr);
         if (refine) z = z2;
-        lZd = log(z);
+        // z is in [1, K]: an fp32 log is exact to ~1e-7 absolute, far inside the
+        // 1e-4 relative bar of l_n; r itself uses 1/z.
+        const double lZd = (double)logf((float)z);
+        const float invz = (float)(1.0 / z);
         if (valid && psub == 0) {
           const double l = (double)m + lZd;
           ll_acc += l;
           if (ll_point) ll_point[grow] = (float)l;
         }
-      }
-      const float lZ = (float)lZd;
+#pragma unroll 4
+        for (int i = 0; i < 32; ++i) srow[psub + tpr * i] = valid ? srow[psub + tpr * i] * invz : 0.f;
+      } else if (!valid) {
 #pragma unroll 1
-      for (int i = 0; i < 32; ++i) {
-        const int kl = psub + tpr * i;
-        const float r = valid ? expf(srow[kl] - lZ) : 0.f;
-        srow[kl] = r;
-        if (R && valid && k0 + kl < K) R[grow * K + k0 + kl] = r;
+        for (int i = 0; i < 32; ++i) srow[psub + tpr * i] = 0.f;
       }
+      if (R && valid)
+#pragma unroll 1
+        for (int i = 0; i < 32; ++i) {
+          const int kl = psub + tpr * i;
+          if (k0 + kl < K) R[grow * K + k0 + kl] = srow[kl];
+        }
     }
     __syncthreads();
 
-    // 4. statistics
+    // 4. statistics, with the next X tile streaming into the other buffer
+    const int64_t rn = r0 + 64;
+    if (async_x && rn < hi) async_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, reinterpret_cast<const float*>(X),
+                                             rn, hi, d, wave, waves, lane);
 #pragma unroll 1
     for (int g = 0; g < 2; ++g) {
 #pragma unroll 2
@@ -380,6 +477,13 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         }
       }
     }
+    if (rn < hi) {
+      if (async_x)
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's async tile loads have landed
+      else
+        load_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, X, rn, hi, d, DP, tid, nthr, vec);
+    }
+    cur ^= 1;
   }
 
   // statistics partial of this (chunk, slab)
@@ -683,15 +787,17 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
   const Workspace& w = p.ws;
   const int nthr = p.waves * 64;
   const int KS = p.waves * 32;
-  const size_t lds = (size_t)(64 * (32 * DT + 4) + 64 * (KS + 8) + 128) * sizeof(float) + (size_t)nthr * sizeof(double);
+  const size_t lds = (size_t)(2 * 64 * (32 * DT + 4) + 64 * (KS + 8) + 128) * sizeof(float) +
+                     (size_t)nthr * sizeof(double) + (size_t)p.waves * kRefCap * sizeof(uint32_t);
   auto fn = estep_stats_kernel<DT, MODE, XT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(p.P * p.kslabs);
+  const int vec = (sizeof(XT) == 4 && p.d % 4 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0) ? 1 : 0;
   fn<<<grid, nthr, lds, stream>>>(X, p.N, p.d, p.K, p.Kp, p.waves, p.kslabs, p.rows_per_chunk,
                                   reinterpret_cast<const float4*>(w.W32p), w.c32, mu, w.iv64, w.c64d, w.errc,
-                                  w.rowref, w.partials, w.llpart, ll_point, R);
+                                  w.rowref, w.partials, w.llpart, ll_point, R, vec);
   return hipGetLastError();
 }
 
@@ -733,12 +839,25 @@ static hipError_t estep_typed(const Plan& p, const XT* X, const float* mu, float
   return e;
 }
 
+static thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+void set_timing_events(hipEvent_t start, hipEvent_t stop) {
+  t_ev_start = start;
+  t_ev_stop = stop;
+}
+
 hipError_t launch_estep(const Plan& p, const void* X, int x_dtype, const float* mu, float* Nk, float* Sx,
                         float* Sxx, double* loglik_total, float* loglik_point, float* R, hipStream_t stream) {
   if (p.N == 0) return launch_zero_outputs(Nk, Sx, Sxx, p.d, p.K, loglik_total, stream);
-  hipError_t e = x_dtype == 1
-                     ? estep_typed(p, reinterpret_cast<const _Float16*>(X), mu, loglik_point, R, stream)
-                     : estep_typed(p, reinterpret_cast<const float*>(X), mu, loglik_point, R, stream);
+  hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
+  t_ev_start = t_ev_stop = nullptr;
+  hipError_t e = hipSuccess;
+  if (ev0) e = hipEventRecord(ev0, stream);
+  if (e != hipSuccess) return e;
+  e = x_dtype == 1 ? estep_typed(p, reinterpret_cast<const _Float16*>(X), mu, loglik_point, R, stream)
+                   : estep_typed(p, reinterpret_cast<const float*>(X), mu, loglik_point, R, stream);
+  if (e != hipSuccess) return e;
+  if (ev1) e = hipEventRecord(ev1, stream);
   if (e != hipSuccess) return e;
   const Workspace& w = p.ws;
   if (Nk && Sx && Sxx) {

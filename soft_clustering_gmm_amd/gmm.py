@@ -22,6 +22,7 @@ REGIME_AUTO, REGIME_SINGLE, REGIME_TWOPASS = 0, 1, 2
 EXPORTS = (
     "gmm_version", "gmm_error_string", "gmm_workspace_bytes", "gmm_estep_stats",
     "gmm_estep_stats_regime", "gmm_estep_resp", "gmm_mstep", "gmm_em_iterate", "gmm_assign_top2",
+    "gmm_set_timing_events",
 )
 
 
@@ -55,6 +56,8 @@ def _load() -> ctypes.CDLL:
     L.gmm_em_iterate.argtypes = [P, I32, I64, I32, I32, I32, F32, P, P, P, P, P, SZ, P]
     L.gmm_assign_top2.restype = ctypes.c_int
     L.gmm_assign_top2.argtypes = [P, I32, I64, I32, P, P, P, I32, P, P, P, SZ, P]
+    L.gmm_set_timing_events.restype = ctypes.c_int
+    L.gmm_set_timing_events.argtypes = [P, P]
     return L
 
 
@@ -183,6 +186,14 @@ def em_iterate(X, mu, var, logw, iters: int, var_floor: float, *, ws=None):
         _ptr(X), _xtype(X), N, d, K, iters, float(var_floor), _ptr(mu), _ptr(var), _ptr(logw),
         _ptr(hist), _ptr(ws), ws.numel(), _stream(dev)))
     return hist[:iters]
+
+
+def set_timing_events(start, stop) -> None:
+    """One-shot: the next E-step on this thread records these torch.cuda.Events
+    (already created, e.g. by one record()) around its fused kernel(s)."""
+    _check("gmm_set_timing_events", lib().gmm_set_timing_events(
+        None if start is None else ctypes.c_void_p(start.cuda_event),
+        None if stop is None else ctypes.c_void_p(stop.cuda_event)))
 
 
 def assign_top2(X, mu, var, logw, *, ws=None):
