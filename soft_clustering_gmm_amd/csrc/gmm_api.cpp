@@ -50,6 +50,9 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
                                  : 256 * std::max(1, 8 / p.waves);
   target = std::max<int64_t>(1, std::min<int64_t>(target, p.tiles));
   p.rows_per_chunk = ceil_div(std::max<int64_t>(p.tiles, 1), target) * kTileN;
+  // Each chunk accumulates its statistics in fp32 MFMA accumulators; capping
+  // its rows keeps that accumulation error near 1e-5 relative.
+  p.rows_per_chunk = std::min<int64_t>(p.rows_per_chunk, kMaxChunkRows);
   p.P = N == 0 ? 0 : ceil_div(N, p.rows_per_chunk);
 
   size_t off = 0;

@@ -15,6 +15,7 @@ constexpr int kMaxK = 65536;
 constexpr int kSlabWaves = 8;        // waves (x32 components) per two-pass slab
 constexpr int kSingleMaxK = 256;     // largest K the single sweep keeps on chip
 constexpr int kLseWaves = 4;         // waves per block in the fp64 normaliser pass
+constexpr int64_t kMaxChunkRows = 32768;  // rows per statistics partial, at most
 
 // Device pointers into the caller's workspace, filled by gmm::plan().
 struct Workspace {

@@ -118,21 +118,25 @@ __device__ __forceinline__ void load_x_tile(float* xs, const XT* X, int64_t r0, 
 // Parameter precompute (fp64 arithmetic)
 // ---------------------------------------------------------------------------
 
-// One thread per (padded) component: the score constants and the inputs of
-// the fp32 error bound.
+// One wave per (padded) component: the score constants and the inputs of
+// the fp32 error bound; lanes stride over the features and reduce in a fixed
+// order.
 __global__ void comp_consts_kernel(const float* __restrict__ mu, const float* __restrict__ var,
                                    const float* __restrict__ logw, int K, int d, int Kp, int Kp16,
                                    float* __restrict__ c32, double* __restrict__ c64e,
                                    double* __restrict__ c64d, float* __restrict__ compmax) {
-  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  const int k = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (k >= Kp) return;
   if (k >= K) {
-    c32[k] = -INFINITY;
-    if (k < Kp16) c64e[k] = -INFINITY;
+    if (lane == 0) {
+      c32[k] = -INFINITY;
+      if (k < Kp16) c64e[k] = -INFINITY;
+    }
     return;
   }
   double slv = 0.0, sm2 = 0.0, amax = 0.0, bmax = 0.0;
-  for (int j = 0; j < d; ++j) {
+  for (int j = lane; j < d; j += 64) {
     const double v = var[(size_t)k * d + j], m = mu[(size_t)k * d + j];
     const double iv = 1.0 / v;
     slv += log(v);
@@ -140,14 +144,22 @@ __global__ void comp_consts_kernel(const float* __restrict__ mu, const float* __
     amax = fmax(amax, 0.5 * iv);
     bmax = fmax(bmax, fabs(m * iv));
   }
-  const double cd = (double)logw[k] - 0.5 * ((double)d * kLog2Pi + slv);
-  const double ce = cd - 0.5 * sm2;
-  c64d[k] = cd;
-  c64e[k] = ce;
-  c32[k] = (float)ce;
-  compmax[3 * k + 0] = (float)amax;
-  compmax[3 * k + 1] = (float)bmax;
-  compmax[3 * k + 2] = isfinite(ce) ? (float)fabs(ce) : 0.0f;
+  for (int o = 32; o > 0; o >>= 1) {
+    slv += __shfl_xor(slv, o, 64);
+    sm2 += __shfl_xor(sm2, o, 64);
+    amax = fmax(amax, __shfl_xor(amax, o, 64));
+    bmax = fmax(bmax, __shfl_xor(bmax, o, 64));
+  }
+  if (lane == 0) {
+    const double cd = (double)logw[k] - 0.5 * ((double)d * kLog2Pi + slv);
+    const double ce = cd - 0.5 * sm2;
+    c64d[k] = cd;
+    c64e[k] = ce;
+    c32[k] = (float)ce;
+    compmax[3 * k + 0] = (float)amax;
+    compmax[3 * k + 1] = (float)bmax;
+    compmax[3 * k + 2] = isfinite(ce) ? (float)fabs(ce) : 0.0f;
+  }
 }
 
 // One thread per (component, feature) over Kp x DP: packed MFMA operands.
@@ -338,26 +350,43 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       ab = group_sum(ab, tpr);
       const float Ebound = gam * (a_max * sq + b_max * ab + c_max);
 
+      // Each thread owns the 16-byte chunks psub + tpr*i (i < 8) of its row,
+      // i.e. components 4*(psub + tpr*i) + u, u < 4; bit 4i+u of `mask`.
+      float4* srow4 = reinterpret_cast<float4*>(srow);
       float m, lZ = 0.f, thr;
       double z = 0.0;
       if (MODE == 0) {
-        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        float mx = -INFINITY;
 #pragma unroll 4
-        for (int i = 0; i < 32; ++i) m4[i & 3] = fmaxf(m4[i & 3], srow[psub + tpr * i]);
-        m = group_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])), tpr);
-#pragma unroll 4
-        for (int i = 0; i < 32; ++i) {
-          const float e = expf(srow[psub + tpr * i] - m);
-          srow[psub + tpr * i] = e;
-          z += (double)e;
+        for (int i = 0; i < 8; ++i) {
+          const float4 v = srow4[psub + tpr * i];
+          mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+        }
+        m = group_max(mx, tpr);
+#pragma unroll 2
+        for (int i = 0; i < 8; ++i) {
+          float4 v = srow4[psub + tpr * i];
+          v.x = expf(v.x - m);
+          v.y = expf(v.y - m);
+          v.z = expf(v.z - m);
+          v.w = expf(v.w - m);
+          srow4[psub + tpr * i] = v;
+          z += ((double)v.x + (double)v.y) + ((double)v.z + (double)v.w);
         }
         z = group_sum_d(z, tpr);
         thr = kExpWindow;  // e >= exp(-kWindow)
       } else {
         m = rv[2 * row];
         lZ = rv[2 * row + 1];
-#pragma unroll 4
-        for (int i = 0; i < 32; ++i) srow[psub + tpr * i] = expf((srow[psub + tpr * i] - m) - lZ);
+#pragma unroll 2
+        for (int i = 0; i < 8; ++i) {
+          float4 v = srow4[psub + tpr * i];
+          v.x = expf((v.x - m) - lZ);
+          v.y = expf((v.y - m) - lZ);
+          v.z = expf((v.z - m) - lZ);
+          v.w = expf((v.w - m) - lZ);
+          srow4[psub + tpr * i] = v;
+        }
         thr = kExpWindow * expf(-lZ);  // r >= exp(-kWindow - lZ)
       }
       const float rmax = MODE == 0 ? (float)(1.0 / z) : expf(-lZ);
@@ -365,8 +394,13 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       uint32_t mask = 0;
       if (refine)
 #pragma unroll 4
-        for (int i = 0; i < 32; ++i)
-          if (srow[psub + tpr * i] >= thr) mask |= 1u << i;
+        for (int i = 0; i < 8; ++i) {
+          const float4 v = srow4[psub + tpr * i];
+          mask |= (v.x >= thr ? 1u : 0u) << (4 * i);
+          mask |= (v.y >= thr ? 1u : 0u) << (4 * i + 1);
+          mask |= (v.z >= thr ? 1u : 0u) << (4 * i + 2);
+          mask |= (v.w >= thr ? 1u : 0u) << (4 * i + 3);
+        }
       // Exact re-score of the window entries. Each wave pools the entries of
       // its rows into an LDS list and re-scores four at a time, sixteen lanes
       // per entry splitting the features (fp64, difference form).
@@ -387,7 +421,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           while (m2) {
             const int i = __ffs(m2) - 1;
             m2 &= m2 - 1u;
-            if (pos >= p0 && pos < p0 + kRefCap) wl[pos - p0] = ((uint32_t)row << 16) | (uint32_t)(psub + tpr * i);
+            if (pos >= p0 && pos < p0 + kRefCap)
+              wl[pos - p0] = ((uint32_t)row << 16) | (uint32_t)(4 * (psub + tpr * (i >> 2)) + (i & 3));
             ++pos;
           }
           wave_lds_sync();
@@ -428,28 +463,38 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         double z2 = 0.0;
         if (refine)
 #pragma unroll 4
-          for (int i = 0; i < 32; ++i) z2 += (double)srow[psub + tpr * i];
+          for (int i = 0; i < 8; ++i) {
+            const float4 v = srow4[psub + tpr * i];
+            z2 += ((double)v.x + (double)v.y) + ((double)v.z + (double)v.w);
+          }
         z2 = group_sum_d(z2, tpr);
         if (refine) z = z2;
         // z is in [1, K]: an fp32 log is exact to ~1e-7 absolute, far inside the
         // 1e-4 relative bar of l_n; r itself uses 1/z.
         const double lZd = (double)logf((float)z);
-        const float invz = (float)(1.0 / z);
+        const float invz = valid ? (float)(1.0 / z) : 0.f;
         if (valid && psub == 0) {
           const double l = (double)m + lZd;
           ll_acc += l;
           if (ll_point) ll_point[grow] = (float)l;
         }
 #pragma unroll 4
-        for (int i = 0; i < 32; ++i) srow[psub + tpr * i] = valid ? srow[psub + tpr * i] * invz : 0.f;
+        for (int i = 0; i < 8; ++i) {
+          float4 v = srow4[psub + tpr * i];
+          v.x *= invz;
+          v.y *= invz;
+          v.z *= invz;
+          v.w *= invz;
+          srow4[psub + tpr * i] = v;
+        }
       } else if (!valid) {
 #pragma unroll 1
-        for (int i = 0; i < 32; ++i) srow[psub + tpr * i] = 0.f;
+        for (int i = 0; i < 8; ++i) srow4[psub + tpr * i] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
       if (R && valid)
 #pragma unroll 1
         for (int i = 0; i < 32; ++i) {
-          const int kl = psub + tpr * i;
+          const int kl = 4 * (psub + tpr * (i >> 2)) + (i & 3);
           if (k0 + kl < K) R[grow * K + k0 + kl] = srow[kl];
         }
     }
@@ -773,7 +818,7 @@ static inline unsigned nblocks(int64_t n, int b) { return (unsigned)((n + b - 1)
 hipError_t launch_precompute(const Plan& p, const float* mu, const float* var, const float* logw,
                              hipStream_t stream) {
   const Workspace& w = p.ws;
-  comp_consts_kernel<<<nblocks(p.Kp, 256), 256, 0, stream>>>(mu, var, logw, p.K, p.d, p.Kp, p.Kp16, w.c32,
+  comp_consts_kernel<<<nblocks(p.Kp, 4), 256, 0, stream>>>(mu, var, logw, p.K, p.d, p.Kp, p.Kp16, w.c32,
                                                                w.c64e, w.c64d, w.compmax);
   pack_kernel<<<nblocks((int64_t)p.Kp * p.DP, 256), 256, 0, stream>>>(mu, var, p.K, p.d, p.Kp, p.Kp16, p.DP,
                                                                         w.W32p, w.W64p, w.iv64);
