@@ -67,7 +67,7 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
   const size_t o_c64e = take((size_t)p.Kp16 * sizeof(double));
   const size_t o_iv64 = take((size_t)K * d * sizeof(double));
   const size_t o_c64d = take((size_t)K * sizeof(double));
-  const size_t o_cmax = take((size_t)K * 3 * sizeof(float));
+  const size_t o_cmax = take((size_t)K * 4 * sizeof(float));
   const size_t o_errc = take(4 * sizeof(float));
   const size_t o_rowref = take((size_t)std::max<int64_t>(N, 1) * sizeof(float2));
   const size_t o_part = take((size_t)std::max<int64_t>(p.P, 1) * p.Kp * p.E * sizeof(float));

@@ -39,7 +39,9 @@ constexpr double kLog2Pi = 1.83787706640934548356065947281;
 constexpr float kWindow = 20.0f;   // re-score components with s >= max - kWindow
 constexpr float kExpWindow = 2.0611536e-9f;  // exp(-kWindow)
 constexpr float kGateTau = 5e-7f;  // re-score a row when 2 E_n * r_max could exceed this
-constexpr float kUnitRound = 5.9604644775390625e-8f;  // 2^-24
+// Per-operation relative error assumed for fp32 arithmetic in the bound below:
+// 2^-23, which also covers an accumulator that truncates rather than rounds.
+constexpr float kUnitRound = 1.1920928955078125e-7f;
 constexpr int kRefCap = 128;       // re-score list entries per wave and pass
 
 // Row of the 32x32 MFMA accumulator held in slot j by lanes of half h:
@@ -135,7 +137,7 @@ __global__ void comp_consts_kernel(const float* __restrict__ mu, const float* __
     }
     return;
   }
-  double slv = 0.0, sm2 = 0.0, amax = 0.0, bmax = 0.0;
+  double slv = 0.0, sm2 = 0.0, amax = 0.0, bmax = 0.0, b2 = 0.0;
   for (int j = lane; j < d; j += 64) {
     const double v = var[(size_t)k * d + j], m = mu[(size_t)k * d + j];
     const double iv = 1.0 / v;
@@ -143,10 +145,12 @@ __global__ void comp_consts_kernel(const float* __restrict__ mu, const float* __
     sm2 += m * m * iv;
     amax = fmax(amax, 0.5 * iv);
     bmax = fmax(bmax, fabs(m * iv));
+    b2 += (m * iv) * (m * iv);
   }
   for (int o = 32; o > 0; o >>= 1) {
     slv += __shfl_xor(slv, o, 64);
     sm2 += __shfl_xor(sm2, o, 64);
+    b2 += __shfl_xor(b2, o, 64);
     amax = fmax(amax, __shfl_xor(amax, o, 64));
     bmax = fmax(bmax, __shfl_xor(bmax, o, 64));
   }
@@ -156,9 +160,10 @@ __global__ void comp_consts_kernel(const float* __restrict__ mu, const float* __
     c64d[k] = cd;
     c64e[k] = ce;
     c32[k] = (float)ce;
-    compmax[3 * k + 0] = (float)amax;
-    compmax[3 * k + 1] = (float)bmax;
-    compmax[3 * k + 2] = isfinite(ce) ? (float)fabs(ce) : 0.0f;
+    compmax[4 * k + 0] = (float)amax;
+    compmax[4 * k + 1] = (float)bmax;
+    compmax[4 * k + 2] = isfinite(ce) ? (float)fabs(ce) : 0.0f;
+    compmax[4 * k + 3] = (float)sqrt(b2);
   }
 }
 
@@ -194,30 +199,21 @@ __global__ void pack_kernel(const float* __restrict__ mu, const float* __restric
   }
 }
 
-// One block: global maxima of the per-component error-bound inputs.
+// One block: global maxima of the per-component error-bound inputs
+// errc = {max |A_kj|, max |B_kj|, max |c_k|, max_k ||B_k||_2}.
 __global__ void errc_kernel(const float* __restrict__ compmax, int K, float* __restrict__ errc) {
-  __shared__ float s[3][256];
-  float a = 0.f, b = 0.f, c = 0.f;
-  for (int k = threadIdx.x; k < K; k += blockDim.x) {
-    a = fmaxf(a, compmax[3 * k]);
-    b = fmaxf(b, compmax[3 * k + 1]);
-    c = fmaxf(c, compmax[3 * k + 2]);
-  }
-  s[0][threadIdx.x] = a;
-  s[1][threadIdx.x] = b;
-  s[2][threadIdx.x] = c;
+  __shared__ float s[4][256];
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = threadIdx.x; k < K; k += blockDim.x)
+    for (int i = 0; i < 4; ++i) v[i] = fmaxf(v[i], compmax[4 * k + i]);
+  for (int i = 0; i < 4; ++i) s[i][threadIdx.x] = v[i];
   __syncthreads();
   for (int o = blockDim.x / 2; o > 0; o >>= 1) {
     if ((int)threadIdx.x < o)
-      for (int i = 0; i < 3; ++i) s[i][threadIdx.x] = fmaxf(s[i][threadIdx.x], s[i][threadIdx.x + o]);
+      for (int i = 0; i < 4; ++i) s[i][threadIdx.x] = fmaxf(s[i][threadIdx.x], s[i][threadIdx.x + o]);
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    errc[0] = s[0][0];
-    errc[1] = s[1][0];
-    errc[2] = s[2][0];
-    errc[3] = 0.f;
-  }
+  if (threadIdx.x < 4) errc[threadIdx.x] = s[threadIdx.x][0];
 }
 
 // ---------------------------------------------------------------------------
@@ -261,8 +257,12 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
 
   const int tpr = waves;  // threads per row in the row phase
   const int prow = tid / tpr, psub = tid - prow * tpr;
-  const float a_max = errc[0], b_max = errc[1], c_max = errc[2];
-  const float gam = (float)(2 * DP + 8) * kUnitRound;
+  const float a_max = errc[0], b_max = errc[1], c_max = errc[2], b2_max = errc[3];
+  // fp32 score error: the MFMA sums 2*DP products of rounded operands from
+  // zero, then c is added once, so
+  //   |s32 - s| <= (2*DP + 4) u sum_i |F_i W_i| + 2 u |c|,
+  //   sum_i |F_i W_i| <= a_max |x|^2 + min(b_max |x|_1, b2_max |x|_2).
+  const float gam = (float)(2 * DP + 4) * kUnitRound;
 
   v16f SX[DT], SXX[DT];
 #pragma unroll
@@ -348,12 +348,12 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       }
       sq = group_sum(sq, tpr);
       ab = group_sum(ab, tpr);
-      const float Ebound = gam * (a_max * sq + b_max * ab + c_max);
+      const float Ebound = gam * (a_max * sq + fminf(b_max * ab, b2_max * sqrtf(sq))) + 2.f * kUnitRound * c_max;
 
       // Each thread owns the 16-byte chunks psub + tpr*i (i < 8) of its row,
       // i.e. components 4*(psub + tpr*i) + u, u < 4; bit 4i+u of `mask`.
       float4* srow4 = reinterpret_cast<float4*>(srow);
-      float m, lZ = 0.f, thr;
+      float m, lZ = 0.f;
       double z = 0.0;
       if (MODE == 0) {
         float mx = -INFINITY;
@@ -374,7 +374,6 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           z += ((double)v.x + (double)v.y) + ((double)v.z + (double)v.w);
         }
         z = group_sum_d(z, tpr);
-        thr = kExpWindow;  // e >= exp(-kWindow)
       } else {
         m = rv[2 * row];
         lZ = rv[2 * row + 1];
@@ -387,20 +386,48 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           v.w = expf((v.w - m) - lZ);
           srow4[psub + tpr * i] = v;
         }
-        thr = kExpWindow * expf(-lZ);  // r >= exp(-kWindow - lZ)
       }
-      const float rmax = MODE == 0 ? (float)(1.0 / z) : expf(-lZ);
-      const bool refine = valid && (2.f * Ebound * rmax > kGateTau);
+      // Which entries need the exact re-score (E = Ebound, r_k = e_k / z):
+      //  MODE 0: an unrefined entry is off by <= 2 E r_k, so every entry with
+      //   r_k > tau/(2E) is refined; the refined ones are then off by at most
+      //   E * U, U = unrefined mass, which must stay <= tau, else the window
+      //   widens to every entry within kWindow of the maximum.
+      //  MODE 1: l_n comes from the exact first pass, so an unrefined entry is
+      //   off by <= E r_k and entries with r_k > tau/E are refined.
+      // With the max entry below the threshold the row needs nothing.
+      float thr = MODE == 0 ? kGateTau * (float)z / (2.f * Ebound) : kGateTau / Ebound;
+      const float top = MODE == 0 ? 1.f : expf(-lZ);  // largest e (MODE 0) or r (MODE 1)
+      const bool refine = valid && (top > thr);
       uint32_t mask = 0;
+      double unref = 0.0;
       if (refine)
 #pragma unroll 4
         for (int i = 0; i < 8; ++i) {
           const float4 v = srow4[psub + tpr * i];
-          mask |= (v.x >= thr ? 1u : 0u) << (4 * i);
-          mask |= (v.y >= thr ? 1u : 0u) << (4 * i + 1);
-          mask |= (v.z >= thr ? 1u : 0u) << (4 * i + 2);
-          mask |= (v.w >= thr ? 1u : 0u) << (4 * i + 3);
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (vv[u] >= thr)
+              mask |= 1u << (4 * i + u);
+            else
+              unref += (double)vv[u];
+          }
         }
+      if (MODE == 0) {
+        unref = group_sum_d(unref, tpr);
+        if (refine && (double)Ebound * unref / z > (double)kGateTau) {
+          thr = kExpWindow;
+          mask = 0;
+#pragma unroll 4
+          for (int i = 0; i < 8; ++i) {
+            const float4 v = srow4[psub + tpr * i];
+            mask |= (v.x >= thr ? 1u : 0u) << (4 * i);
+            mask |= (v.y >= thr ? 1u : 0u) << (4 * i + 1);
+            mask |= (v.z >= thr ? 1u : 0u) << (4 * i + 2);
+            mask |= (v.w >= thr ? 1u : 0u) << (4 * i + 3);
+          }
+        }
+      }
       // Exact re-score of the window entries. Each wave pools the entries of
       // its rows into an LDS list and re-scores four at a time, sixteen lanes
       // per entry splitting the features (fp64, difference form).

@@ -81,6 +81,23 @@ def test_estep_edge_shapes(G, N, d, K):
         _run_and_check(G, X, mu, var, logw, r, f"edge N={N} d={d} K={K} regime={r}")
 
 
+def test_near_tie_pairs_with_large_scores(G):
+    """Pairs of almost identical components and |s| ~ 10^3: r ~ 0.5 on many rows,
+    far beyond what fp32 scores alone resolve to 1e-5; the re-score must catch it."""
+    rng = np.random.default_rng(21)
+    K2, d, N = 32, 128, 2000
+    C = rng.normal(0, 6, (K2, d))
+    mu = np.concatenate([C, C + rng.normal(0, 2e-3, C.shape)]).astype(np.float32)
+    var = np.concatenate([np.full((K2, d), 0.5), np.full((K2, d), 0.5)]).astype(np.float32)
+    logw = np.full(2 * K2, -np.log(2 * K2), np.float32)
+    lab = rng.integers(0, K2, N)
+    X = (C[lab] + rng.normal(0, 1.5, (N, d))).astype(np.float32)
+    S = oracle.component_scores(X, mu, var, logw)
+    assert np.abs(S).max() > 500
+    for r in (1, 2):
+        _run_and_check(G, X, mu, var, logw, r, f"near-tie pairs regime={r}")
+
+
 def test_estep_empty_input(G):
     X = torch.zeros(0, 4, device="cuda")
     mu = torch.zeros(3, 4, device="cuda")
