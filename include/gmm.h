@@ -53,9 +53,12 @@ enum gmm_status {
 enum gmm_dtype { GMM_F32 = 0, GMM_F16 = 1 };
 
 /* Regime of the E-step (Turbo-GMM abstract: a single sweep over the component
- * axis kept on chip when it fits, a two-pass fallback otherwise). AUTO takes
- * the single sweep for K <= 256 and two passes above. */
-enum gmm_regime { GMM_REGIME_AUTO = 0, GMM_REGIME_SINGLE = 1, GMM_REGIME_TWOPASS = 2 };
+ * axis kept on chip when it fits, a two-pass fallback otherwise).
+ *   SINGLE  - single sweep, 32-component tiles, K <= 256
+ *   TWOPASS - normalisers first (exact fp64 pass), then statistics; any K
+ *   SMALLK  - single sweep with 16-component tiles, K <= 16 and d <= 64
+ * AUTO takes SMALLK when it applies, else SINGLE for K <= 256, else TWOPASS. */
+enum gmm_regime { GMM_REGIME_AUTO = 0, GMM_REGIME_SINGLE = 1, GMM_REGIME_TWOPASS = 2, GMM_REGIME_SMALLK = 3 };
 
 /* Library version, major*10000 + minor*100 + patch. */
 int gmm_version(void);
@@ -83,7 +86,8 @@ int gmm_estep_stats(const void* X, int32_t x_dtype, int64_t N, int32_t d,
                     double* loglik_total, float* loglik_point,
                     void* workspace, size_t ws_bytes, void* stream);
 
-/* gmm_estep_stats with the regime forced (GMM_REGIME_SINGLE needs K <= 256). */
+/* gmm_estep_stats with the regime forced (GMM_REGIME_SINGLE needs K <= 256,
+ * GMM_REGIME_SMALLK needs K <= 16 and d <= 64; otherwise GMM_EUNSUPPORTED). */
 int gmm_estep_stats_regime(const void* X, int32_t x_dtype, int64_t N, int32_t d,
                            const float* mu, const float* var, const float* logw, int32_t K,
                            float* Nk, float* Sx, float* Sxx,

@@ -22,38 +22,55 @@ static int pow2_waves(int K) {
 int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
   if (N < 0 || d < 1 || K < 1) return GMM_EINVAL;
   if (d > kMaxD || K > kMaxK || N >= ((int64_t)1 << 40)) return GMM_EUNSUPPORTED;
-  if (regime < GMM_REGIME_AUTO || regime > GMM_REGIME_TWOPASS) return GMM_EINVAL;
-  if (regime == GMM_REGIME_AUTO) regime = K <= kSingleMaxK ? GMM_REGIME_SINGLE : GMM_REGIME_TWOPASS;
+  if (regime < GMM_REGIME_AUTO || regime > GMM_REGIME_SMALLK) return GMM_EINVAL;
+  const bool small_ok = K <= kSmallMaxK && d <= kSmallMaxD;
+  if (regime == GMM_REGIME_AUTO)
+    regime = small_ok ? GMM_REGIME_SMALLK : K <= kSingleMaxK ? GMM_REGIME_SINGLE : GMM_REGIME_TWOPASS;
   if (regime == GMM_REGIME_SINGLE && K > kSingleMaxK) return GMM_EUNSUPPORTED;
+  if (regime == GMM_REGIME_SMALLK && !small_ok) return GMM_EUNSUPPORTED;
 
   Plan p{};
   p.N = N;
   p.d = d;
   p.K = K;
-  p.DT = (d + 31) / 32;
-  p.DP = 32 * p.DT;
   p.regime = regime;
-  if (K <= kSingleMaxK) {
-    p.waves = pow2_waves(K);
+  p.tiles = ceil_div(N, kTileN);
+  if (regime == GMM_REGIME_SMALLK) {
+    // 16-component tiles; each wave streams its own rows in 64-point tiles.
+    p.DT = 0;
+    p.DP = 16 * (int)ceil_div(d, 16);
+    p.waves = kSmallWaves;
     p.kslabs = 1;
+    p.Kp = 16;
+    const int64_t blocks = 256 * 2;  // two 4-wave blocks per CU (LDS-bound)
+    int64_t wave_rows = ceil_div(std::max<int64_t>(ceil_div(N, blocks * kSmallWaves), 1), 64) * 64;
+    wave_rows = std::min<int64_t>(wave_rows, kMaxChunkRows / kSmallWaves);
+    p.rows_per_chunk = wave_rows * kSmallWaves;
+    p.P = N == 0 ? 0 : ceil_div(N, p.rows_per_chunk);
   } else {
-    p.waves = kSlabWaves;
-    p.kslabs = (int)ceil_div(K, 32 * kSlabWaves);
+    p.DT = (d + 31) / 32;
+    p.DP = 32 * p.DT;
+    if (K <= kSingleMaxK) {
+      p.waves = pow2_waves(K);
+      p.kslabs = 1;
+    } else {
+      p.waves = kSlabWaves;
+      p.kslabs = (int)ceil_div(K, 32 * kSlabWaves);
+    }
+    p.Kp = 32 * p.waves * p.kslabs;
+    // Row chunks: one statistics partial per chunk. Aim for one resident block
+    // per SIMD-set (8 waves per CU) across 256 CUs.
+    int64_t target = p.kslabs > 1 ? std::max<int64_t>(1, 256 / p.kslabs)
+                                   : 256 * std::max(1, 8 / p.waves);
+    target = std::max<int64_t>(1, std::min<int64_t>(target, p.tiles));
+    p.rows_per_chunk = ceil_div(std::max<int64_t>(p.tiles, 1), target) * kTileN;
+    // Each chunk accumulates its statistics in fp32 MFMA accumulators; capping
+    // its rows keeps that accumulation error near 1e-5 relative.
+    p.rows_per_chunk = std::min<int64_t>(p.rows_per_chunk, kMaxChunkRows);
+    p.P = N == 0 ? 0 : ceil_div(N, p.rows_per_chunk);
   }
-  p.Kp = 32 * p.waves * p.kslabs;
   p.Kp16 = (int)ceil_div(K, 16) * 16;
   p.E = 1 + 2 * p.DP;
-  p.tiles = ceil_div(N, kTileN);
-  // Row chunks: one statistics partial per chunk. Aim for one resident block
-  // per SIMD-set (8 waves per CU) across 256 CUs.
-  int64_t target = p.kslabs > 1 ? std::max<int64_t>(1, 256 / p.kslabs)
-                                 : 256 * std::max(1, 8 / p.waves);
-  target = std::max<int64_t>(1, std::min<int64_t>(target, p.tiles));
-  p.rows_per_chunk = ceil_div(std::max<int64_t>(p.tiles, 1), target) * kTileN;
-  // Each chunk accumulates its statistics in fp32 MFMA accumulators; capping
-  // its rows keeps that accumulation error near 1e-5 relative.
-  p.rows_per_chunk = std::min<int64_t>(p.rows_per_chunk, kMaxChunkRows);
-  p.P = N == 0 ? 0 : ceil_div(N, p.rows_per_chunk);
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -61,7 +78,8 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
     off = align_up(off + bytes, 256);
     return o;
   };
-  const size_t o_W32p = take((size_t)p.Kp * 2 * p.DP * sizeof(float));
+  // the fp32 operand layout is built in whole 32-component tiles
+  const size_t o_W32p = take((size_t)ceil_div(p.Kp, 32) * 32 * 2 * p.DP * sizeof(float));
   const size_t o_c32 = take((size_t)p.Kp * sizeof(float));
   const size_t o_W64p = take((size_t)p.Kp16 * 2 * p.DP * sizeof(double));
   const size_t o_c64e = take((size_t)p.Kp16 * sizeof(double));
@@ -95,7 +113,7 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
 
 static size_t workspace_bytes(int64_t N, int d, int K) {
   size_t best = 0;
-  for (int r = GMM_REGIME_SINGLE; r <= GMM_REGIME_TWOPASS; ++r) {
+  for (int r = GMM_REGIME_SINGLE; r <= GMM_REGIME_SMALLK; ++r) {
     Plan p;
     if (make_plan(N, d, K, r, nullptr, &p) == GMM_OK) best = std::max(best, p.bytes);
   }
@@ -132,7 +150,8 @@ const char* gmm_error_string(int code) {
   switch (code) {
     case GMM_OK: return "ok";
     case GMM_EINVAL: return "invalid argument (null pointer, negative size, bad dtype or regime)";
-    case GMM_EUNSUPPORTED: return "unsupported shape or regime (1<=d<=128, 1<=K<=65536; single sweep needs K<=256)";
+    case GMM_EUNSUPPORTED:
+      return "unsupported shape or regime (1<=d<=128, 1<=K<=65536; single sweep needs K<=256, small-K K<=16 and d<=64)";
     case GMM_EWORKSPACE: return "workspace missing, misaligned (256 B) or smaller than gmm_workspace_bytes()";
     case GMM_EHIP: return "HIP launch failed";
     default: return "unknown status";

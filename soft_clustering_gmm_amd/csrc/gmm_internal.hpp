@@ -14,7 +14,10 @@ constexpr int kMaxD = 128;
 constexpr int kMaxK = 65536;
 constexpr int kSlabWaves = 8;        // waves (x32 components) per two-pass slab
 constexpr int kSingleMaxK = 256;     // largest K the single sweep keeps on chip
+constexpr int kSmallMaxK = 16;       // small-K kernel: one 16-component tile
+constexpr int kSmallMaxD = 64;
 constexpr int kLseWaves = 4;         // waves per block in the fp64 normaliser pass
+constexpr int kSmallWaves = 4;       // waves per block in the small-K kernel
 constexpr int64_t kMaxChunkRows = 32768;  // rows per statistics partial, at most
 
 // Device pointers into the caller's workspace, filled by gmm::plan().
@@ -36,8 +39,8 @@ struct Workspace {
 struct Plan {
   int64_t N;
   int d, K;
-  int DT, DP;       // DP = 32*DT >= d: padded feature count
-  int regime;       // 1 single, 2 two-pass
+  int DT, DP;       // DP >= d: padded feature count (32*DT; 16-multiple for small-K)
+  int regime;       // 1 single, 2 two-pass, 3 small-K
   int waves;        // waves per block in the statistics kernel
   int kslabs;       // component slabs (1 for the single sweep)
   int Kp;           // padded K of the statistics kernel = 32*waves*kslabs

@@ -387,37 +387,51 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           srow4[psub + tpr * i] = v;
         }
       }
-      // Which entries need the exact re-score (E = Ebound, r_k = e_k / z):
-      //  MODE 0: an unrefined entry is off by <= 2 E r_k, so every entry with
-      //   r_k > tau/(2E) is refined; the refined ones are then off by at most
-      //   E * U, U = unrefined mass, which must stay <= tau, else the window
-      //   widens to every entry within kWindow of the maximum.
-      //  MODE 1: l_n comes from the exact first pass, so an unrefined entry is
-      //   off by <= E r_k and entries with r_k > tau/E are refined.
-      // With the max entry below the threshold the row needs nothing.
-      float thr = MODE == 0 ? kGateTau * (float)z / (2.f * Ebound) : kGateTau / Ebound;
-      const float top = MODE == 0 ? 1.f : expf(-lZ);  // largest e (MODE 0) or r (MODE 1)
-      const bool refine = valid && (top > thr);
+      // Which entries need the exact re-score (E = Ebound, r_k = e_k / z)?
+      //  MODE 0: l_n comes from the same fp32 scores, so an unrefined entry is
+      //   off by r_k |ds_k - sum_j r_j ds_j| <= 2 E r_k (1 - r_k): entries with
+      //   2 E r_k (1 - r_k) > tau are refined (a nearly one-hot row needs
+      //   nothing). Refined entries are then off by at most E * U, U = the
+      //   unrefined mass; if that could exceed tau the window widens to every
+      //   entry within kWindow of the row maximum.
+      //  MODE 1: l_n is exact (first pass), an unrefined entry is off by
+      //   <= E r_k, and entries with r_k > tau / E are refined.
       uint32_t mask = 0;
-      double unref = 0.0;
-      if (refine)
+      if (MODE == 0) {
+        const float zf = (float)z;
+        const float thr2 = kGateTau * zf * zf / (2.f * Ebound);  // on e (z - e)
+        const float maxq = zf >= 2.f ? zf - 1.f : 0.25f * zf * zf;
+        const bool refine = valid && maxq > thr2;
+        double unref = 0.0;
+        if (refine)
 #pragma unroll 4
-        for (int i = 0; i < 8; ++i) {
-          const float4 v = srow4[psub + tpr * i];
-          const float vv[4] = {v.x, v.y, v.z, v.w};
+          for (int i = 0; i < 8; ++i) {
+            const float4 v = srow4[psub + tpr * i];
+            const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (vv[u] >= thr)
-              mask |= 1u << (4 * i + u);
-            else
-              unref += (double)vv[u];
+            for (int u = 0; u < 4; ++u) {
+              if (vv[u] * (zf - vv[u]) > thr2)
+                mask |= 1u << (4 * i + u);
+              else
+                unref += (double)vv[u];
+            }
+          }
+        unref = group_sum_d(unref, tpr);
+        const float anyflag = group_max(mask ? 1.f : 0.f, tpr);
+        if (refine && anyflag > 0.f && (double)Ebound * unref / z > (double)kGateTau) {
+          mask = 0;
+#pragma unroll 4
+          for (int i = 0; i < 8; ++i) {
+            const float4 v = srow4[psub + tpr * i];
+            mask |= (v.x >= kExpWindow ? 1u : 0u) << (4 * i);
+            mask |= (v.y >= kExpWindow ? 1u : 0u) << (4 * i + 1);
+            mask |= (v.z >= kExpWindow ? 1u : 0u) << (4 * i + 2);
+            mask |= (v.w >= kExpWindow ? 1u : 0u) << (4 * i + 3);
           }
         }
-      if (MODE == 0) {
-        unref = group_sum_d(unref, tpr);
-        if (refine && (double)Ebound * unref / z > (double)kGateTau) {
-          thr = kExpWindow;
-          mask = 0;
+      } else {
+        const float thr = kGateTau / Ebound;
+        if (valid && expf(-lZ) > thr)
 #pragma unroll 4
           for (int i = 0; i < 8; ++i) {
             const float4 v = srow4[psub + tpr * i];
@@ -426,7 +440,6 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
             mask |= (v.z >= thr ? 1u : 0u) << (4 * i + 2);
             mask |= (v.w >= thr ? 1u : 0u) << (4 * i + 3);
           }
-        }
       }
       // Exact re-score of the window entries. Each wave pools the entries of
       // its rows into an LDS list and re-scores four at a time, sixteen lanes
@@ -487,15 +500,16 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         }
       }
       if (MODE == 0) {
+        const bool redo = group_max(mask ? 1.f : 0.f, tpr) > 0.f;  // this row was re-scored
         double z2 = 0.0;
-        if (refine)
+        if (redo)
 #pragma unroll 4
           for (int i = 0; i < 8; ++i) {
             const float4 v = srow4[psub + tpr * i];
             z2 += ((double)v.x + (double)v.y) + ((double)v.z + (double)v.w);
           }
         z2 = group_sum_d(z2, tpr);
-        if (refine) z = z2;
+        if (redo) z = z2;
         // z is in [1, K]: an fp32 log is exact to ~1e-7 absolute, far inside the
         // 1e-4 relative bar of l_n; r itself uses 1/z.
         const double lZd = (double)logf((float)z);
@@ -580,6 +594,369 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       for (int i = 0; i < nthr; ++i) s += lls[i];
       llpart[chunk] = s;
     }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Small-K single sweep (K <= 16, d <= 64): 16x16x4 f32 MFMA tiles
+// ---------------------------------------------------------------------------
+//
+// Every wave owns all (at most 16) components and works alone on 16-point
+// tiles of its own row range; waves only meet at the start (parameters into
+// LDS) and at the end (statistics partial of the block). The 16x16x4 score
+// accumulator holds, in lane (g, c) slot j, point 4g+j against component c:
+// a row is one 16-lane group, so the row max and log-sum-exp are 16-lane
+// butterflies in registers, and slot j is also the A operand of the
+// statistics MFMA for step j (component c, point slot g). The score operands
+// (16 components x 2d) live in registers; mu and 1/var sit in LDS for the
+// exact re-score.
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// All-reduce over each 16-lane row with DPP (xor 1, xor 2, half-row mirror,
+// row mirror). Every lane of the row ends with the same, bitwise identical
+// value (each step combines commutatively).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffll), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ float bfly16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f<kDppMirror>(v));
+}
+__device__ __forceinline__ float bfly16_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppMirror>(v);
+}
+__device__ __forceinline__ double bfly16_sum_d(double v) {
+  v += dpp_d<kDppXor1>(v);
+  v += dpp_d<kDppXor2>(v);
+  v += dpp_d<kDppHalfMirror>(v);
+  return v + dpp_d<kDppMirror>(v);
+}
+
+// N independent 16-lane all-reduces, step-interleaved so that the DPP
+// hazards of one chain are covered by the others.
+template <int N>
+__device__ __forceinline__ void bfly16_max_n(float* v) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f<kDppXor1>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f<kDppXor2>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f<kDppHalfMirror>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f<kDppMirror>(v[i]));
+}
+template <int N>
+__device__ __forceinline__ void bfly16_sum_n(float* v) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f<kDppXor1>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f<kDppXor2>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f<kDppHalfMirror>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f<kDppMirror>(v[i]);
+}
+
+// exp(x) for x <= ~0 through the hardware exp2 (1 ulp): the relative error is
+// ~|x| * 2^-24 * log2(e) from rounding x*log2(e), i.e. an absolute error in
+// exp(x) of at most ~3e-8 over x <= 0.
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
+// Per wave: a 64-point tile of X [64][XS] and a score/responsibility tile
+// [64][SS] in LDS. Scores come from four 16x16x4 blocks; the row phase then
+// runs one point per lane (in-lane max / sum over the <= 16 components), and
+// the statistics MFMAs read r back in the accumulator layout.
+template <int DS>
+struct SmallTile {
+  static constexpr int DP = 16 * DS, XS = DP + 4, SS = 20;
+  static constexpr int XF = 64 * XS, SF = 64 * SS;  // floats per wave
+  static constexpr int PF = DS <= 2 ? DP / 4 : 0;   // float4 per lane prefetched in registers
+};
+
+template <int DS, typename XT>
+__global__ void __launch_bounds__(256)
+estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wave_rows,
+                   const double* __restrict__ W64p, const float* __restrict__ c32,
+                   const float* __restrict__ mu, const double* __restrict__ iv64,
+                   const double* __restrict__ c64d, const float* __restrict__ errc,
+                   float* __restrict__ partials, double* __restrict__ llpart,
+                   float* __restrict__ ll_point, float* __restrict__ R, int vec) {
+  using T = SmallTile<DS>;
+  constexpr int DP = T::DP, S = DP / 2, XS = T::XS, SS = T::SS, E = 1 + 2 * DP;
+  __shared__ __align__(16) float tiles[kSmallWaves][T::XF + T::SF];
+  __shared__ float mus[16 * DP];
+  __shared__ double ivs[16 * DP];
+  __shared__ double cds[16];
+  __shared__ double lls[kSmallWaves];
+  __shared__ float rowm[kSmallWaves][64];
+  __shared__ uint32_t elist[kSmallWaves][64];
+  static_assert(16 * E <= T::XF + T::SF, "the block partial is staged in the tile space");
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+
+  for (int i = tid; i < 16 * DP; i += blockDim.x) {
+    const int k = i / DP, f = i - k * DP;
+    const bool in = k < K && f < d;
+    mus[i] = in ? mu[(size_t)k * d + f] : 0.f;
+    ivs[i] = in ? iv64[(size_t)k * d + f] : 0.0;
+  }
+  if (tid < 16) cds[tid] = tid < K ? c64d[tid] : 0.0;
+  __syncthreads();
+
+  float w[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) w[s] = (float)W64p[s * 64 + lane];
+  float cks[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) cks[k] = c32[k];
+  const float a_max = errc[0], c_max = errc[2], b2_max = errc[3];
+  const float gam = (float)(2 * DP + 4) * kUnitRound;
+
+  v4f SX[DS], SXX[DS];
+#pragma unroll
+  for (int t = 0; t < DS; ++t) SX[t] = SXX[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float nk = 0.f;
+  double ll = 0.0;
+
+  float* xs = &tiles[wave][0];
+  float* sc = &tiles[wave][T::XF];
+  const int64_t wid = (int64_t)blockIdx.x * kSmallWaves + wave;
+  const int64_t lo = wid * wave_rows;
+  const int64_t hi = min(N, lo + wave_rows);
+  const bool pf = vec && sizeof(XT) == 4 && T::PF > 0;
+  const float* Xf = reinterpret_cast<const float*>(X);
+
+  // register prefetch of a 64-row tile: float4 chunk ch = 64 i + lane is row
+  // ch / (DP/4), features 4 (ch % (DP/4)); rows past hi and features past d
+  // read as zero.
+  float4 pre[T::PF > 0 ? T::PF : 1];
+  auto fetch = [&](int64_t r) {
+#pragma unroll
+    for (int i = 0; i < T::PF; ++i) {
+      const int ch = 64 * i + lane;
+      const int row = ch / (DP / 4), q = ch - row * (DP / 4);
+      const int64_t gr = r + row;
+      pre[i] = (gr < hi && 4 * q < d) ? *reinterpret_cast<const float4*>(Xf + gr * d + 4 * q)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  if (pf && lo < hi) fetch(lo);
+
+  for (int64_t r0 = lo; r0 < hi; r0 += 64) {
+    // 1. X tile -> LDS (prefetched registers, or direct loads), next tile requested
+    if (pf) {
+#pragma unroll
+      for (int i = 0; i < T::PF; ++i) {
+        const int ch = 64 * i + lane;
+        const int row = ch / (DP / 4), q = ch - row * (DP / 4);
+        *reinterpret_cast<float4*>(xs + row * XS + 4 * q) = pre[i];
+      }
+      if (r0 + 64 < hi) fetch(r0 + 64);
+    } else {
+      for (int e = lane; e < 64 * DP; e += 64) {
+        const int row = e / DP, f = e - row * DP;
+        const int64_t gr = r0 + row;
+        xs[row * XS + f] = (gr < hi && f < d) ? load_x(X, gr * d + f) : 0.f;
+      }
+    }
+    wave_lds_sync();
+
+    // 2. scores, 16-point block b: lane (g, c) supplies point 16b + c, step s
+    //    feature 2s + g/2 (x^2 for even g); accumulator slot j = point 16b+4g+j
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const float x = xs[(16 * b + c) * XS + 2 * s + (g >> 1)];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32((g & 1) ? x : x * x, w[s], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[(16 * b + 4 * g + j) * SS + c] = acc[j];
+    }
+    wave_lds_sync();
+
+    // 3. row phase: lane = point
+    {
+      const int p = lane;
+      const int64_t gr = r0 + p;
+      const bool valid = gr < hi;
+      float e[16];
+      float m = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(sc + p * SS + 4 * q);
+        e[4 * q] = v.x + cks[4 * q];
+        e[4 * q + 1] = v.y + cks[4 * q + 1];
+        e[4 * q + 2] = v.z + cks[4 * q + 2];
+        e[4 * q + 3] = v.w + cks[4 * q + 3];
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) m = fmaxf(m, e[k]);
+      float z = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        e[k] = fast_exp(e[k] - m);
+        z += e[k];
+      }
+      float sq = 0.f;
+      const float* xr = xs + p * XS;
+#pragma unroll
+      for (int q = 0; q < DP / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(xr + 4 * q);
+        sq += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+      // re-score rule of the single sweep (see the main kernel): refine entries
+      // with 2 E r (1 - r) > tau; widen to the kWindow window if the unrefined
+      // mass could still move the refined ones by more than tau.
+      const float Eb = gam * (a_max * sq + b2_max * __builtin_sqrtf(sq)) + 2.f * kUnitRound * c_max;
+      const float thr2 = kGateTau * z * z * __builtin_amdgcn_rcpf(2.f * Eb);  // on e (z - e)
+      uint32_t mask = 0;
+      float unref = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const bool fl = valid && e[k] * (z - e[k]) > thr2;
+        mask |= (fl ? 1u : 0u) << k;
+        unref += fl ? 0.f : e[k];
+      }
+      if (mask && Eb * unref > kGateTau * z) {
+        mask = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) mask |= (valid && e[k] >= kExpWindow ? 1u : 0u) << k;
+      }
+      // Exact re-score (fp64 difference form) of the wave's flagged entries:
+      // e goes to the score tile, the entries to an LDS list, and four entries
+      // at a time are re-scored by sixteen lanes each (features sl + 16u).
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(sc + p * SS + 4 * q) = make_float4(e[4 * q], e[4 * q + 1], e[4 * q + 2], e[4 * q + 3]);
+      rowm[wave][p] = m;
+      const int cnt = __popc(mask);
+      int incl = cnt;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      const int total = __shfl(incl, 63, 64);
+      if (total > 0) {
+        const int base = incl - cnt;
+        for (int p0 = 0; p0 < total; p0 += 64) {
+          uint32_t m2 = mask;
+          int pos = base;
+          while (m2) {
+            const int k = __ffs(m2) - 1;
+            m2 &= m2 - 1u;
+            if (pos >= p0 && pos < p0 + 64) elist[wave][pos - p0] = ((uint32_t)p << 4) | (uint32_t)k;
+            ++pos;
+          }
+          wave_lds_sync();
+          const int n = min(total - p0, 64);
+          for (int e0 = 0; e0 < n; e0 += 4) {
+            const int ei = e0 + (lane >> 4), sl = lane & 15;
+            const bool act = ei < n;
+            const uint32_t ent = act ? elist[wave][ei] : 0u;
+            const int ep = (int)(ent >> 4), ek = (int)(ent & 15u);
+            double a = 0.0;
+            if (act) {
+#pragma unroll
+              for (int u = 0; u < DS; ++u) {
+                const int f = sl + 16 * u;  // features >= d carry 1/var = 0
+                const double t = (double)xs[ep * XS + f] - (double)mus[ek * DP + f];
+                a += t * t * ivs[ek * DP + f];
+              }
+            }
+            a = bfly16_sum_d(a);
+            if (act && sl == 0) sc[ep * SS + ek] = fast_exp((float)((cds[ek] - 0.5 * a) - (double)rowm[wave][ep]));
+          }
+          wave_lds_sync();
+        }
+        if (mask) {
+          z = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(sc + p * SS + 4 * q);
+            e[4 * q] = v.x;
+            e[4 * q + 1] = v.y;
+            e[4 * q + 2] = v.z;
+            e[4 * q + 3] = v.w;
+            z += (v.x + v.y) + (v.z + v.w);
+          }
+        }
+      }
+      const float inv = valid ? __builtin_amdgcn_rcpf(z) : 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(sc + p * SS + 4 * q) =
+            make_float4(e[4 * q] * inv, e[4 * q + 1] * inv, e[4 * q + 2] * inv, e[4 * q + 3] * inv);
+      if (valid) {
+        const double l = (double)m + (double)(__builtin_amdgcn_logf(z) * 0.69314718055994531f);
+        ll += l;
+        if (ll_point) ll_point[gr] = (float)l;
+        if (R)
+          for (int k = 0; k < K; ++k) R[gr * K + k] = e[k] * inv;
+      }
+    }
+    wave_lds_sync();
+
+    // 4. statistics: step j of block b uses r of point 16b + 4g + j (component c)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = 16 * b + 4 * g + j;
+        const float r = sc[p * SS + c];
+        nk += r;
+#pragma unroll
+        for (int t = 0; t < DS; ++t) {
+          const float xv = xs[p * XS + 16 * t + c];
+          SX[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(r, xv, SX[t], 0, 0, 0);
+          SXX[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(r, xv * xv, SXX[t], 0, 0, 0);
+        }
+      }
+    wave_lds_sync();  // the tiles are rewritten by the next iteration
+  }
+
+  // block partial: waves -> LDS (own tile space) -> fixed-order sum
+  float* ws = &tiles[wave][0];
+#pragma unroll
+  for (int t = 0; t < DS; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int comp = 4 * g + j, f = 16 * t + c;
+      ws[comp * E + 1 + f] = SX[t][j];
+      ws[comp * E + 1 + DP + f] = SXX[t][j];
+    }
+  nk += __shfl_xor(nk, 16, 64);
+  nk += __shfl_xor(nk, 32, 64);
+  if (g == 0) ws[c * E] = nk;
+  for (int o = 1; o < 64; o <<= 1) ll += __shfl_xor(ll, o, 64);
+  if (lane == 0) lls[wave] = ll;
+  __syncthreads();
+  float* part = partials + (size_t)blockIdx.x * 16 * E;
+  for (int i = tid; i < 16 * E; i += blockDim.x) {
+    float a = 0.f;
+    for (int v = 0; v < kSmallWaves; ++v) a += tiles[v][i];
+    part[i] = a;
+  }
+  if (tid == 0) {
+    double a = 0.0;
+    for (int v = 0; v < kSmallWaves; ++v) a += lls[v];
+    llpart[blockIdx.x] = a;
   }
 }
 
@@ -882,10 +1259,30 @@ static hipError_t run_lse(const Plan& p, const XT* X, float* ll_point, int32_t* 
   return hipGetLastError();
 }
 
+template <int DS, typename XT>
+static hipError_t run_small(const Plan& p, const XT* X, const float* mu, float* ll_point, float* R,
+                            hipStream_t stream) {
+  const Workspace& w = p.ws;
+  const int vec = (sizeof(XT) == 4 && p.d % 4 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0) ? 1 : 0;
+  estep_small_kernel<DS, XT><<<(unsigned)p.P, 64 * kSmallWaves, 0, stream>>>(
+      X, p.N, p.d, p.K, p.rows_per_chunk / kSmallWaves, w.W64p, w.c32, mu, w.iv64, w.c64d, w.errc, w.partials,
+      w.llpart, ll_point, R, vec);
+  return hipGetLastError();
+}
+
 template <typename XT>
 static hipError_t estep_typed(const Plan& p, const XT* X, const float* mu, float* ll_point, float* R,
                               hipStream_t stream) {
   hipError_t e = hipSuccess;
+  if (p.regime == 3) {
+    switch (p.DP / 16) {
+      case 1: e = run_small<1>(p, X, mu, ll_point, R, stream); break;
+      case 2: e = run_small<2>(p, X, mu, ll_point, R, stream); break;
+      case 3: e = run_small<3>(p, X, mu, ll_point, R, stream); break;
+      default: e = run_small<4>(p, X, mu, ll_point, R, stream); break;
+    }
+    return e;
+  }
   if (p.regime == 1) {
     switch (p.DT) {
       case 1: e = run_stats<1, 0>(p, X, mu, ll_point, R, stream); break;
@@ -938,7 +1335,7 @@ hipError_t launch_estep(const Plan& p, const void* X, int x_dtype, const float* 
                                                                Sx, Sxx);
   }
   if (loglik_total) {
-    const int64_t nll = p.regime == 1 ? p.P : p.tiles;
+    const int64_t nll = p.regime == 2 ? p.tiles : p.P;
     reduce_ll_kernel<<<1, 256, 0, stream>>>(w.llpart, nll, loglik_total);
   }
   return hipGetLastError();

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgmm_mi355x.so")
 
 GMM_F32, GMM_F16 = 0, 1
-REGIME_AUTO, REGIME_SINGLE, REGIME_TWOPASS = 0, 1, 2
+REGIME_AUTO, REGIME_SINGLE, REGIME_TWOPASS, REGIME_SMALLK = 0, 1, 2, 3
 
 EXPORTS = (
     "gmm_version", "gmm_error_string", "gmm_workspace_bytes", "gmm_estep_stats",

@@ -75,6 +75,8 @@ def test_estep_argument_validation(L):
     assert _estep(L, wsb=16) == -3                         # too small
     assert _estep(L, K=300, regime=1) == -2                # single sweep needs K <= 256
     assert _estep(L, regime=5) == -1
+    assert _estep(L, K=17, regime=3) == -2                 # small-K needs K <= 16
+    assert _estep(L, d=65, regime=3) == -2                 # ... and d <= 64
 
 
 def test_other_entry_points_validate(L):

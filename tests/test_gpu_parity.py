@@ -54,13 +54,24 @@ def _run_and_check(G, X, mu, var, logw, regime, what):
     print(f"{what}: max rel dl {el:.2e}  max |dr| {er:.2e}  stats {es[0]:.1e}/{es[1]:.1e}/{es[2]:.1e}", flush=True)
 
 
-REGIMES = {"single": 1, "twopass": 2}
+REGIMES = {"single": 1, "twopass": 2, "smallk": 3}
 
 
-@pytest.mark.parametrize("regime", ["single", "twopass"])
+def _regimes(K, d):
+    out = [2]
+    if K <= 256:
+        out.append(1)
+    if K <= 16 and d <= 64:
+        out.append(3)
+    return out
+
+
+@pytest.mark.parametrize("regime", ["single", "twopass", "smallk"])
 @pytest.mark.parametrize("name,N", [("tiny", None), ("ref", 3001), ("smallk", 5003)])
 def test_estep_small_k_workloads(G, name, N, regime):
     X, mu, var, logw = _case(name, N)
+    if REGIMES[regime] not in _regimes(mu.shape[0], X.shape[1]):
+        pytest.skip("regime does not apply to this shape")
     _run_and_check(G, X, mu, var, logw, REGIMES[regime], f"{name} N={len(X)} {regime}")
 
 
@@ -72,12 +83,12 @@ def test_estep_large_k_workloads(G, name, N, scale):
 
 @pytest.mark.parametrize("N,d,K", [
     (1, 3, 1), (63, 5, 3), (65, 1, 2), (130, 33, 33), (200, 100, 7), (129, 128, 64),
-    (97, 17, 257), (77, 64, 300), (150, 96, 129), (64, 32, 256),
+    (97, 17, 257), (77, 64, 300), (150, 96, 129), (64, 32, 256), (300, 48, 16), (33, 64, 11),
+    (1000, 20, 13),
 ])
 def test_estep_edge_shapes(G, N, d, K):
     X, mu, var, logw = datagen.random_problem(1000 + N + d + K, N, d, K)
-    regimes = [1, 2] if K <= 256 else [2]
-    for r in regimes:
+    for r in _regimes(K, d):
         _run_and_check(G, X, mu, var, logw, r, f"edge N={N} d={d} K={K} regime={r}")
 
 
@@ -96,6 +107,13 @@ def test_near_tie_pairs_with_large_scores(G):
     assert np.abs(S).max() > 500
     for r in (1, 2):
         _run_and_check(G, X, mu, var, logw, r, f"near-tie pairs regime={r}")
+    # the same construction at a small-K shape
+    C2 = C[:8, :48]
+    mu2 = np.concatenate([C2, C2 + rng.normal(0, 2e-3, C2.shape)]).astype(np.float32)
+    var2 = np.full((16, 48), 0.5, np.float32)
+    lab2 = rng.integers(0, 8, 1500)
+    X2 = (C2[lab2] + rng.normal(0, 1.5, (1500, 48))).astype(np.float32)
+    _run_and_check(G, X2, mu2, var2, np.full(16, -np.log(16), np.float32), 3, "near-tie pairs small-K")
 
 
 def test_estep_empty_input(G):
@@ -113,7 +131,7 @@ def test_single_component_gives_sample_moments(G):
     mu = np.zeros((1, 16), np.float32)
     var = np.ones((1, 16), np.float32)
     logw = np.zeros(1, np.float32)
-    for r in (1, 2):
+    for r in (1, 2, 3):
         Nk, Sx, Sxx, L, _ = G.estep_stats(dev(X), dev(mu), dev(var), dev(logw), regime=r)
         R, _ = G.estep_resp(dev(X), dev(mu), dev(var), dev(logw), regime=r)
         torch.cuda.synchronize()
