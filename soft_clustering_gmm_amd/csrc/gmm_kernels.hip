@@ -718,9 +718,16 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
   if (tid < 16) cds[tid] = tid < K ? c64d[tid] : 0.0;
   __syncthreads();
 
+  // Score operands in registers. Step s pairs lane (g, c) with feature
+  // g*(DP/4) + s/2, as x^2 on even steps and x on odd steps: each lane reads
+  // its point's features contiguously and squares each once. W64p holds
+  // feature f, part t of component c at ((f/2)*4 + 2*(f%2) + t)*16 + c.
   float w[S];
 #pragma unroll
-  for (int s = 0; s < S; ++s) w[s] = (float)W64p[s * 64 + lane];
+  for (int s = 0; s < S; ++s) {
+    const int f = g * (DP / 4) + (s >> 1);
+    w[s] = (float)W64p[((f >> 1) * 4 + 2 * (f & 1) + (s & 1)) * 16 + c];
+  }
   float cks[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) cks[k] = c32[k];
@@ -776,15 +783,21 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
     }
     wave_lds_sync();
 
-    // 2. scores, 16-point block b: lane (g, c) supplies point 16b + c, step s
-    //    feature 2s + g/2 (x^2 for even g); accumulator slot j = point 16b+4g+j
+    // 2. scores, 16-point block b: lane (g, c) supplies point 16b + c,
+    //    feature g*(DP/4) + s/2; accumulator slot j = point 16b+4g+j
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       v4f acc = {0.f, 0.f, 0.f, 0.f};
+      const float* xrow = xs + (16 * b + c) * XS + g * (DP / 4);
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const float x = xs[(16 * b + c) * XS + 2 * s + (g >> 1)];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32((g & 1) ? x : x * x, w[s], acc, 0, 0, 0);
+      for (int q = 0; q < DP / 16; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(xrow + 4 * q);
+        const float xv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[u] * xv[u], w[8 * q + 2 * u], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[u], w[8 * q + 2 * u + 1], acc, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) sc[(16 * b + 4 * g + j) * SS + c] = acc[j];
