@@ -78,7 +78,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ref", choices=["tiny", "ref", "smallk", "largek", "ivf"])
-    ap.add_argument("--cpu-rows", type=int, default=32768, help="row sample for the oracle baseline (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=131072, help="row sample for the oracle baseline (0: skip)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this E-step build runs on a "
