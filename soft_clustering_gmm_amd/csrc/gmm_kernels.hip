@@ -36,6 +36,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 constexpr double kLog2Pi = 1.83787706640934548356065947281;
+constexpr double kLog2E = 1.44269504088896340735992468100;  // 1 / ln 2
+constexpr double kLn2 = 0.693147180559945309417232121458;
 constexpr float kWindow = 20.0f;   // re-score components with s >= max - kWindow
 constexpr float kExpWindow = 2.0611536e-9f;  // exp(-kWindow)
 constexpr float kGateTau = 5e-7f;  // re-score a row when 2 E_n * r_max could exceed this
@@ -70,6 +72,30 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 template <typename XT>
 __device__ __forceinline__ float load_x(const XT* X, int64_t i) { return (float)X[i]; }
+
+// A double moved between lanes by a DPP quad permutation (two 32-bit moves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_quad_d(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffll), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
+// 4 and 8 within each row of 16 lanes, then the last lane of row 0 (row 2)
+// is added to row 1 (row 3), and the last lane of row 1 to rows 2 and 3.
+// Lanes whose DPP source lies outside the row (or whose row is masked off)
+// read 0.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
 
 // Asynchronous fp32 tile load: rows [r0, r0 + 64) of X -> LDS tile [64][XS]
 // with 16-byte global->LDS loads. One wave instruction fills 1 KB of LDS, i.e.
@@ -602,76 +628,21 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
 // Small-K single sweep (K <= 16, d <= 64): 16x16x4 f32 MFMA tiles
 // ---------------------------------------------------------------------------
 //
-// Every wave owns all (at most 16) components and works alone on 16-point
+// Every wave owns all (at most 16) components and works alone on the 64-point
 // tiles of its own row range; waves only meet at the start (parameters into
-// LDS) and at the end (statistics partial of the block). The 16x16x4 score
-// accumulator holds, in lane (g, c) slot j, point 4g+j against component c:
-// a row is one 16-lane group, so the row max and log-sum-exp are 16-lane
-// butterflies in registers, and slot j is also the A operand of the
-// statistics MFMA for step j (component c, point slot g). The score operands
-// (16 components x 2d) live in registers; mu and 1/var sit in LDS for the
-// exact re-score.
+// LDS) and at the end (statistics partial of the block). Per tile:
+//  1. the X tile goes to the wave's LDS tile (prefetched in registers one
+//     tile ahead for fp32 rows of at most 32 features);
+//  2. scores: four 16x16x4 MFMA chains, one per 16-point group, with the
+//     score operands (16 components x 2d, base-2 scaled) in registers; the
+//     accumulators go to the wave's LDS score tile [64][SS];
+//  3. row phase with one lane per point: max, e = 2^(s - m), z, the fp32
+//     error bound and the re-score flags, all in registers; flagged entries
+//     are re-scored exactly (fp64 difference form, one lane per entry);
+//     r = e / z goes back to the score tile;
+//  4. statistics: 16x16x4 MFMAs with r (component c, point slot g) as the A
+//     operand and x or x^2 of those points as B.
 typedef float v4f __attribute__((ext_vector_type(4)));
-
-// All-reduce over each 16-lane row with DPP (xor 1, xor 2, half-row mirror,
-// row mirror). Every lane of the row ends with the same, bitwise identical
-// value (each step combines commutatively).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ double dpp_d(double v) {
-  const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffll), CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-
-__device__ __forceinline__ float bfly16_max(float v) {
-  v = fmaxf(v, dpp_f<kDppXor1>(v));
-  v = fmaxf(v, dpp_f<kDppXor2>(v));
-  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
-  return fmaxf(v, dpp_f<kDppMirror>(v));
-}
-__device__ __forceinline__ float bfly16_sum(float v) {
-  v += dpp_f<kDppXor1>(v);
-  v += dpp_f<kDppXor2>(v);
-  v += dpp_f<kDppHalfMirror>(v);
-  return v + dpp_f<kDppMirror>(v);
-}
-__device__ __forceinline__ double bfly16_sum_d(double v) {
-  v += dpp_d<kDppXor1>(v);
-  v += dpp_d<kDppXor2>(v);
-  v += dpp_d<kDppHalfMirror>(v);
-  return v + dpp_d<kDppMirror>(v);
-}
-
-// N independent 16-lane all-reduces, step-interleaved so that the DPP
-// hazards of one chain are covered by the others.
-template <int N>
-__device__ __forceinline__ void bfly16_max_n(float* v) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f<kDppXor1>(v[i]));
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f<kDppXor2>(v[i]));
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f<kDppHalfMirror>(v[i]));
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f<kDppMirror>(v[i]));
-}
-template <int N>
-__device__ __forceinline__ void bfly16_sum_n(float* v) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] += dpp_f<kDppXor1>(v[i]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] += dpp_f<kDppXor2>(v[i]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] += dpp_f<kDppHalfMirror>(v[i]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] += dpp_f<kDppMirror>(v[i]);
-}
 
 // exp(x) for x <= ~0 through the hardware exp2 (1 ulp): the relative error is
 // ~|x| * 2^-24 * log2(e) from rounding x*log2(e), i.e. an absolute error in
@@ -687,21 +658,27 @@ struct SmallTile {
   static constexpr int DP = 16 * DS, XS = DP + 4, SS = 20;
   static constexpr int XF = 64 * XS, SF = 64 * SS;  // floats per wave
   static constexpr int PF = DS <= 2 ? DP / 4 : 0;   // float4 per lane prefetched in registers
+  // exact re-score: lanes per entry and features per lane
+  static constexpr int LPE = DS == 1 ? 1 : (DS == 2 ? 2 : 4), FPL = DP / LPE;
 };
 
 template <int DS, typename XT>
 __global__ void __launch_bounds__(256)
 estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wave_rows,
-                   const double* __restrict__ W64p, const float* __restrict__ c32,
+                   const double* __restrict__ W64p, const double* __restrict__ c64e,
                    const float* __restrict__ mu, const double* __restrict__ iv64,
                    const double* __restrict__ c64d, const float* __restrict__ errc,
                    float* __restrict__ partials, double* __restrict__ llpart,
                    float* __restrict__ ll_point, float* __restrict__ R, int vec) {
   using T = SmallTile<DS>;
   constexpr int DP = T::DP, S = DP / 2, XS = T::XS, SS = T::SS, E = 1 + 2 * DP;
+  // Row stride (doubles) of the re-score parameters, padded so that one lane
+  // per entry reading 16-byte pieces of different components' rows spreads
+  // over the banks.
+  constexpr int MS = DP + 2;
   __shared__ __align__(16) float tiles[kSmallWaves][T::XF + T::SF];
-  __shared__ float mus[16 * DP];
-  __shared__ double ivs[16 * DP];
+  __shared__ __align__(16) double mus[16 * MS];
+  __shared__ __align__(16) double ivs[16 * MS];
   __shared__ double cds[16];
   __shared__ double lls[kSmallWaves];
   __shared__ float rowm[kSmallWaves][64];
@@ -712,8 +689,8 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
   for (int i = tid; i < 16 * DP; i += blockDim.x) {
     const int k = i / DP, f = i - k * DP;
     const bool in = k < K && f < d;
-    mus[i] = in ? mu[(size_t)k * d + f] : 0.f;
-    ivs[i] = in ? iv64[(size_t)k * d + f] : 0.0;
+    mus[k * MS + f] = in ? (double)mu[(size_t)k * d + f] : 0.0;
+    ivs[k * MS + f] = in ? iv64[(size_t)k * d + f] : 0.0;
   }
   if (tid < 16) cds[tid] = tid < K ? c64d[tid] : 0.0;
   __syncthreads();
@@ -722,15 +699,20 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
   // g*(DP/4) + s/2, as x^2 on even steps and x on odd steps: each lane reads
   // its point's features contiguously and squares each once. W64p holds
   // feature f, part t of component c at ((f/2)*4 + 2*(f%2) + t)*16 + c.
+  // Operands and constants are scaled by log2(e) before rounding to fp32, so
+  // the scores come out in base-2 units and e = 2^(s - m) needs no multiply.
+  // Every fp32 operand is still the correctly rounded value of an exact one,
+  // so the error bound below holds for the scaled scores with each maximum
+  // scaled alike; it is applied in natural units, where it is unchanged.
   float w[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int f = g * (DP / 4) + (s >> 1);
-    w[s] = (float)W64p[((f >> 1) * 4 + 2 * (f & 1) + (s & 1)) * 16 + c];
+    w[s] = (float)(W64p[((f >> 1) * 4 + 2 * (f & 1) + (s & 1)) * 16 + c] * kLog2E);
   }
   float cks[16];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) cks[k] = c32[k];
+  for (int k = 0; k < 16; ++k) cks[k] = (float)(c64e[k] * kLog2E);
   const float a_max = errc[0], c_max = errc[2], b2_max = errc[3];
   const float gam = (float)(2 * DP + 4) * kUnitRound;
 
@@ -753,6 +735,12 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
   // read as zero.
   float4 pre[T::PF > 0 ? T::PF : 1];
   auto fetch = [&](int64_t r) {
+    if (d == DP && r + 64 <= hi) {  // a whole tile of unpadded rows: 64 * DP contiguous floats
+      const float4* src = reinterpret_cast<const float4*>(Xf + r * DP) + lane;
+#pragma unroll
+      for (int i = 0; i < T::PF; ++i) pre[i] = src[64 * i];
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < T::PF; ++i) {
       const int ch = 64 * i + lane;
@@ -783,6 +771,9 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
     }
     wave_lds_sync();
 
+    // The MFMA phases run at raised wave priority, so that a wave issuing
+    // MFMAs is preferred while the other wave of the SIMD does VALU work.
+    __builtin_amdgcn_s_setprio(1);
     // 2. scores, 16-point block b: lane (g, c) supplies point 16b + c,
     //    feature g*(DP/4) + s/2; accumulator slot j = point 16b+4g+j
 #pragma unroll
@@ -802,6 +793,7 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
 #pragma unroll
       for (int j = 0; j < 4; ++j) sc[(16 * b + 4 * g + j) * SS + c] = acc[j];
     }
+    __builtin_amdgcn_s_setprio(0);
     wave_lds_sync();
 
     // 3. row phase: lane = point
@@ -824,7 +816,7 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
       float z = 0.f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        e[k] = fast_exp(e[k] - m);
+        e[k] = __builtin_amdgcn_exp2f(e[k] - m);
         z += e[k];
       }
       float sq = 0.f;
@@ -853,20 +845,16 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
         for (int k = 0; k < 16; ++k) mask |= (valid && e[k] >= kExpWindow ? 1u : 0u) << k;
       }
       // Exact re-score (fp64 difference form) of the wave's flagged entries:
-      // e goes to the score tile, the entries to an LDS list, and four entries
-      // at a time are re-scored by sixteen lanes each (features sl + 16u).
+      // e goes to the score tile, the entries to an LDS list, and LPE lanes
+      // re-score one entry (FPL features each, partial sums combined by DPP).
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<float4*>(sc + p * SS + 4 * q) = make_float4(e[4 * q], e[4 * q + 1], e[4 * q + 2], e[4 * q + 3]);
       rowm[wave][p] = m;
-      const int cnt = __popc(mask);
-      int incl = cnt;
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-      }
-      const int total = __shfl(incl, 63, 64);
-      if (total > 0) {
+      if (__ballot(mask != 0)) {
+        const int cnt = __popc(mask);
+        const int incl = wave_incl_scan(cnt);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
         const int base = incl - cnt;
         for (int p0 = 0; p0 < total; p0 += 64) {
           uint32_t m2 = mask;
@@ -878,23 +866,35 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
             ++pos;
           }
           wave_lds_sync();
-          const int n = min(total - p0, 64);
-          for (int e0 = 0; e0 < n; e0 += 4) {
-            const int ei = e0 + (lane >> 4), sl = lane & 15;
-            const bool act = ei < n;
-            const uint32_t ent = act ? elist[wave][ei] : 0u;
+          constexpr int LPE = T::LPE, FPL = T::FPL, EPR = 64 / LPE;
+          const int n = min(total - p0, 64), part = lane % LPE;
+          for (int e0 = 0; e0 < n; e0 += EPR) {
+            const int ei = e0 + lane / LPE;
+            const uint32_t ent = ei < n ? elist[wave][ei] : 0u;
             const int ep = (int)(ent >> 4), ek = (int)(ent & 15u);
-            double a = 0.0;
-            if (act) {
-#pragma unroll
-              for (int u = 0; u < DS; ++u) {
-                const int f = sl + 16 * u;  // features >= d carry 1/var = 0
-                const double t = (double)xs[ep * XS + f] - (double)mus[ek * DP + f];
-                a += t * t * ivs[ek * DP + f];
-              }
+            const float* xr = xs + ep * XS + part * FPL;
+            const double* mr = mus + ek * MS + part * FPL;
+            const double* ir = ivs + ek * MS + part * FPL;
+            double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;  // features >= d carry 1/var = 0
+#pragma unroll 2
+            for (int q = 0; q < FPL / 4; ++q) {
+              const float4 xv = *reinterpret_cast<const float4*>(xr + 4 * q);
+              const double2 m01 = *reinterpret_cast<const double2*>(mr + 4 * q);
+              const double2 m23 = *reinterpret_cast<const double2*>(mr + 4 * q + 2);
+              const double2 i01 = *reinterpret_cast<const double2*>(ir + 4 * q);
+              const double2 i23 = *reinterpret_cast<const double2*>(ir + 4 * q + 2);
+              const double t0 = (double)xv.x - m01.x, t1 = (double)xv.y - m01.y;
+              const double t2 = (double)xv.z - m23.x, t3 = (double)xv.w - m23.y;
+              a0 = fma(t0 * t0, i01.x, a0);
+              a1 = fma(t1 * t1, i01.y, a1);
+              a2 = fma(t2 * t2, i23.x, a2);
+              a3 = fma(t3 * t3, i23.y, a3);
             }
-            a = bfly16_sum_d(a);
-            if (act && sl == 0) sc[ep * SS + ek] = fast_exp((float)((cds[ek] - 0.5 * a) - (double)rowm[wave][ep]));
+            double a = (a0 + a1) + (a2 + a3);
+            if (LPE >= 2) a += dpp_quad_d<0xB1>(a);  // lanes xor 1
+            if (LPE >= 4) a += dpp_quad_d<0x4E>(a);  // lanes xor 2
+            if (ei < n && part == 0)
+              sc[ep * SS + ek] = __builtin_amdgcn_exp2f((float)((cds[ek] - 0.5 * a) * kLog2E - (double)rowm[wave][ep]));
           }
           wave_lds_sync();
         }
@@ -903,29 +903,33 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float4 v = *reinterpret_cast<const float4*>(sc + p * SS + 4 * q);
-            e[4 * q] = v.x;
-            e[4 * q + 1] = v.y;
-            e[4 * q + 2] = v.z;
-            e[4 * q + 3] = v.w;
             z += (v.x + v.y) + (v.z + v.w);
           }
         }
       }
+      // r = e / z in place (e is read back from the tile, so it need not stay
+      // in registers across the re-score)
       const float inv = valid ? __builtin_amdgcn_rcpf(z) : 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(sc + p * SS + 4 * q) =
-            make_float4(e[4 * q] * inv, e[4 * q + 1] * inv, e[4 * q + 2] * inv, e[4 * q + 3] * inv);
+      for (int q = 0; q < 4; ++q) {
+        float4 v = *reinterpret_cast<float4*>(sc + p * SS + 4 * q);
+        v.x *= inv;
+        v.y *= inv;
+        v.z *= inv;
+        v.w *= inv;
+        *reinterpret_cast<float4*>(sc + p * SS + 4 * q) = v;
+      }
       if (valid) {
-        const double l = (double)m + (double)(__builtin_amdgcn_logf(z) * 0.69314718055994531f);
+        const double l = ((double)m + (double)__builtin_amdgcn_logf(z)) * kLn2;  // logf is log2
         ll += l;
         if (ll_point) ll_point[gr] = (float)l;
         if (R)
-          for (int k = 0; k < K; ++k) R[gr * K + k] = e[k] * inv;
+          for (int k = 0; k < K; ++k) R[gr * K + k] = sc[p * SS + k];
       }
     }
     wave_lds_sync();
 
+    __builtin_amdgcn_s_setprio(1);
     // 4. statistics: step j of block b uses r of point 16b + 4g + j (component c)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -941,6 +945,7 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
           SXX[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(r, xv * xv, SXX[t], 0, 0, 0);
         }
       }
+    __builtin_amdgcn_s_setprio(0);
     wave_lds_sync();  // the tiles are rewritten by the next iteration
   }
 
@@ -1278,7 +1283,7 @@ static hipError_t run_small(const Plan& p, const XT* X, const float* mu, float* 
   const Workspace& w = p.ws;
   const int vec = (sizeof(XT) == 4 && p.d % 4 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0) ? 1 : 0;
   estep_small_kernel<DS, XT><<<(unsigned)p.P, 64 * kSmallWaves, 0, stream>>>(
-      X, p.N, p.d, p.K, p.rows_per_chunk / kSmallWaves, w.W64p, w.c32, mu, w.iv64, w.c64d, w.errc, w.partials,
+      X, p.N, p.d, p.K, p.rows_per_chunk / kSmallWaves, w.W64p, w.c64e, mu, w.iv64, w.c64d, w.errc, w.partials,
       w.llpart, ll_point, R, vec);
   return hipGetLastError();
 }
