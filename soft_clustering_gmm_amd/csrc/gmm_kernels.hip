@@ -50,19 +50,6 @@ constexpr int kRefCap = 128;       // re-score list entries per wave and pass
 // D[row][col] with col = lane % 32 and row = 8*(j/4) + 4*h + j%4.
 __device__ __forceinline__ int acc_row(int h, int j) { return ((j >> 2) << 3) + (h << 2) + (j & 3); }
 
-__device__ __forceinline__ float group_max(float v, int tpr) {
-  for (int o = 1; o < tpr; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float group_sum(float v, int tpr) {
-  for (int o = 1; o < tpr; o <<= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ double group_sum_d(double v, int tpr) {
-  for (int o = 1; o < tpr; o <<= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // Orders this wave's LDS writes before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -73,13 +60,53 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <typename XT>
 __device__ __forceinline__ float load_x(const XT* X, int64_t i) { return (float)X[i]; }
 
-// A double moved between lanes by a DPP quad permutation (two 32-bit moves).
+// A double moved between lanes by a DPP lane permutation within each row of
+// 16 lanes (two 32-bit moves).
 template <int CTRL>
-__device__ __forceinline__ double dpp_quad_d(double v) {
+__device__ __forceinline__ double dpp_d(double v) {
   const long long b = __double_as_longlong(v);
   const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffll), CTRL, 0xF, 0xF, false);
   const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// DPP lane permutations within a row of 16 lanes: quad xor 1, quad xor 2,
+// mirror within each half row (i <-> 7 - i), mirror within the row
+// (i <-> 15 - i). Applied in this order as add steps they leave every lane of
+// the row with the sum over the row (the quad sums, then the half-row sums,
+// then the row sum), bitwise identical on all 16 lanes.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+__device__ __forceinline__ double row16_sum_d(double v) {
+  v += dpp_d<kDppXor1>(v);
+  v += dpp_d<kDppXor2>(v);
+  v += dpp_d<kDppHalfMirror>(v);
+  return v + dpp_d<kDppMirror>(v);
+}
+
+// All-reduce over aligned groups of tpr consecutive lanes (tpr a power of two
+// <= 8) with the DPP steps above; every lane of a group ends with the same
+// value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float group_max(float v, int tpr) {
+  if (tpr > 1) v = fmaxf(v, dpp_f<kDppXor1>(v));
+  if (tpr > 2) v = fmaxf(v, dpp_f<kDppXor2>(v));
+  if (tpr > 4) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  return v;
+}
+__device__ __forceinline__ float group_sum(float v, int tpr) {
+  if (tpr > 1) v += dpp_f<kDppXor1>(v);
+  if (tpr > 2) v += dpp_f<kDppXor2>(v);
+  if (tpr > 4) v += dpp_f<kDppHalfMirror>(v);
+  return v;
+}
+__device__ __forceinline__ double group_sum_d(double v, int tpr) {
+  if (tpr > 1) v += dpp_d<kDppXor1>(v);
+  if (tpr > 2) v += dpp_d<kDppXor2>(v);
+  if (tpr > 4) v += dpp_d<kDppHalfMirror>(v);
+  return v;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
@@ -473,12 +500,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       if (MODE == 0 && psub == 0) rv[2 * row] = m;
       {
         const int cnt = __popc(mask);
-        int incl = cnt;
-        for (int o = 1; o < 64; o <<= 1) {
-          const int t = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += t;
-        }
-        const int total = __shfl(incl, 63, 64);
+        const int incl = wave_incl_scan(cnt);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
         const int base = incl - cnt;
         uint32_t* wl = reflist + wave * kRefCap;
         for (int p0 = 0; p0 < total; p0 += kRefCap) {
@@ -513,10 +536,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
                 acc += t * t * w;
               }
             }
-            acc += __shfl_xor(acc, 1, 64);
-            acc += __shfl_xor(acc, 2, 64);
-            acc += __shfl_xor(acc, 4, 64);
-            acc += __shfl_xor(acc, 8, 64);
+            acc = row16_sum_d(acc);  // the 16 lanes of an entry form one DPP row
             if (act && sl == 0) {
               const double dl = (c64d[kg] - 0.5 * acc) - (double)rv[2 * er];  // exact s - m
               sc[er * SCS + ek] = MODE == 0 ? expf((float)dl) : expf((float)(dl - (double)rv[2 * er + 1]));
@@ -891,8 +911,8 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
               a3 = fma(t3 * t3, i23.y, a3);
             }
             double a = (a0 + a1) + (a2 + a3);
-            if (LPE >= 2) a += dpp_quad_d<0xB1>(a);  // lanes xor 1
-            if (LPE >= 4) a += dpp_quad_d<0x4E>(a);  // lanes xor 2
+            if (LPE >= 2) a += dpp_d<kDppXor1>(a);
+            if (LPE >= 4) a += dpp_d<kDppXor2>(a);
             if (ei < n && part == 0)
               sc[ep * SS + ek] = __builtin_amdgcn_exp2f((float)((cds[ek] - 0.5 * a) * kLog2E - (double)rowm[wave][ep]));
           }
