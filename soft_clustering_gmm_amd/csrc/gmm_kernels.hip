@@ -356,11 +356,12 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         acc0[j] = 0.f;
         acc1[j] = 0.f;
       }
-      // one-ahead register prefetch of the (L2-resident) score operands
+      // two-ahead register prefetch of the (L2-resident) score operands
       float4 w = Wt[0];
+      float4 wn = Wt[(1 < Q ? 1 : 0) * 64];
 #pragma unroll 1
       for (int q = 0; q < Q; ++q) {
-        const float4 wn = Wt[(q + 1 < Q ? q + 1 : q) * 64];
+        const float4 wnn = Wt[(q + 2 < Q ? q + 2 : Q - 1) * 64];
         const float4 x0 = *reinterpret_cast<const float4*>(xs + c * XS + 4 * q);
         const float4 x1 = *reinterpret_cast<const float4*>(xs + (c + 32) * XS + 4 * q);
         const float wv[4] = {w.x, w.y, w.z, w.w};
@@ -374,6 +375,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, wv[u], acc1, 0, 0, 0);
         }
         w = wn;
+        wn = wnn;
       }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
