@@ -137,6 +137,34 @@ int gmm_assign_top2(const void* X, int32_t x_dtype, int64_t N, int32_t d,
                     const float* mu, const float* var, const float* logw, int32_t K,
                     int32_t* idx, float* resp, void* workspace, size_t ws_bytes, void* stream);
 
+/* Row-chunked E-step for X that stays in HOST memory (Flash-GMM abstract:
+ * datasets far larger than one GPU holds; the statistics are additive over
+ * rows, so they are accumulated chunk by chunk). X_host is a host pointer
+ * to the same row-major N x d layout; best pinned (hipHostMalloc or a pinned
+ * torch tensor), since pageable memory cannot overlap its copies. Rows go
+ * to the device chunk_rows at a time through two staging buffers in the
+ * workspace: the copy of chunk i+1 runs on a library-owned copy stream
+ * (one per device, created on first use, default priority) while chunk i is
+ * scored on `stream`. Per chunk the E-step is the one of gmm_estep_stats
+ * (AUTO regime); the chunks' statistics and log-likelihoods are summed in
+ * fp64 in chunk order, so results are deterministic for a given chunk_rows
+ * and agree with gmm_estep_stats to rounding. Outputs are device pointers as
+ * in gmm_estep_stats; loglik_point (nullable) gets all N values.
+ * The workspace must hold gmm_workspace_bytes_chunked(N, d, K, chunk_rows,
+ * x_dtype) bytes. X_host must stay valid and unmodified until `stream` has
+ * completed. Calls on one device are serialised by the library while they
+ * enqueue; callers must not reuse a workspace on two streams at once.
+ * chunk_rows >= 1 (values above N are treated as N). */
+int gmm_estep_stats_chunked(const void* X_host, int32_t x_dtype, int64_t N, int32_t d,
+                            const float* mu, const float* var, const float* logw, int32_t K,
+                            float* Nk, float* Sx, float* Sxx,
+                            double* loglik_total, float* loglik_point, int64_t chunk_rows,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for gmm_estep_stats_chunked; 0 for arguments outside the
+ * limits (or chunk_rows < 1, unknown x_dtype). */
+size_t gmm_workspace_bytes_chunked(int64_t N, int32_t d, int32_t K, int64_t chunk_rows, int32_t x_dtype);
+
 #ifdef __cplusplus
 }
 #endif

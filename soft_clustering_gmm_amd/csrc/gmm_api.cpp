@@ -6,6 +6,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 
 #include "gmm_internal.hpp"
 
@@ -138,6 +140,58 @@ static int check_common(const void* X, int32_t xt, int64_t N, int32_t d, int32_t
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? GMM_OK : GMM_EHIP; }
 
+// Row-chunked E-step: workspace = [chunk plan region (the larger of the
+// full-chunk and tail-chunk plans; the parameter regions at its start are
+// laid out identically for every chunk size)] [staging 0] [staging 1]
+// [fp64 accumulators: K * (1 + 2d) statistics + 1 log-likelihood].
+struct ChunkLayout {
+  int64_t chunk;
+  size_t plan_bytes, stage_bytes, stage_off[2], acc_off, total;
+};
+
+static int chunk_layout(int64_t N, int d, int K, int64_t chunk_rows, int x_dtype, ChunkLayout* L) {
+  if (N < 0 || d < 1 || K < 1 || chunk_rows < 1) return GMM_EINVAL;
+  if (x_dtype != GMM_F32 && x_dtype != GMM_F16) return GMM_EINVAL;
+  if (d > kMaxD || K > kMaxK || N >= ((int64_t)1 << 40)) return GMM_EUNSUPPORTED;
+  const int64_t c = std::max<int64_t>(std::min(chunk_rows, N), 1);
+  const int64_t tail = N % c;
+  size_t pb = workspace_bytes(c, d, K);
+  if (tail) pb = std::max(pb, workspace_bytes(tail, d, K));
+  L->chunk = c;
+  L->plan_bytes = align_up(pb, 256);
+  L->stage_bytes = align_up((size_t)c * d * (x_dtype == GMM_F16 ? 2 : 4), 256);
+  L->stage_off[0] = L->plan_bytes;
+  L->stage_off[1] = L->plan_bytes + L->stage_bytes;
+  L->acc_off = L->plan_bytes + 2 * L->stage_bytes;
+  L->total = L->acc_off + align_up(((size_t)K * (1 + 2 * d) + 1) * sizeof(double), 256);
+  return GMM_OK;
+}
+
+// Per-device copy stream and events of the chunked E-step, created on first
+// use and kept for the life of the process. The mutex serialises the
+// enqueue sequence of concurrent calls (events are re-recorded per call).
+struct ChunkRes {
+  hipStream_t copy = nullptr;
+  hipEvent_t entry = nullptr, copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr};
+};
+static std::mutex g_chunk_mutex;
+static std::map<int, ChunkRes> g_chunk_res;
+
+static hipError_t chunk_resources(ChunkRes** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  ChunkRes& r = g_chunk_res[dev];
+  if (!r.copy) {
+    if ((e = hipStreamCreateWithFlags(&r.copy, hipStreamNonBlocking)) != hipSuccess) return e;
+    hipEvent_t* evs[5] = {&r.entry, &r.copied[0], &r.copied[1], &r.done[0], &r.done[1]};
+    for (hipEvent_t* ev : evs)
+      if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &r;
+  return hipSuccess;
+}
+
 }  // namespace gmm
 
 using namespace gmm;
@@ -232,6 +286,59 @@ int gmm_em_iterate(const void* X, int32_t x_dtype, int64_t N, int32_t d, int32_t
     if (e != hipSuccess) return GMM_EHIP;
   }
   return GMM_OK;
+}
+
+size_t gmm_workspace_bytes_chunked(int64_t N, int32_t d, int32_t K, int64_t chunk_rows, int32_t x_dtype) {
+  ChunkLayout L;
+  return chunk_layout(N, d, K, chunk_rows, x_dtype, &L) == GMM_OK ? L.total : 0;
+}
+
+int gmm_estep_stats_chunked(const void* X_host, int32_t x_dtype, int64_t N, int32_t d, const float* mu,
+                            const float* var, const float* logw, int32_t K, float* Nk, float* Sx, float* Sxx,
+                            double* loglik_total, float* loglik_point, int64_t chunk_rows, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  int st = check_common(X_host, x_dtype, N, d, K, mu, var, logw);
+  if (st) return st;
+  if (!Nk || !Sx || !Sxx || !loglik_total) return GMM_EINVAL;
+  ChunkLayout L;
+  if ((st = chunk_layout(N, d, K, chunk_rows, x_dtype, &L))) return st;
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 || ws_bytes < L.total) return GMM_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) return hip_status(launch_zero_outputs(Nk, Sx, Sxx, d, K, loglik_total, s));
+  char* base = static_cast<char*>(workspace);
+  void* stage[2] = {base + L.stage_off[0], base + L.stage_off[1]};
+  double* acc = reinterpret_cast<double*>(base + L.acc_off);
+  const size_t row_bytes = (size_t)d * (x_dtype == GMM_F16 ? 2 : 4);
+  const char* xh = static_cast<const char*>(X_host);
+
+  std::lock_guard<std::mutex> lock(g_chunk_mutex);
+  ChunkRes* r = nullptr;
+  hipError_t e = chunk_resources(&r);
+  Plan p;
+  if (e == hipSuccess && make_plan(L.chunk, d, K, GMM_REGIME_AUTO, workspace, &p) != GMM_OK) return GMM_EINVAL;
+  if (e == hipSuccess) e = launch_precompute(p, mu, var, logw, s);
+  // the staging buffers may still be read by earlier work on `stream`
+  if (e == hipSuccess) e = hipEventRecord(r->entry, s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(r->copy, r->entry, 0);
+  const int64_t nchunks = (N + L.chunk - 1) / L.chunk;
+  for (int64_t i = 0; i < nchunks && e == hipSuccess; ++i) {
+    const int b = (int)(i & 1);
+    const int64_t off = i * L.chunk, n = std::min(L.chunk, N - off);
+    if (i >= 2) e = hipStreamWaitEvent(r->copy, r->done[b], 0);  // chunk i-2 is done with buffer b
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(stage[b], xh + (size_t)off * row_bytes, (size_t)n * row_bytes, hipMemcpyHostToDevice,
+                         r->copy);
+    if (e == hipSuccess) e = hipEventRecord(r->copied[b], r->copy);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, r->copied[b], 0);
+    Plan pc;
+    if (e == hipSuccess && make_plan(n, d, K, GMM_REGIME_AUTO, workspace, &pc) != GMM_OK) return GMM_EINVAL;
+    if (e == hipSuccess)
+      e = launch_estep_accum(pc, stage[b], x_dtype, mu, acc, i == 0 ? 1 : 0,
+                             loglik_point ? loglik_point + off : nullptr, s);
+    if (e == hipSuccess) e = hipEventRecord(r->done[b], s);
+  }
+  if (e == hipSuccess) e = launch_finalize_stats(acc, K, d, Nk, Sx, Sxx, loglik_total, s);
+  return hip_status(e);
 }
 
 int gmm_set_timing_events(void* start, void* stop) {

@@ -68,6 +68,12 @@ void set_timing_events(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_estep(const Plan& p, const void* X, int x_dtype, const float* mu,
                         float* Nk, float* Sx, float* Sxx, double* loglik_total,
                         float* loglik_point, float* R, hipStream_t stream);
+// Row-chunked E-step: one chunk's statistics and log-likelihood are added to
+// the fp64 accumulators acc[K * (1 + 2d) + 1] (set instead when `first`).
+hipError_t launch_estep_accum(const Plan& p, const void* X, int x_dtype, const float* mu, double* acc, int first,
+                              float* loglik_point, hipStream_t stream);
+hipError_t launch_finalize_stats(const double* acc, int K, int d, float* Nk, float* Sx, float* Sxx,
+                                 double* loglik_total, hipStream_t stream);
 hipError_t launch_top2(const Plan& p, const void* X, int x_dtype, int32_t* idx, float* resp,
                        hipStream_t stream);
 hipError_t launch_mstep(const float* Nk, const float* Sx, const float* Sxx, int64_t N, int d, int K,

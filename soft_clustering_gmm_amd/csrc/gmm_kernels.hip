@@ -1176,13 +1176,10 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
 // ---------------------------------------------------------------------------
 
 // out element (k, e) of [Nk | Sx | Sxx] = sum over chunks p in order 0..P-1.
-__global__ void reduce_stats_kernel(const float* __restrict__ partials, int64_t P, int Kp, int E, int DP,
-                                    int K, int d, float* __restrict__ Nk, float* __restrict__ Sx,
-                                    float* __restrict__ Sxx) {
-  const int W = 1 + 2 * d;
-  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (t >= (int64_t)K * W) return;
-  const int k = (int)(t / W), e = (int)(t - (int64_t)k * W);
+// Fixed-order fp64 sum over the P statistics partials of output element e
+// (0: Nk, 1..d: Sx, d+1..2d: Sxx) of component k.
+__device__ __forceinline__ double sum_partials(const float* __restrict__ partials, int64_t P, int Kp, int E,
+                                               int DP, int d, int k, int e) {
   const int src = e == 0 ? 0 : (e <= d ? e : DP + (e - d));
   const float* p0 = partials + (size_t)k * E + src;
   const size_t stride = (size_t)Kp * E;
@@ -1195,7 +1192,17 @@ __global__ void reduce_stats_kernel(const float* __restrict__ partials, int64_t 
     s3 += p0[(p + 3) * stride];
   }
   for (; p < P; ++p) s0 += p0[p * stride];
-  const float s = (float)((s0 + s1) + (s2 + s3));
+  return (s0 + s1) + (s2 + s3);
+}
+
+__global__ void reduce_stats_kernel(const float* __restrict__ partials, int64_t P, int Kp, int E, int DP,
+                                    int K, int d, float* __restrict__ Nk, float* __restrict__ Sx,
+                                    float* __restrict__ Sxx) {
+  const int W = 1 + 2 * d;
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= (int64_t)K * W) return;
+  const int k = (int)(t / W), e = (int)(t - (int64_t)k * W);
+  const float s = (float)sum_partials(partials, P, Kp, E, DP, d, k, e);
   if (e == 0)
     Nk[k] = s;
   else if (e <= d)
@@ -1204,8 +1211,39 @@ __global__ void reduce_stats_kernel(const float* __restrict__ partials, int64_t 
     Sxx[(size_t)k * d + e - 1 - d] = s;
 }
 
-// One block of 256: fixed-order sum of n doubles.
-__global__ void reduce_ll_kernel(const double* __restrict__ part, int64_t n, double* __restrict__ out) {
+// Row-chunked E-step: the statistics of one chunk of rows are added (in
+// chunk order) to fp64 accumulators acc[k * (1 + 2d) + e], e as above.
+__global__ void accum_stats_kernel(const float* __restrict__ partials, int64_t P, int Kp, int E, int DP, int K,
+                                   int d, double* __restrict__ acc, int first) {
+  const int W = 1 + 2 * d;
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= (int64_t)K * W) return;
+  const int k = (int)(t / W), e = (int)(t - (int64_t)k * W);
+  const double s = sum_partials(partials, P, Kp, E, DP, d, k, e);
+  acc[t] = first ? s : acc[t] + s;
+}
+
+__global__ void finalize_stats_kernel(const double* __restrict__ acc, int K, int d, float* __restrict__ Nk,
+                                      float* __restrict__ Sx, float* __restrict__ Sxx,
+                                      double* __restrict__ loglik_total) {
+  const int W = 1 + 2 * d;
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t == 0) loglik_total[0] = acc[(int64_t)K * W];
+  if (t >= (int64_t)K * W) return;
+  const int k = (int)(t / W), e = (int)(t - (int64_t)k * W);
+  const float s = (float)acc[t];
+  if (e == 0)
+    Nk[k] = s;
+  else if (e <= d)
+    Sx[(size_t)k * d + e - 1] = s;
+  else
+    Sxx[(size_t)k * d + e - 1 - d] = s;
+}
+
+// One block of 256: fixed-order sum of n doubles, stored to out[0] (or, with
+// accumulate, added to it).
+template <bool ACCUM>
+__global__ void reduce_ll_kernel(const double* __restrict__ part, int64_t n, double* __restrict__ out, int first) {
   __shared__ double s[256];
   const int64_t per = (n + 255) / 256;
   const int64_t lo = threadIdx.x * per, hi = min(n, lo + per);
@@ -1217,7 +1255,7 @@ __global__ void reduce_ll_kernel(const double* __restrict__ part, int64_t n, dou
     if ((int)threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[0] = s[0];
+  if (threadIdx.x == 0) out[0] = (!ACCUM || first) ? s[0] : out[0] + s[0];
 }
 
 __global__ void zero_outputs_kernel(float* __restrict__ Nk, float* __restrict__ Sx, float* __restrict__ Sxx,
@@ -1376,8 +1414,28 @@ hipError_t launch_estep(const Plan& p, const void* X, int x_dtype, const float* 
   }
   if (loglik_total) {
     const int64_t nll = p.regime == 2 ? p.tiles : p.P;
-    reduce_ll_kernel<<<1, 256, 0, stream>>>(w.llpart, nll, loglik_total);
+    reduce_ll_kernel<false><<<1, 256, 0, stream>>>(w.llpart, nll, loglik_total, 0);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_estep_accum(const Plan& p, const void* X, int x_dtype, const float* mu, double* acc, int first,
+                              float* loglik_point, hipStream_t stream) {
+  hipError_t e = x_dtype == 1 ? estep_typed(p, reinterpret_cast<const _Float16*>(X), mu, loglik_point, nullptr, stream)
+                              : estep_typed(p, reinterpret_cast<const float*>(X), mu, loglik_point, nullptr, stream);
+  if (e != hipSuccess) return e;
+  const Workspace& w = p.ws;
+  const int64_t n = (int64_t)p.K * (1 + 2 * p.d);
+  accum_stats_kernel<<<nblocks(n, 256), 256, 0, stream>>>(w.partials, p.P, p.Kp, p.E, p.DP, p.K, p.d, acc, first);
+  const int64_t nll = p.regime == 2 ? p.tiles : p.P;
+  reduce_ll_kernel<true><<<1, 256, 0, stream>>>(w.llpart, nll, acc + n, first);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_stats(const double* acc, int K, int d, float* Nk, float* Sx, float* Sxx,
+                                 double* loglik_total, hipStream_t stream) {
+  const int64_t n = (int64_t)K * (1 + 2 * d);
+  finalize_stats_kernel<<<nblocks(n, 256), 256, 0, stream>>>(acc, K, d, Nk, Sx, Sxx, loglik_total);
   return hipGetLastError();
 }
 

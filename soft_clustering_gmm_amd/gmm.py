@@ -22,7 +22,7 @@ REGIME_AUTO, REGIME_SINGLE, REGIME_TWOPASS, REGIME_SMALLK = 0, 1, 2, 3
 EXPORTS = (
     "gmm_version", "gmm_error_string", "gmm_workspace_bytes", "gmm_estep_stats",
     "gmm_estep_stats_regime", "gmm_estep_resp", "gmm_mstep", "gmm_em_iterate", "gmm_assign_top2",
-    "gmm_set_timing_events",
+    "gmm_set_timing_events", "gmm_estep_stats_chunked", "gmm_workspace_bytes_chunked",
 )
 
 
@@ -58,6 +58,10 @@ def _load() -> ctypes.CDLL:
     L.gmm_assign_top2.argtypes = [P, I32, I64, I32, P, P, P, I32, P, P, P, SZ, P]
     L.gmm_set_timing_events.restype = ctypes.c_int
     L.gmm_set_timing_events.argtypes = [P, P]
+    L.gmm_estep_stats_chunked.restype = ctypes.c_int
+    L.gmm_estep_stats_chunked.argtypes = [P, I32, I64, I32, P, P, P, I32, P, P, P, P, P, I64, P, SZ, P]
+    L.gmm_workspace_bytes_chunked.restype = SZ
+    L.gmm_workspace_bytes_chunked.argtypes = [I64, I32, I32, I64, I32]
     return L
 
 
@@ -149,6 +153,39 @@ def estep_stats(X, mu, var, logw, *, regime: int = REGIME_AUTO, want_point_logli
     _check("gmm_estep_stats_regime", lib().gmm_estep_stats_regime(
         _ptr(X), _xtype(X), N, d, _ptr(mu), _ptr(var), _ptr(logw), K, _ptr(Nk), _ptr(Sx), _ptr(Sxx),
         _ptr(L), _ptr(lp), _ptr(ws), ws.numel(), regime, _stream(dev)))
+    return Nk, Sx, Sxx, L, lp
+
+
+def workspace_chunked(N: int, d: int, K: int, chunk_rows: int, x_dtype: int, device) -> torch.Tensor:
+    """A device workspace for estep_stats_chunked."""
+    nb = int(lib().gmm_workspace_bytes_chunked(N, d, K, chunk_rows, x_dtype))
+    if nb == 0:
+        raise ValueError(f"unsupported shape N={N} d={d} K={K} chunk_rows={chunk_rows}")
+    return torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+def estep_stats_chunked(X_host, mu, var, logw, chunk_rows: int, *, want_point_loglik: bool = False, ws=None):
+    """E-step over X in host memory (a CPU tensor, ideally pinned), streamed to the
+    device chunk_rows rows at a time; returns the estep_stats outputs (on mu's device)."""
+    if X_host.device.type != "cpu" or X_host.dim() != 2 or not X_host.is_contiguous():
+        raise ValueError("X_host must be a contiguous 2-d CPU tensor")
+    N, d = X_host.shape
+    K = mu.shape[0]
+    dev = mu.device
+    xt = _xtype(X_host)
+    _need(mu, "mu", torch.float32, (K, d), dev)
+    _need(var, "var", torch.float32, (K, d), dev)
+    _need(logw, "logw", torch.float32, (K,), dev)
+    Nk = torch.empty(K, dtype=torch.float32, device=dev)
+    Sx = torch.empty(K, d, dtype=torch.float32, device=dev)
+    Sxx = torch.empty(K, d, dtype=torch.float32, device=dev)
+    L = torch.empty((), dtype=torch.float64, device=dev)
+    lp = torch.empty(N, dtype=torch.float32, device=dev) if want_point_loglik else None
+    if ws is None:
+        ws = workspace_chunked(N, d, K, chunk_rows, xt, dev)
+    _check("gmm_estep_stats_chunked", lib().gmm_estep_stats_chunked(
+        _ptr(X_host), xt, N, d, _ptr(mu), _ptr(var), _ptr(logw), K, _ptr(Nk), _ptr(Sx), _ptr(Sxx), _ptr(L),
+        _ptr(lp), chunk_rows, _ptr(ws), ws.numel(), _stream(dev)))
     return Nk, Sx, Sxx, L, lp
 
 

@@ -96,3 +96,32 @@ def test_other_entry_points_validate(L):
     assert L.gmm_assign_top2(FAKE, 0, 10, 4, FAKE, FAKE, FAKE, 3, FAKE, FAKE, FAKE, 8, None) == -3
     assert L.gmm_estep_resp(FAKE, 0, 10, 4, FAKE, FAKE, FAKE, 3, None, None, FAKE, 1 << 40, 0, None) == -1
     assert L.gmm_estep_resp(FAKE, 1, 10, 4, FAKE, FAKE, FAKE, 3, FAKE, None, FAKE, 1 << 40, 9, None) == -1
+
+
+def _chunked(L, X=FAKE, xt=0, N=100, d=4, K=3, chunk=10, ws=FAKE, wsb=1 << 40):
+    return L.gmm_estep_stats_chunked(X, xt, N, d, FAKE, FAKE, FAKE, K, FAKE, FAKE, FAKE, FAKE, None, chunk,
+                                     ws, wsb, None)
+
+
+def test_chunked_argument_validation(L):
+    assert _chunked(L, chunk=0) == -1
+    assert _chunked(L, chunk=-5) == -1
+    assert _chunked(L, xt=3) == -1
+    assert _chunked(L, X=None) == -1
+    assert _chunked(L, d=129) == -2
+    assert _chunked(L, ws=None) == -3
+    assert _chunked(L, ws=ctypes.c_void_p(0x100010)) == -3
+    assert _chunked(L, wsb=64) == -3
+
+
+def test_chunked_workspace_bytes(L):
+    assert L.gmm_workspace_bytes_chunked(100, 4, 3, 0, 0) == 0
+    assert L.gmm_workspace_bytes_chunked(100, 4, 3, 10, 2) == 0
+    assert L.gmm_workspace_bytes_chunked(100, 200, 3, 10, 0) == 0
+    chunked = L.gmm_workspace_bytes_chunked(1 << 20, 128, 256, 1 << 16, 0)
+    # the workspace holds chunk-sized regions only: it does not grow with N
+    assert chunked > 2 * (1 << 16) * 128 * 4
+    assert L.gmm_workspace_bytes_chunked(1 << 30, 128, 256, 1 << 16, 0) == chunked
+    assert L.gmm_workspace_bytes_chunked(1 << 30, 128, 256, 1 << 16, 0) < L.gmm_workspace_bytes(1 << 30, 128, 256)
+    assert L.gmm_workspace_bytes_chunked(1 << 20, 128, 256, 1 << 16, 1) < chunked  # fp16 staging
+    assert chunked % 256 == 0
