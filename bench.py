@@ -72,6 +72,46 @@ def cpu_baseline(X, mu, var, logw, rows: int):
                       f"{rows} of {X.shape[0]} rows, same parameters; {dt:.2f} s on 1 host thread"}
 
 
+def host_streamed(args, w, X, mu, var, logw, torch, gmm, dev):
+    """One step = the row-chunked E-step over X in pinned host memory (copies of
+    chunk i+1 overlap the scoring of chunk i) plus the M-step, from the initial
+    parameters. Prints one JSON line with the PCIe-inclusive rate."""
+    N, d, K = X.shape[0], X.shape[1], mu.shape[0]
+    Xh = torch.from_numpy(X).pin_memory()
+    mu0, var0, lw0 = (torch.from_numpy(a.copy()).to(dev) for a in (mu, var, logw))
+    mud, vard, lwd = mu0.clone(), var0.clone(), lw0.clone()
+    xt = gmm.GMM_F16 if X.dtype == np.float16 else gmm.GMM_F32
+    ws = gmm.workspace_chunked(N, d, K, args.chunk_rows, xt, dev)
+
+    def step():
+        mud.copy_(mu0)
+        vard.copy_(var0)
+        lwd.copy_(lw0)
+        Nk, Sx, Sxx, _, _ = gmm.estep_stats_chunked(Xh, mud, vard, lwd, args.chunk_rows, ws=ws)
+        gmm.mstep(Nk, Sx, Sxx, N, VAR_FLOOR, mud, vard, lwd)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    xbytes = X.nbytes
+    out = {
+        "metric": METRIC + " [X streamed from pinned host memory]", "value": N * K / (ms * 1e-3), "unit": UNIT,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: N={N} d={d} K={K} {w.x_dtype}; X in pinned host memory, "
+                               f"{args.chunk_rows} rows per chunk; step = chunked E-step + M-step",
+                   "N": N, "d": d, "K": K, "x_dtype": w.x_dtype, "chunk_rows": args.chunk_rows},
+        "host_to_device_GBps": round(xbytes / (ms * 1e-3) / 1e9, 2),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -79,6 +119,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ref", choices=["tiny", "ref", "smallk", "largek", "ivf"])
     ap.add_argument("--cpu-rows", type=int, default=131072, help="row sample for the oracle baseline (0: skip)")
+    ap.add_argument("--x-on-host", action="store_true",
+                    help="keep X in pinned host memory and stream it through the row-chunked E-step "
+                         "(PCIe-inclusive rate; not the HBM-resident headline)")
+    ap.add_argument("--chunk-rows", type=int, default=1 << 18, help="rows per chunk with --x-on-host")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this E-step build runs on a "
@@ -92,6 +136,8 @@ def main(argv=None):
 
     w = datagen.WORKLOADS[args.workload]
     X, mu, var, logw = datagen.make_workload(args.workload)
+    if args.x_on_host:
+        return host_streamed(args, w, X, mu, var, logw, torch, gmm, dev)
     N, d, K = X.shape[0], X.shape[1], mu.shape[0]
     Xd = torch.from_numpy(X).to(dev)
     mu0, var0, lw0 = (torch.from_numpy(a.copy()).to(dev) for a in (mu, var, logw))
