@@ -6,6 +6,7 @@ this package. The HIP library never calls it and shares no code with it.
 from .gmm_oracle import (  # noqa: F401
     LOG_2PI,
     EMPTY_REL,
+    border_lists,
     component_scores,
     em,
     estep,

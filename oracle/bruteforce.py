@@ -63,3 +63,13 @@ def top2_loop(S):
                 b2 = k
         out.append((b1, b2))
     return out
+
+
+def border_lists_loop(idx, resp, K, threshold):
+    """The inverted lists by direct enumeration: list k = every n, in order,
+    whose first pick is k or whose second pick is k with resp >= threshold."""
+    lists = []
+    for k in range(K):
+        lists.append([n for n in range(len(idx))
+                      if idx[n][0] == k or (idx[n][1] == k and float(resp[n][1]) >= float(threshold))])
+    return lists

@@ -237,3 +237,36 @@ def top2(X, mu, var, logw, *, form="difference", row_chunk=_ROW_CHUNK):
         sel = np.take_along_axis(S, order[:, :take], axis=1)
         r[lo:hi, :take] = np.exp(sel - l[:, None])
     return idx, r
+
+
+# ---------------------------------------------------------------------------
+# Inverted lists with border vectors (from the top-2 assignment)
+# ---------------------------------------------------------------------------
+
+def border_lists(idx, resp, K, threshold):
+    """Inverted lists of a soft coarse quantizer with border vectors.
+
+    "Flash-GMM: a memory-efficient kernel for scalable soft clustering",
+    abstract: responsibilities let vectors near cluster borders be assigned
+    to several clusters. Reading taken: point n is listed under its most
+    responsible component idx[n, 0], and also under idx[n, 1] when
+    idx[n, 1] >= 0 and resp[n, 1] >= threshold (the comparison is made on the
+    float32 responsibility as given). Each list holds point indices in
+    increasing order.
+
+    Returns (offsets, members): offsets is int64 of length K + 1 (list k is
+    members[offsets[k]:offsets[k + 1]]), members int64 of length offsets[K].
+    """
+    idx = np.asarray(idx)
+    resp = np.asarray(resp, dtype=np.float32)
+    N = idx.shape[0]
+    n = np.arange(N, dtype=np.int64)
+    prim = idx[:, 0] >= 0
+    sec = (idx[:, 1] >= 0) & (resp[:, 1] >= np.float32(threshold))
+    keys = np.concatenate([idx[prim, 0], idx[sec, 1]]).astype(np.int64)
+    vals = np.concatenate([n[prim], n[sec]])
+    order = np.lexsort((vals, keys))  # by list, then by point index
+    members = vals[order]
+    counts = np.bincount(keys, minlength=K)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return offsets, members

@@ -146,3 +146,26 @@ def random_problem(seed: int, N: int, d: int, K: int, *, spread: float = 3.0,
     w = rng.dirichlet(np.ones(K)) if K > 0 else np.zeros(0)
     logw = np.log(w).astype(np.float32)
     return X, mu, var, logw
+
+
+def random_top2(seed: int, N: int, K: int, *, border_frac: float = 0.3):
+    """Synthetic top-2 assignments (idx N x 2 int32, resp N x 2 float32) for the
+    inverted-list build: a uniform first pick, a different uniform second
+    pick (-1 when K = 1), resp[:, 0] in [0.5, 1), and resp[:, 1] drawn below
+    1 - resp[:, 0], with about border_frac of the rows given a large second
+    responsibility. Random numbers only; no mixture arithmetic."""
+    rng = np.random.default_rng(seed)
+    idx = np.empty((N, 2), dtype=np.int32)
+    idx[:, 0] = rng.integers(0, K, N)
+    if K > 1:
+        off = rng.integers(1, K, N)
+        idx[:, 1] = (idx[:, 0] + off) % K
+    else:
+        idx[:, 1] = -1
+    r0 = rng.uniform(0.5, 1.0, N)
+    big = rng.random(N) < border_frac
+    r1 = np.where(big, (1.0 - r0) * rng.uniform(0.5, 1.0, N), (1.0 - r0) * rng.uniform(0.0, 0.02, N))
+    if K == 1:
+        r1[:] = 0.0
+    resp = np.stack([r0, r1], axis=1).astype(np.float32)
+    return idx, resp

@@ -260,3 +260,37 @@ def test_empty_input():
     mu = np.zeros((2, 3), np.float32)
     e = oracle.estep(X, mu, np.ones_like(mu), np.log([0.5, 0.5]))
     assert e["L"] == 0.0 and (e["Nk"] == 0).all() and e["l"].shape == (0,)
+
+
+# ---------------------------------------------------------------------------
+# Inverted lists with border vectors
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,N,K,thr", [(0, 200, 7, 0.1), (1, 57, 1, 0.1), (2, 300, 2, 0.0), (3, 150, 13, 2.0)])
+def test_border_lists_against_enumeration(seed, N, K, thr):
+    idx, resp = datagen.random_top2(seed, N, K)
+    off, mem = oracle.border_lists(idx, resp, K, thr)
+    ref = bruteforce.border_lists_loop(idx.tolist(), resp.tolist(), K, thr)
+    assert off[0] == 0 and len(off) == K + 1
+    for k in range(K):
+        assert mem[off[k]:off[k + 1]].tolist() == ref[k], k
+
+
+def test_border_lists_closed_forms():
+    idx, resp = datagen.random_top2(4, 1000, 9)
+    N = idx.shape[0]
+    # threshold above 1: no border vectors, the lists partition the points by first pick
+    off, mem = oracle.border_lists(idx, resp, 9, 1.5)
+    assert off[-1] == N and np.array_equal(np.sort(mem), np.arange(N))
+    assert np.array_equal(np.diff(off), np.bincount(idx[:, 0], minlength=9))
+    # threshold 0: every point sits in exactly two lists
+    off, mem = oracle.border_lists(idx, resp, 9, 0.0)
+    assert off[-1] == 2 * N and np.array_equal(np.bincount(mem, minlength=N), np.full(N, 2))
+    # general threshold: N + (number of second picks at or above it) entries, each list increasing
+    t = 0.05
+    off, mem = oracle.border_lists(idx, resp, 9, t)
+    assert off[-1] == N + int((resp[:, 1] >= np.float32(t)).sum())
+    for k in range(9):
+        seg = mem[off[k]:off[k + 1]]
+        assert np.all(np.diff(seg) > 0)
+        assert np.all((idx[seg, 0] == k) | ((idx[seg, 1] == k) & (resp[seg, 1] >= np.float32(t))))
