@@ -165,6 +165,24 @@ int gmm_estep_stats_chunked(const void* X_host, int32_t x_dtype, int64_t N, int3
  * limits (or chunk_rows < 1, unknown x_dtype). */
 size_t gmm_workspace_bytes_chunked(int64_t N, int32_t d, int32_t K, int64_t chunk_rows, int32_t x_dtype);
 
+/* Inverted lists with border vectors from a top-2 assignment (Flash-GMM
+ * abstract: a soft coarse quantizer assigns vectors near cluster borders to
+ * several clusters). idx and resp are the N x 2 outputs of gmm_assign_top2
+ * (device): point n is listed under idx[n][0] (which must lie in [0, K)) and,
+ * when idx[n][1] >= 0 and resp[n][1] >= border_threshold, also under
+ * idx[n][1]. Outputs (device): offsets, K + 1 int64 (list k is
+ * members[offsets[k] .. offsets[k+1]), offsets[K] = number of entries) and
+ * members, int32 point indices, increasing within each list. The result is
+ * a pure function of the inputs (no atomics decide any order).
+ * members_capacity must be >= 2N; N < 2^31. The workspace must hold
+ * gmm_border_lists_workspace_bytes(N, K) bytes, 256-byte aligned. */
+int gmm_border_lists(const int32_t* idx, const float* resp, int64_t N, int32_t K, float border_threshold,
+                     int64_t* offsets, int32_t* members, int64_t members_capacity,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for gmm_border_lists; 0 for arguments outside the limits. */
+size_t gmm_border_lists_workspace_bytes(int64_t N, int32_t K);
+
 #ifdef __cplusplus
 }
 #endif

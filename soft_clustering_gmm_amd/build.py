@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgmm_mi355x.so")
-SOURCES = ["gmm_kernels.hip", "gmm_api.cpp"]
+SOURCES = ["gmm_kernels.hip", "gmm_lists.hip", "gmm_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are disabled for all device code; the kernels' fp32

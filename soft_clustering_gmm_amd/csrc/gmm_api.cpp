@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <climits>
 #include <map>
 #include <mutex>
 
@@ -339,6 +340,27 @@ int gmm_estep_stats_chunked(const void* X_host, int32_t x_dtype, int64_t N, int3
   }
   if (e == hipSuccess) e = launch_finalize_stats(acc, K, d, Nk, Sx, Sxx, loglik_total, s);
   return hip_status(e);
+}
+
+static bool lists_args_ok(int64_t N, int32_t K) {
+  return N >= 0 && N <= INT32_MAX && K >= 1 && K <= kMaxK;
+}
+
+size_t gmm_border_lists_workspace_bytes(int64_t N, int32_t K) {
+  return lists_args_ok(N, K) ? lists_layout(N, K).bytes : 0;
+}
+
+int gmm_border_lists(const int32_t* idx, const float* resp, int64_t N, int32_t K, float border_threshold,
+                     int64_t* offsets, int32_t* members, int64_t members_capacity, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  if (N < 0 || K < 1) return GMM_EINVAL;
+  if (!lists_args_ok(N, K)) return GMM_EUNSUPPORTED;
+  if (!offsets || (N > 0 && (!idx || !resp || !members))) return GMM_EINVAL;
+  if (members_capacity < 2 * N) return GMM_EINVAL;
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 || ws_bytes < lists_layout(N, K).bytes)
+    return GMM_EWORKSPACE;
+  return hip_status(launch_border_lists(idx, resp, N, K, border_threshold, offsets, members, workspace,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int gmm_set_timing_events(void* start, void* stop) {

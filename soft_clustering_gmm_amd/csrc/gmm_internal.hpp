@@ -76,6 +76,14 @@ hipError_t launch_finalize_stats(const double* acc, int K, int d, float* Nk, flo
                                  double* loglik_total, hipStream_t stream);
 hipError_t launch_top2(const Plan& p, const void* X, int x_dtype, int32_t* idx, float* resp,
                        hipStream_t stream);
+// Border-vector inverted lists (gmm_lists.hip): workspace layout and launcher.
+struct ListsLayout {
+  int64_t blocks_a, blocks_b;  // blocks of the pass over the points, and of the second pass (0: none)
+  size_t o_H, o_O, o_total, o_keys, o_tmp_keys, o_tmp_vals, bytes;
+};
+ListsLayout lists_layout(int64_t N, int K);
+hipError_t launch_border_lists(const int32_t* idx, const float* resp, int64_t N, int K, float thr,
+                               int64_t* offsets, int32_t* members, void* workspace, hipStream_t stream);
 hipError_t launch_mstep(const float* Nk, const float* Sx, const float* Sxx, int64_t N, int d, int K,
                         float var_floor, float* mu, float* var, float* logw, hipStream_t stream);
 hipError_t launch_zero_outputs(float* Nk, float* Sx, float* Sxx, int d, int K,

@@ -23,6 +23,7 @@ EXPORTS = (
     "gmm_version", "gmm_error_string", "gmm_workspace_bytes", "gmm_estep_stats",
     "gmm_estep_stats_regime", "gmm_estep_resp", "gmm_mstep", "gmm_em_iterate", "gmm_assign_top2",
     "gmm_set_timing_events", "gmm_estep_stats_chunked", "gmm_workspace_bytes_chunked",
+    "gmm_border_lists", "gmm_border_lists_workspace_bytes",
 )
 
 
@@ -62,6 +63,10 @@ def _load() -> ctypes.CDLL:
     L.gmm_estep_stats_chunked.argtypes = [P, I32, I64, I32, P, P, P, I32, P, P, P, P, P, I64, P, SZ, P]
     L.gmm_workspace_bytes_chunked.restype = SZ
     L.gmm_workspace_bytes_chunked.argtypes = [I64, I32, I32, I64, I32]
+    L.gmm_border_lists.restype = ctypes.c_int
+    L.gmm_border_lists.argtypes = [P, P, I64, I32, F32, P, P, I64, P, SZ, P]
+    L.gmm_border_lists_workspace_bytes.restype = SZ
+    L.gmm_border_lists_workspace_bytes.argtypes = [I64, I32]
     return L
 
 
@@ -243,3 +248,25 @@ def assign_top2(X, mu, var, logw, *, ws=None):
         _ptr(X), _xtype(X), N, d, _ptr(mu), _ptr(var), _ptr(logw), K, _ptr(idx), _ptr(resp),
         _ptr(ws), ws.numel(), _stream(dev)))
     return idx, resp
+
+
+def border_lists(idx, resp, K: int, threshold: float, *, ws=None, members=None):
+    """Inverted lists with border vectors from a top-2 assignment (idx N x 2 int32,
+    resp N x 2 float32, on the GPU): returns (offsets[K+1] int64, members int32
+    of capacity 2N; the lists are members[:offsets[K]])."""
+    N = idx.shape[0]
+    dev = idx.device
+    _need(idx, "idx", torch.int32, (N, 2), dev)
+    _need(resp, "resp", torch.float32, (N, 2), dev)
+    offsets = torch.empty(K + 1, dtype=torch.int64, device=dev)
+    if members is None:
+        members = torch.empty(max(2 * N, 1), dtype=torch.int32, device=dev)
+    if ws is None:
+        nb = int(lib().gmm_border_lists_workspace_bytes(N, K))
+        if nb == 0:
+            raise ValueError(f"unsupported N={N} K={K}")
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    _check("gmm_border_lists", lib().gmm_border_lists(
+        _ptr(idx), _ptr(resp), N, K, float(threshold), _ptr(offsets), _ptr(members), members.numel(),
+        _ptr(ws), ws.numel(), _stream(dev)))
+    return offsets, members

@@ -125,3 +125,19 @@ def test_chunked_workspace_bytes(L):
     assert L.gmm_workspace_bytes_chunked(1 << 30, 128, 256, 1 << 16, 0) < L.gmm_workspace_bytes(1 << 30, 128, 256)
     assert L.gmm_workspace_bytes_chunked(1 << 20, 128, 256, 1 << 16, 1) < chunked  # fp16 staging
     assert chunked % 256 == 0
+
+
+def test_border_lists_argument_validation(L):
+    def call(idx=FAKE, resp=FAKE, N=100, K=8, off=FAKE, mem=FAKE, cap=200, ws=FAKE, wsb=1 << 40):
+        return L.gmm_border_lists(idx, resp, N, K, 0.1, off, mem, cap, ws, wsb, None)
+    assert call(N=-1) == -1
+    assert call(K=0) == -1
+    assert call(K=70000) == -2
+    assert call(N=1 << 31) == -2                 # point indices are int32
+    assert call(idx=None) == -1
+    assert call(off=None) == -1
+    assert call(cap=199) == -1                   # capacity must cover 2N entries
+    assert call(ws=None) == -3
+    assert call(wsb=8) == -3
+    assert L.gmm_border_lists_workspace_bytes(100, 0) == 0
+    assert L.gmm_border_lists_workspace_bytes(1 << 20, 1024) > L.gmm_border_lists_workspace_bytes(1 << 20, 256)
