@@ -112,6 +112,46 @@ def host_streamed(args, w, X, mu, var, logw, torch, gmm, dev):
     return 0
 
 
+def border_lists_bench(args, w, torch, gmm, dev):
+    """One step = the inverted-list build (gmm_border_lists) over a synthetic
+    top-2 assignment of the workload's N points and K lists, inputs in HBM.
+    HBM roofline on the algorithmic bytes: read idx and resp (16 B per point),
+    write one int32 per list entry and the K + 1 offsets."""
+    from soft_clustering_gmm_amd import datagen
+    N, K = w.N, w.K
+    idx, resp = datagen.random_top2(11, N, K)
+    idx_d, resp_d = torch.from_numpy(idx).to(dev), torch.from_numpy(resp).to(dev)
+    members = torch.empty(2 * N, dtype=torch.int32, device=dev)
+    ws = torch.empty(int(gmm.lib().gmm_border_lists_workspace_bytes(N, K)), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        off, _ = gmm.border_lists(idx_d, resp_d, K, args.border_threshold, ws=ws, members=members)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        off, _ = gmm.border_lists(idx_d, resp_d, K, args.border_threshold, ws=ws, members=members)
+        b.record()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    entries = int(off[-1].item())
+    alg = N * 16 + entries * 4 + (K + 1) * 8
+    gbps = alg / (k_ms * 1e-3) / 1e9
+    out = {
+        "metric": "border-vector inverted-list build, points/s", "value": N / (ms * 1e-3), "unit": "points/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": f"{w.name} shape: N={N} K={K}, synthetic top-2 (seed 11), threshold "
+                               f"{args.border_threshold}, {entries} list entries", "N": N, "K": K},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": alg, "avg_launch_ms": round(k_ms, 4)},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +163,10 @@ def main(argv=None):
                     help="keep X in pinned host memory and stream it through the row-chunked E-step "
                          "(PCIe-inclusive rate; not the HBM-resident headline)")
     ap.add_argument("--chunk-rows", type=int, default=1 << 18, help="rows per chunk with --x-on-host")
+    ap.add_argument("--border-lists", action="store_true",
+                    help="time the border-vector inverted-list build on the workload's N and K from a "
+                         "synthetic top-2 assignment resident in HBM")
+    ap.add_argument("--border-threshold", type=float, default=0.05)
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this E-step build runs on a "
@@ -135,6 +179,8 @@ def main(argv=None):
     dev = torch.device("cuda:0")
 
     w = datagen.WORKLOADS[args.workload]
+    if args.border_lists:
+        return border_lists_bench(args, w, torch, gmm, dev)
     X, mu, var, logw = datagen.make_workload(args.workload)
     if args.x_on_host:
         return host_streamed(args, w, X, mu, var, logw, torch, gmm, dev)

@@ -174,7 +174,7 @@ size_t gmm_workspace_bytes_chunked(int64_t N, int32_t d, int32_t K, int64_t chun
  * members[offsets[k] .. offsets[k+1]), offsets[K] = number of entries) and
  * members, int32 point indices, increasing within each list. The result is
  * a pure function of the inputs (no atomics decide any order).
- * members_capacity must be >= 2N; N < 2^31. The workspace must hold
+ * idx must be 8-byte aligned. members_capacity must be >= 2N; N < 2^31. The workspace must hold
  * gmm_border_lists_workspace_bytes(N, K) bytes, 256-byte aligned. */
 int gmm_border_lists(const int32_t* idx, const float* resp, int64_t N, int32_t K, float border_threshold,
                      int64_t* offsets, int32_t* members, int64_t members_capacity,

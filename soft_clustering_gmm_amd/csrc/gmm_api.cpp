@@ -356,6 +356,7 @@ int gmm_border_lists(const int32_t* idx, const float* resp, int64_t N, int32_t K
   if (N < 0 || K < 1) return GMM_EINVAL;
   if (!lists_args_ok(N, K)) return GMM_EUNSUPPORTED;
   if (!offsets || (N > 0 && (!idx || !resp || !members))) return GMM_EINVAL;
+  if (reinterpret_cast<uintptr_t>(idx) % 8 != 0) return GMM_EINVAL;  // read as (first, second) pairs
   if (members_capacity < 2 * N) return GMM_EINVAL;
   if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 || ws_bytes < lists_layout(N, K).bytes)
     return GMM_EWORKSPACE;

@@ -79,7 +79,7 @@ hipError_t launch_top2(const Plan& p, const void* X, int x_dtype, int32_t* idx, 
 // Border-vector inverted lists (gmm_lists.hip): workspace layout and launcher.
 struct ListsLayout {
   int64_t blocks_a, blocks_b;  // blocks of the pass over the points, and of the second pass (0: none)
-  size_t o_H, o_O, o_total, o_keys, o_tmp_keys, o_tmp_vals, bytes;
+  size_t o_H, o_O, o_total, o_S, o_keys, o_tmp_keys, o_tmp_vals, bytes;
 };
 ListsLayout lists_layout(int64_t N, int K);
 hipError_t launch_border_lists(const int32_t* idx, const float* resp, int64_t N, int K, float thr,

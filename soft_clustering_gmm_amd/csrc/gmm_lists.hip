@@ -12,16 +12,25 @@
 // articles (sorting by cluster id instead of scattering with atomics). Per
 // pass: per-block digit histograms, one exclusive scan over them (digit
 // major), then a scatter in which each one-wave block ranks its items
-// stably with ballots. Everything is integer work and deterministic.
+// stably with ballots into an LDS stage ordered by digit, and writes each
+// digit's run out contiguously. Everything is integer work and deterministic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gmm_device.hpp"
 #include "gmm_internal.hpp"
 
 namespace gmm {
 
-constexpr int kListPoints = 2048;  // points per block in the pass over (idx, resp)
-constexpr int kListItems = 4096;   // items per block in the second pass
+constexpr int kListPoints = 1024;  // points per block in the pass over (idx, resp)
+constexpr int kListItems = 2048;   // items per block in the second pass (= the LDS stage)
+
+// Orders this wave's LDS accesses (all lanes) before its later ones.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // Lanes of the wave whose digit equals x, from the 8 bit-plane ballots of
 // the wave's digits and the ballot of valid lanes.
@@ -38,10 +47,9 @@ __device__ __forceinline__ void digit_ballots(bool v, int dg, uint64_t* b, uint6
   for (int i = 0; i < 8; ++i) b[i] = __ballot(v && ((dg >> i) & 1));
 }
 
-// Items of point n: (idx[n][0], n) always, (idx[n][1], n) if it is a border vector.
-__device__ __forceinline__ bool second_pick(const int32_t* idx, const float* resp, int64_t n, float thr) {
-  return idx[2 * n + 1] >= 0 && resp[2 * n + 1] >= thr;
-}
+// Items of point n: (idx[n][0], n) always, and (idx[n][1], n) when
+// idx[n][1] >= 0 and resp[n][1] >= thr (a border vector). Items of a block
+// are ordered by point, first pick before second pick.
 
 // Histogram of the block's item digits -> H[digit * B + block].
 template <bool FROM_POINTS>
@@ -54,69 +62,176 @@ lists_hist_kernel(const int32_t* __restrict__ idx, const float* __restrict__ res
   for (int i = lane; i < 256; i += 64) h[i] = 0;
   __syncthreads();
   if (FROM_POINTS) {
+    constexpr int R = kListPoints / 64;
     const int64_t lo = blockIdx.x * (int64_t)kListPoints, hi = min(N, lo + kListPoints);
-    for (int64_t n = lo + lane; n < hi; n += 64) {
-      atomicAdd(&h[(idx[2 * n] >> shift) & 255], 1);
-      if (second_pick(idx, resp, n, thr)) atomicAdd(&h[(idx[2 * n + 1] >> shift) & 255], 1);
+    int2 pk[R];
+    float r1[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {  // all loads in flight at once
+      const int64_t n = lo + 64 * r + lane;
+      pk[r] = n < hi ? reinterpret_cast<const int2*>(idx)[n] : make_int2(0, -1);
+      r1[r] = n < hi ? resp[2 * n + 1] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (lo + 64 * r + lane < hi) {
+        atomicAdd(&h[(pk[r].x >> shift) & 255], 1);
+        if (pk[r].y >= 0 && r1[r] >= thr) atomicAdd(&h[(pk[r].y >> shift) & 255], 1);
+      }
     }
   } else {
+    constexpr int R = kListItems / 64;
     const int64_t M = *total;
     const int64_t lo = blockIdx.x * (int64_t)kListItems, hi = min(M, lo + kListItems);
-    for (int64_t i = lo + lane; i < hi; i += 64) atomicAdd(&h[(keys[i] >> shift) & 255], 1);
+    int ki[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t i = lo + 64 * r + lane;
+      ki[r] = i < hi ? keys[i] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (lo + 64 * r + lane < hi) atomicAdd(&h[(ki[r] >> shift) & 255], 1);
   }
   __syncthreads();
   for (int i = lane; i < 256; i += 64) H[(int64_t)i * B + blockIdx.x] = h[i];
 }
 
-// Exclusive scan of H (n = 256 * B entries, in index order) -> O; the grand
-// total goes to *total. One block of 1024 threads, each summing a contiguous
-// segment, then a scan of the 1024 segment sums.
-__global__ void __launch_bounds__(1024)
-lists_scan_kernel(const int32_t* __restrict__ H, int64_t n, int64_t* __restrict__ O, int64_t* __restrict__ total) {
-  __shared__ int64_t s[1024];
+// Exclusive scan of H (n = 256 * B entries, in index order) -> O, with the
+// grand total in *total: per-1024-entry segment sums, a scan of those sums
+// in one block, then each segment scanned locally on top of its offset.
+constexpr int kScanSeg = 1024;  // entries per segment (256 threads x 4)
+
+__device__ __forceinline__ int64_t block_excl_scan256(int64_t v, int64_t* s, int64_t* block_total) {
   const int t = threadIdx.x;
-  const int64_t per = (n + 1023) / 1024;
-  const int64_t lo = min(n, t * per), hi = min(n, lo + per);
-  int64_t a = 0;
-  for (int64_t i = lo; i < hi; ++i) a += H[i];
-  s[t] = a;
+  s[t] = v;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
-    const int64_t v = t >= o ? s[t - o] : 0;
+  for (int o = 1; o < 256; o <<= 1) {  // inclusive Hillis-Steele scan
+    const int64_t a = t >= o ? s[t - o] : 0;
     __syncthreads();
-    s[t] += v;
+    s[t] += a;
     __syncthreads();
   }
-  int64_t run = s[t] - a;
-  for (int64_t i = lo; i < hi; ++i) {
-    O[i] = run;
-    run += H[i];
-  }
-  if (t == 1023) *total = s[1023];
+  const int64_t incl = s[t];
+  *block_total = s[255];
+  __syncthreads();
+  return incl - v;
 }
 
-// Stable scatter of the block's items by digit: each 64-item round is ranked
-// with ballots, on top of per-digit running positions kept in LDS.
+__global__ void __launch_bounds__(256)
+lists_seg_sums_kernel(const int32_t* __restrict__ H, int64_t n, int64_t* __restrict__ S) {
+  __shared__ int64_t s[256];
+  const int64_t base = blockIdx.x * (int64_t)kScanSeg + 4 * threadIdx.x;
+  int64_t a = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a += base + j < n ? H[base + j] : 0;
+  int64_t tot;
+  block_excl_scan256(a, s, &tot);
+  if (threadIdx.x == 0) S[blockIdx.x] = tot;
+}
+
+// In place: S[i] <- sum of S[0..i), for nseg segment sums; *total <- sum of all.
+__global__ void __launch_bounds__(256)
+lists_seg_scan_kernel(int64_t* __restrict__ S, int64_t nseg, int64_t* __restrict__ total) {
+  __shared__ int64_t s[256];
+  const int64_t per = (nseg + 255) / 256;
+  const int64_t lo = min(nseg, threadIdx.x * per), hi = min(nseg, lo + per);
+  int64_t a = 0;
+  for (int64_t i = lo; i < hi; ++i) a += S[i];
+  int64_t tot;
+  int64_t run = block_excl_scan256(a, s, &tot);
+  for (int64_t i = lo; i < hi; ++i) {
+    const int64_t v = S[i];
+    S[i] = run;
+    run += v;
+  }
+  if (threadIdx.x == 0) *total = tot;
+}
+
+__global__ void __launch_bounds__(256)
+lists_seg_apply_kernel(const int32_t* __restrict__ H, int64_t n, const int64_t* __restrict__ S,
+                       int64_t* __restrict__ O) {
+  __shared__ int64_t s[256];
+  const int64_t base = blockIdx.x * (int64_t)kScanSeg + 4 * threadIdx.x;
+  int64_t v[4], a = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = base + j < n ? H[base + j] : 0;
+    a += v[j];
+  }
+  int64_t tot;
+  int64_t run = S[blockIdx.x] + block_excl_scan256(a, s, &tot);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (base + j < n) O[base + j] = run;
+    run += v[j];
+  }
+}
+
+static hipError_t excl_scan(const int32_t* H, int64_t n, int64_t* O, int64_t* S, int64_t* total,
+                            hipStream_t stream) {
+  const int64_t nseg = (n + kScanSeg - 1) / kScanSeg;
+  lists_seg_sums_kernel<<<(unsigned)nseg, 256, 0, stream>>>(H, n, S);
+  lists_seg_scan_kernel<<<1, 256, 0, stream>>>(S, nseg, total);
+  lists_seg_apply_kernel<<<(unsigned)nseg, 256, 0, stream>>>(H, n, S, O);
+  return hipGetLastError();
+}
+
+// Stable scatter of the block's items by digit. Each 64-item round is ranked
+// with ballots on top of per-digit running positions, into an LDS stage laid
+// out by digit (the block's exclusive digit offsets come from its histogram
+// column of H); the stage is then written out in order, so each digit's run
+// of the block lands contiguously at O[digit][block].
 template <bool FROM_POINTS>
 __global__ void __launch_bounds__(64)
 lists_scatter_kernel(const int32_t* __restrict__ idx, const float* __restrict__ resp, int64_t N, float thr,
                      const int32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
-                     const int64_t* __restrict__ total, int shift, const int64_t* __restrict__ O, int64_t B,
-                     int32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out) {
-  __shared__ int64_t base[256];
+                     const int64_t* __restrict__ total, int shift, const int32_t* __restrict__ H,
+                     const int64_t* __restrict__ O, int64_t B, int32_t* __restrict__ keys_out,
+                     int32_t* __restrict__ vals_out) {
+  __shared__ int32_t sk[kListItems], sv[kListItems];
+  __shared__ int32_t loc[256], loff[256];
+  __shared__ int64_t gofs[256];
   const int lane = threadIdx.x;
-  for (int i = lane; i < 256; i += 64) base[i] = O[(int64_t)i * B + blockIdx.x];
+  // local exclusive offsets of the 256 digits (lane holds digits 4 lane .. 4 lane + 3)
+  int h[4], hs = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[j] = H[(int64_t)(4 * lane + j) * B + blockIdx.x];
+    hs += h[j];
+  }
+  int run = wave_incl_scan(hs) - hs;
+  const int nitems = __builtin_amdgcn_readlane(run + hs, 63);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    loff[4 * lane + j] = run;
+    loc[4 * lane + j] = run;
+    gofs[4 * lane + j] = O[(int64_t)(4 * lane + j) * B + blockIdx.x];
+    run += h[j];
+  }
   __syncthreads();
   const uint64_t lt = (1ull << lane) - 1ull, le = lt | (1ull << lane);
   const uint64_t gt = ~le, ge = ~lt;
   if (FROM_POINTS) {
+    // all of the block's inputs are requested up front (one memory latency per block)
+    constexpr int R = kListPoints / 64;
     const int64_t lo = blockIdx.x * (int64_t)kListPoints, hi = min(N, lo + kListPoints);
-    for (int64_t r0 = lo; r0 < hi; r0 += 64) {
-      const int64_t n = r0 + lane;
+    int2 pk[R];
+    float r1[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t n = lo + 64 * r + lane;
+      pk[r] = n < hi ? reinterpret_cast<const int2*>(idx)[n] : make_int2(0, -1);
+      r1[r] = n < hi ? resp[2 * n + 1] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t n = lo + 64 * r + lane;
+      if (lo + 64 * r >= hi) break;
       const bool vp = n < hi;
-      const int kp = vp ? idx[2 * n] : 0;
-      const bool vs = vp && second_pick(idx, resp, n, thr);
-      const int ks = vs ? idx[2 * n + 1] : 0;
+      const int kp = pk[r].x;
+      const bool vs = vp && pk[r].y >= 0 && r1[r] >= thr;
+      const int ks = vs ? pk[r].y : 0;
       const int dp = (kp >> shift) & 255, ds = (ks >> shift) & 255;
       uint64_t bp[8], bs[8], mvp, mvs;
       digit_ballots(vp, dp, bp, &mvp);
@@ -124,49 +239,59 @@ lists_scatter_kernel(const int32_t* __restrict__ idx, const float* __restrict__ 
       // item order in the round: (lane 0 first pick, lane 0 second pick, lane 1 first pick, ...)
       const uint64_t pp = digit_match(dp, bp, mvp), ps = digit_match(dp, bs, mvs);
       const uint64_t sp = digit_match(ds, bp, mvp), ss = digit_match(ds, bs, mvs);
-      const int64_t pos_p = base[dp] + __popcll(pp & lt) + __popcll(ps & lt);
-      const int64_t pos_s = base[ds] + __popcll(sp & le) + __popcll(ss & lt);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int pos_p = loc[dp] + __popcll(pp & lt) + __popcll(ps & lt);
+      const int pos_s = loc[ds] + __popcll(sp & le) + __popcll(ss & lt);
+      wave_lds_fence();
       if (vp) {
-        keys_out[pos_p] = kp;
-        vals_out[pos_p] = (int32_t)n;
-        if ((pp & gt) == 0 && (ps & ge) == 0) base[dp] = pos_p + 1;  // last item of this digit
+        sk[pos_p] = kp;
+        sv[pos_p] = (int32_t)n;
+        if ((pp & gt) == 0 && (ps & ge) == 0) loc[dp] = pos_p + 1;  // last item of this digit
       }
       if (vs) {
-        keys_out[pos_s] = ks;
-        vals_out[pos_s] = (int32_t)n;
-        if ((sp & gt) == 0 && (ss & gt) == 0) base[ds] = pos_s + 1;
+        sk[pos_s] = ks;
+        sv[pos_s] = (int32_t)n;
+        if ((sp & gt) == 0 && (ss & gt) == 0) loc[ds] = pos_s + 1;
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_lds_fence();
     }
   } else {
+    constexpr int R = kListItems / 64;
     const int64_t M = *total;
     const int64_t lo = blockIdx.x * (int64_t)kListItems, hi = min(M, lo + kListItems);
-    for (int64_t r0 = lo; r0 < hi; r0 += 64) {
-      const int64_t i = r0 + lane;
+    int ki[R], vi[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t i = lo + 64 * r + lane;
+      ki[r] = i < hi ? keys_in[i] : 0;
+      vi[r] = i < hi ? vals_in[i] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t i = lo + 64 * r + lane;
+      if (lo + 64 * r >= hi) break;
       const bool v = i < hi;
-      const int k = v ? keys_in[i] : 0;
+      const int k = ki[r];
       const int dg = (k >> shift) & 255;
       uint64_t b[8], mv;
       digit_ballots(v, dg, b, &mv);
       const uint64_t m = digit_match(dg, b, mv);
-      const int64_t pos = base[dg] + __popcll(m & lt);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int pos = loc[dg] + __popcll(m & lt);
+      wave_lds_fence();
       if (v) {
-        keys_out[pos] = k;
-        vals_out[pos] = vals_in[i];
-        if ((m & gt) == 0) base[dg] = pos + 1;
+        sk[pos] = k;
+        sv[pos] = vi[r];
+        if ((m & gt) == 0) loc[dg] = pos + 1;
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_lds_fence();
     }
+  }
+  __syncthreads();
+  for (int j = lane; j < nitems; j += 64) {
+    const int k = sk[j];
+    const int dg = (k >> shift) & 255;
+    const int64_t g = gofs[dg] + (j - loff[dg]);
+    keys_out[g] = k;
+    vals_out[g] = sv[j];
   }
 }
 
@@ -207,6 +332,8 @@ ListsLayout lists_layout(int64_t N, int K) {
   off += up((size_t)256 * (Bmax > 0 ? Bmax : 1) * sizeof(int64_t));
   L.o_total = off;
   off += up(2 * sizeof(int64_t));
+  L.o_S = off;  // segment sums of the scan
+  off += up((size_t)((256 * (Bmax > 0 ? Bmax : 1) + kScanSeg - 1) / kScanSeg) * sizeof(int64_t));
   L.o_keys = off;  // final keys (sorted by list)
   off += up((size_t)(2 * N > 0 ? 2 * N : 1) * sizeof(int32_t));
   L.o_tmp_keys = off;
@@ -224,6 +351,7 @@ hipError_t launch_border_lists(const int32_t* idx, const float* resp, int64_t N,
   int32_t* H = reinterpret_cast<int32_t*>(w + L.o_H);
   int64_t* O = reinterpret_cast<int64_t*>(w + L.o_O);
   int64_t* total = reinterpret_cast<int64_t*>(w + L.o_total);
+  int64_t* S = reinterpret_cast<int64_t*>(w + L.o_S);
   int32_t* keys = reinterpret_cast<int32_t*>(w + L.o_keys);
   int32_t* tkeys = reinterpret_cast<int32_t*>(w + L.o_tmp_keys);
   int32_t* tvals = reinterpret_cast<int32_t*>(w + L.o_tmp_vals);
@@ -232,15 +360,17 @@ hipError_t launch_border_lists(const int32_t* idx, const float* resp, int64_t N,
     const int64_t BA = L.blocks_a;
     // pass A: digit 0 of every item, straight from (idx, resp)
     lists_hist_kernel<true><<<(unsigned)BA, 64, 0, stream>>>(idx, resp, N, thr, nullptr, nullptr, 0, H, BA);
-    lists_scan_kernel<<<1, 1024, 0, stream>>>(H, 256 * BA, O, total);
+    hipError_t e = excl_scan(H, 256 * BA, O, S, total, stream);
+    if (e != hipSuccess) return e;
     lists_scatter_kernel<true><<<(unsigned)BA, 64, 0, stream>>>(idx, resp, N, thr, nullptr, nullptr, nullptr, 0,
-                                                                 O, BA, two ? tkeys : keys, two ? tvals : members);
+                                                                 H, O, BA, two ? tkeys : keys, two ? tvals : members);
     if (two) {  // pass B: digit 1, from the pass-A order (stable)
       const int64_t BB = L.blocks_b;
       lists_hist_kernel<false><<<(unsigned)BB, 64, 0, stream>>>(nullptr, nullptr, 0, 0.f, tkeys, total, 8, H, BB);
-      lists_scan_kernel<<<1, 1024, 0, stream>>>(H, 256 * BB, O, total + 1);
+      e = excl_scan(H, 256 * BB, O, S, total + 1, stream);
+      if (e != hipSuccess) return e;
       lists_scatter_kernel<false><<<(unsigned)BB, 64, 0, stream>>>(nullptr, nullptr, 0, 0.f, tkeys, tvals, total, 8,
-                                                                    O, BB, keys, members);
+                                                                    H, O, BB, keys, members);
     }
   } else {
     lists_zero_total_kernel<<<1, 64, 0, stream>>>(total);

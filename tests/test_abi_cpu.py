@@ -135,6 +135,7 @@ def test_border_lists_argument_validation(L):
     assert call(K=70000) == -2
     assert call(N=1 << 31) == -2                 # point indices are int32
     assert call(idx=None) == -1
+    assert call(idx=ctypes.c_void_p(0x100004)) == -1   # not 8-byte aligned
     assert call(off=None) == -1
     assert call(cap=199) == -1                   # capacity must cover 2N entries
     assert call(ws=None) == -3
