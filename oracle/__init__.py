@@ -11,6 +11,9 @@ from .gmm_oracle import (  # noqa: F401
     em,
     estep,
     estep_rows,
+    kmeans,
+    kmeans_assign,
+    kmeans_update,
     log_gauss_diag,
     log_gauss_diag_expanded,
     mstep,

@@ -13,6 +13,8 @@ the Turbo-GMM abstract), so that a slip in either shows up as a mismatch.
 """
 from __future__ import annotations
 
+import math
+
 import mpmath
 
 mpmath.mp.dps = 50
@@ -73,3 +75,17 @@ def border_lists_loop(idx, resp, K, threshold):
         lists.append([n for n in range(len(idx))
                       if idx[n][0] == k or (idx[n][1] == k and float(resp[n][1]) >= float(threshold))])
     return lists
+
+
+def kmeans_assign_loop(X, C):
+    """Nearest centre by direct loops over points, centres and features."""
+    assign, dist2 = [], []
+    for x in X:
+        best, bk = None, -1
+        for k, c in enumerate(C):
+            s = math.fsum((float(a) - float(b)) ** 2 for a, b in zip(x, c))
+            if best is None or s < best:
+                best, bk = s, k
+        assign.append(bk)
+        dist2.append(best)
+    return assign, dist2

@@ -270,3 +270,53 @@ def border_lists(idx, resp, K, threshold):
     counts = np.bincount(keys, minlength=K)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     return offsets, members
+
+
+# ---------------------------------------------------------------------------
+# Lloyd's k-means (hard-assignment workload)
+# ---------------------------------------------------------------------------
+
+def kmeans_assign(X, C, *, row_chunk=_ROW_CHUNK):
+    """Nearest-centre assignment (Flash-KMeans articles: the assignment step of
+    Lloyd's algorithm, an argmin over point-centre distances).
+
+    Returns (assign, dist2): assign[n] = argmin_k ||x_n - c_k||^2 with ties to
+    the lower index, dist2[n] the minimum squared distance; float64 throughout.
+    """
+    X, C = _f64(X), _f64(C)
+    N, K = X.shape[0], C.shape[0]
+    assign = np.empty(N, dtype=np.int64)
+    dist2 = np.empty(N)
+    for lo in range(0, N, row_chunk):
+        hi = min(N, lo + row_chunk)
+        D = ((X[lo:hi, None, :] - C[None, :, :]) ** 2).sum(axis=2)
+        a = np.argmin(D, axis=1)  # first minimum: ties go to the lower index
+        assign[lo:hi] = a
+        dist2[lo:hi] = D[np.arange(hi - lo), a]
+    return assign, dist2
+
+
+def kmeans_update(X, assign, C_prev):
+    """Update step of Lloyd's algorithm: each centre becomes the mean of the
+    points assigned to it; a centre with no points keeps its previous value
+    (reading taken where the pages are silent)."""
+    X = _f64(X)
+    C = _f64(C_prev).copy()
+    K = C.shape[0]
+    counts = np.bincount(assign, minlength=K)
+    sums = np.zeros_like(C)
+    np.add.at(sums, assign, X)
+    nz = counts > 0
+    C[nz] = sums[nz] / counts[nz, None]
+    return C, counts
+
+
+def kmeans(X, C, iters):
+    """`iters` Lloyd iterations from C; returns (C, inertia history), the
+    inertia sum_n dist2[n] being that of the centres before each update."""
+    hist = []
+    for _ in range(iters):
+        a, d2 = kmeans_assign(X, C)
+        hist.append(d2.sum())
+        C, _ = kmeans_update(X, a, C)
+    return C, np.array(hist)

@@ -294,3 +294,53 @@ def test_border_lists_closed_forms():
         seg = mem[off[k]:off[k + 1]]
         assert np.all(np.diff(seg) > 0)
         assert np.all((idx[seg, 0] == k) | ((idx[seg, 1] == k) & (resp[seg, 1] >= np.float32(t))))
+
+
+# ---------------------------------------------------------------------------
+# Lloyd's k-means
+# ---------------------------------------------------------------------------
+
+def test_kmeans_assign_against_loops():
+    X, _, _, _ = datagen.random_problem(21, 40, 5, 4)
+    C = X[[3, 11, 17, 29, 31, 2]].astype(np.float64) + 0.25
+    a, d2 = oracle.kmeans_assign(X, C)
+    ra, rd = bruteforce.kmeans_assign_loop(X.tolist(), C.tolist())
+    assert a.tolist() == ra
+    np.testing.assert_allclose(d2, rd, rtol=1e-13, atol=1e-12)
+
+
+def test_kmeans_assign_is_the_gmm_hard_limit():
+    """Nearest centre = most responsible component of a mixture with unit
+    variances and equal weights (a different formula: the GMM score)."""
+    X, mu, _, _ = datagen.make_workload("tiny", N=1500)
+    K, d = mu.shape
+    a, _ = oracle.kmeans_assign(X, mu)
+    S = oracle.component_scores(X, mu, np.ones((K, d)), np.full(K, -math.log(K)))
+    assert np.array_equal(a, np.argmax(S, axis=1))
+
+
+def test_kmeans_assign_ties_go_low():
+    C = np.array([[1.0, 0.0], [-1.0, 0.0], [0.0, 5.0]])
+    a, d2 = oracle.kmeans_assign(np.array([[0.0, 0.0], [0.0, 1.0], [0.0, 4.0]]), C)
+    assert a.tolist() == [0, 0, 2] and d2.tolist() == [1.0, 2.0, 1.0]
+
+
+def test_kmeans_update_closed_forms():
+    rng = np.random.default_rng(5)
+    X = rng.integers(-8, 9, size=(300, 6)).astype(np.float64)
+    C0 = np.full((4, 6), 123.0)
+    # one cluster: the column means; a cluster with no points keeps its centre
+    C, n = oracle.kmeans_update(X, np.zeros(300, dtype=np.int64), C0)
+    np.testing.assert_allclose(C[0], X.mean(axis=0), rtol=0, atol=1e-12)
+    assert np.array_equal(C[1:], C0[1:]) and n.tolist() == [300, 0, 0, 0]
+    # exact small-integer means by direct sums
+    lab = rng.integers(0, 3, 300)
+    C, n = oracle.kmeans_update(X, lab, C0)
+    for k in range(3):
+        assert np.allclose(C[k], np.array([math.fsum(X[lab == k][:, j]) for j in range(6)]) / (lab == k).sum())
+
+
+def test_kmeans_inertia_non_increasing():
+    X, mu, _, _ = datagen.make_workload("tiny")
+    _, hist = oracle.kmeans(X, mu.astype(np.float64), 8)
+    assert (np.diff(hist) <= 1e-9 * hist[:-1]).all(), hist
