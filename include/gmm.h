@@ -183,6 +183,36 @@ int gmm_border_lists(const int32_t* idx, const float* resp, int64_t N, int32_t K
 /* Workspace bytes for gmm_border_lists; 0 for arguments outside the limits. */
 size_t gmm_border_lists_workspace_bytes(int64_t N, int32_t K);
 
+/* Lloyd's k-means on the same machinery (Flash-KMeans articles: a fused
+ * assignment that never writes the N x K distance matrix, and a centroid
+ * update that sorts points by cluster id and reduces contiguous segments
+ * instead of scattering with atomics). C is K x d float (device), X as in
+ * gmm_estep_stats; N < 2^31. The workspace must hold
+ * gmm_kmeans_workspace_bytes(N, d, K) bytes, 256-byte aligned.
+ *
+ * gmm_kmeans_assign: assign[n] = argmin_k ||x_n - c_k||^2 (ties to the lower
+ * index), computed from fp64 distances; dist2[n] (nullable) the minimum
+ * squared distance as float; *inertia (nullable, device double) their sum. */
+int gmm_kmeans_assign(const void* X, int32_t x_dtype, int64_t N, int32_t d, const float* C, int32_t K,
+                      int32_t* assign, float* dist2, double* inertia,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/* gmm_kmeans_update: C[k] (in/out) becomes the mean of the points with
+ * assign[n] == k, summed in fp64 in point order; a centre with no points
+ * keeps its value. counts (nullable, K int64) receives the cluster sizes.
+ * assign[n] must lie in [0, K). */
+int gmm_kmeans_update(const void* X, int32_t x_dtype, int64_t N, int32_t d, const int32_t* assign, int32_t K,
+                      float* C, int64_t* counts, void* workspace, size_t ws_bytes, void* stream);
+
+/* `iters` Lloyd iterations on the device (assign, then update); inertia_hist
+ * (device, iters doubles) receives the inertia of the centres before each
+ * update. C is in/out. Needs N >= 1. */
+int gmm_kmeans_iterate(const void* X, int32_t x_dtype, int64_t N, int32_t d, int32_t K, int32_t iters,
+                       float* C, double* inertia_hist, void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for the k-means entry points; 0 outside the limits. */
+size_t gmm_kmeans_workspace_bytes(int64_t N, int32_t d, int32_t K);
+
 #ifdef __cplusplus
 }
 #endif

@@ -364,6 +364,126 @@ int gmm_border_lists(const int32_t* idx, const float* resp, int64_t N, int32_t K
                                         static_cast<hipStream_t>(stream)));
 }
 
+// k-means workspace: [two-pass plan region] [unit variances K x d] [zero
+// log-weights K] [list-build region] [offsets K+1] [members N] [segment
+// counts K] [segment offsets K+1] [scan scratch] [segment sums] [assign N].
+struct KmLayout {
+  size_t plan, ones, zeros, lists, offsets, members, seg, segoff, scan, part, assign, total;
+  int64_t max_segments;
+};
+
+static bool kmeans_args_ok(int64_t N, int d, int K) {
+  return N >= 0 && N <= INT32_MAX && d >= 1 && d <= kMaxD && K >= 1 && K <= kMaxK;
+}
+
+static KmLayout kmeans_layout(int64_t N, int d, int K) {
+  KmLayout L{};
+  Plan p;
+  make_plan(N, d, K, GMM_REGIME_TWOPASS, nullptr, &p);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + std::max<size_t>(bytes, 1), 256);
+    return o;
+  };
+  L.plan = take(p.bytes);
+  L.ones = take((size_t)K * d * sizeof(float));
+  L.zeros = take((size_t)K * sizeof(float));
+  L.lists = take(lists_layout(N, K).bytes);
+  L.offsets = take((size_t)(K + 1) * sizeof(int64_t));
+  L.members = take((size_t)N * sizeof(int32_t));
+  L.seg = take((size_t)K * sizeof(int32_t));
+  L.segoff = take((size_t)(K + 1) * sizeof(int64_t));
+  L.scan = take((size_t)((K + 1023) / 1024 + 1) * sizeof(int64_t));
+  L.max_segments = kmeans_max_segments(N, K);
+  L.part = take((size_t)L.max_segments * d * sizeof(double));
+  L.assign = take((size_t)N * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
+size_t gmm_kmeans_workspace_bytes(int64_t N, int32_t d, int32_t K) {
+  return kmeans_args_ok(N, d, K) ? kmeans_layout(N, d, K).total : 0;
+}
+
+static int kmeans_check(const void* X, int32_t xt, int64_t N, int32_t d, int32_t K, const float* C, void* ws,
+                        size_t ws_bytes) {
+  if (xt != GMM_F32 && xt != GMM_F16) return GMM_EINVAL;
+  if (N < 0 || d < 1 || K < 1) return GMM_EINVAL;
+  if (!kmeans_args_ok(N, d, K)) return GMM_EUNSUPPORTED;
+  if ((N > 0 && !X) || !C) return GMM_EINVAL;
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % 256 != 0 || ws_bytes < kmeans_layout(N, d, K).total)
+    return GMM_EWORKSPACE;
+  return GMM_OK;
+}
+
+static hipError_t kmeans_assign_impl(const void* X, int32_t xt, int64_t N, int32_t d, const float* C, int32_t K,
+                                     int32_t* assign, float* dist2, double* inertia, char* w, const KmLayout& L,
+                                     hipStream_t s) {
+  float* ones = reinterpret_cast<float*>(w + L.ones);
+  float* zeros = reinterpret_cast<float*>(w + L.zeros);
+  Plan p;
+  make_plan(N, d, K, GMM_REGIME_TWOPASS, w + L.plan, &p);
+  hipError_t e = launch_fill(ones, (int64_t)K * d, 1.f, s);
+  if (e == hipSuccess) e = launch_fill(zeros, K, 0.f, s);
+  if (e == hipSuccess) e = launch_precompute(p, C, ones, zeros, s);
+  if (e == hipSuccess) e = launch_kmeans_assign(p, X, xt, assign, dist2, inertia, s);
+  return e;
+}
+
+static hipError_t kmeans_update_impl(const void* X, int32_t xt, int64_t N, int32_t d, const int32_t* assign,
+                                     int32_t K, float* C, int64_t* counts, char* w, const KmLayout& L,
+                                     hipStream_t s) {
+  int64_t* offsets = reinterpret_cast<int64_t*>(w + L.offsets);
+  int32_t* members = reinterpret_cast<int32_t*>(w + L.members);
+  hipError_t e = launch_border_lists(assign, nullptr, N, K, 0.f, offsets, members, w + L.lists, s);
+  if (e == hipSuccess)
+    e = launch_kmeans_update(X, xt, d, K, offsets, members, reinterpret_cast<int32_t*>(w + L.seg),
+                             reinterpret_cast<int64_t*>(w + L.segoff), reinterpret_cast<int64_t*>(w + L.scan),
+                             reinterpret_cast<double*>(w + L.part), L.max_segments, C, counts, s);
+  return e;
+}
+
+int gmm_kmeans_assign(const void* X, int32_t x_dtype, int64_t N, int32_t d, const float* C, int32_t K,
+                      int32_t* assign, float* dist2, double* inertia, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  int st = kmeans_check(X, x_dtype, N, d, K, C, workspace, ws_bytes);
+  if (st) return st;
+  if (N > 0 && !assign) return GMM_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) return inertia ? hip_status(launch_zero_outputs(nullptr, nullptr, nullptr, d, K, inertia, s)) : GMM_OK;
+  const KmLayout L = kmeans_layout(N, d, K);
+  return hip_status(kmeans_assign_impl(X, x_dtype, N, d, C, K, assign, dist2, inertia,
+                                       static_cast<char*>(workspace), L, s));
+}
+
+int gmm_kmeans_update(const void* X, int32_t x_dtype, int64_t N, int32_t d, const int32_t* assign, int32_t K,
+                      float* C, int64_t* counts, void* workspace, size_t ws_bytes, void* stream) {
+  int st = kmeans_check(X, x_dtype, N, d, K, C, workspace, ws_bytes);
+  if (st) return st;
+  if (N > 0 && !assign) return GMM_EINVAL;
+  const KmLayout L = kmeans_layout(N, d, K);
+  return hip_status(kmeans_update_impl(X, x_dtype, N, d, assign, K, C, counts, static_cast<char*>(workspace), L,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int gmm_kmeans_iterate(const void* X, int32_t x_dtype, int64_t N, int32_t d, int32_t K, int32_t iters, float* C,
+                       double* inertia_hist, void* workspace, size_t ws_bytes, void* stream) {
+  int st = kmeans_check(X, x_dtype, N, d, K, C, workspace, ws_bytes);
+  if (st) return st;
+  if (N < 1 || iters < 0 || (iters > 0 && !inertia_hist)) return GMM_EINVAL;
+  const KmLayout L = kmeans_layout(N, d, K);
+  char* w = static_cast<char*>(workspace);
+  int32_t* assign = reinterpret_cast<int32_t*>(w + L.assign);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int it = 0; it < iters; ++it) {
+    hipError_t e = kmeans_assign_impl(X, x_dtype, N, d, C, K, assign, nullptr, inertia_hist + it, w, L, s);
+    if (e == hipSuccess) e = kmeans_update_impl(X, x_dtype, N, d, assign, K, C, nullptr, w, L, s);
+    if (e != hipSuccess) return GMM_EHIP;
+  }
+  return GMM_OK;
+}
+
 int gmm_set_timing_events(void* start, void* stop) {
   set_timing_events(static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
   return GMM_OK;

@@ -84,6 +84,18 @@ struct ListsLayout {
 ListsLayout lists_layout(int64_t N, int K);
 hipError_t launch_border_lists(const int32_t* idx, const float* resp, int64_t N, int K, float thr,
                                int64_t* offsets, int32_t* members, void* workspace, hipStream_t stream);
+// Lloyd's k-means: nearest-centre assignment through the fp64 top-score pass
+// (the plan's parameters packed from centres, unit variances, zero
+// log-weights); dist2 and inertia (sum of dist2) are nullable.
+hipError_t launch_kmeans_assign(const Plan& p, const void* X, int x_dtype, int32_t* assign, float* dist2,
+                                double* inertia, hipStream_t stream);
+hipError_t launch_fill(float* a, int64_t n, float v, hipStream_t stream);
+// k-means update from the lists of a hard assignment (gmm_lists.hip).
+int64_t kmeans_max_segments(int64_t N, int K);
+hipError_t launch_kmeans_update(const void* X, int x_dtype, int d, int K, const int64_t* offsets,
+                                const int32_t* members, int32_t* seg, int64_t* segoff, int64_t* scan_tmp,
+                                double* part, int64_t max_segments, float* C, int64_t* counts,
+                                hipStream_t stream);
 hipError_t launch_mstep(const float* Nk, const float* Sx, const float* Sxx, int64_t N, int d, int K,
                         float var_floor, float* mu, float* var, float* logw, hipStream_t stream);
 hipError_t launch_zero_outputs(float* Nk, float* Sx, float* Sxx, int d, int K,

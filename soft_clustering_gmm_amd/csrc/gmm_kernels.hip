@@ -1022,7 +1022,8 @@ __global__ void __launch_bounds__(256)
 estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
                  const double* __restrict__ W64p, const double* __restrict__ c64e,
                  float2* __restrict__ rowref, float* __restrict__ ll_point, double* __restrict__ llpart,
-                 int32_t* __restrict__ tidx, float* __restrict__ tresp) {
+                 int32_t* __restrict__ tidx, float* __restrict__ tresp, int32_t* __restrict__ kassign,
+                 float* __restrict__ kdist2, double kconst) {
   constexpr int DP = 32 * DT, S = DP / 2, XS = DP + 1;
   __shared__ float xs[64 * XS];
   __shared__ double sm[kLseWaves][64], sz[kLseWaves][64], sv1[kLseWaves][64], sv2[kLseWaves][64];
@@ -1135,8 +1136,15 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
     }
     const double l = mm + log(zz);
     const int64_t gr = r0 + tid;
-    sl[tid] = gr < N ? l : 0.0;
-    if (gr < N) {
+    // nearest-centre mode (unit variances, zero log-weights): the top score is
+    // -dist^2 / 2 + const, so dist^2 = -2 * top + kconst; block sums of dist^2
+    // replace those of l
+    const double d2 = -2.0 * a1 + kconst;
+    sl[tid] = gr < N ? (kassign ? d2 : l) : 0.0;
+    if (gr < N && kassign) {
+      kassign[gr] = b1;
+      if (kdist2) kdist2[gr] = (float)d2;
+    } else if (gr < N) {
       const float mref = (float)mm;
       if (rowref) rowref[gr] = make_float2(mref, (float)(l - (double)mref));
       if (ll_point) ll_point[gr] = (float)l;
@@ -1161,7 +1169,6 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
 // Reductions, M-step, fills
 // ---------------------------------------------------------------------------
 
-// out element (k, e) of [Nk | Sx | Sxx] = sum over chunks p in order 0..P-1.
 // Fixed-order fp64 sum over the P statistics partials of output element e
 // (0: Nk, 1..d: Sx, d+1..2d: Sxx) of component k.
 __device__ __forceinline__ double sum_partials(const float* __restrict__ partials, int64_t P, int Kp, int E,
@@ -1316,10 +1323,11 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
 
 template <int DT, bool TOP2, typename XT>
 static hipError_t run_lse(const Plan& p, const XT* X, float* ll_point, int32_t* idx, float* resp,
-                          hipStream_t stream) {
+                          hipStream_t stream, int32_t* kassign = nullptr, float* kdist2 = nullptr,
+                          double kconst = 0.0) {
   const Workspace& w = p.ws;
   estep_lse_kernel<DT, TOP2, XT><<<(unsigned)p.tiles, 256, 0, stream>>>(
-      X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp);
+      X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp, kassign, kdist2, kconst);
   return hipGetLastError();
 }
 
@@ -1447,6 +1455,45 @@ hipError_t launch_top2(const Plan& p, const void* X, int x_dtype, int32_t* idx, 
     }
   }
   return e;
+}
+
+hipError_t launch_kmeans_assign(const Plan& p, const void* X, int x_dtype, int32_t* assign, float* dist2,
+                                double* inertia, hipStream_t stream) {
+  if (p.N == 0) return hipSuccess;
+  const double kconst = -(double)p.d * kLog2Pi;  // the score's -d/2 log(2 pi), doubled
+  hipError_t e = hipSuccess;
+  if (x_dtype == 1) {
+    const _Float16* x = reinterpret_cast<const _Float16*>(X);
+    switch (p.DT) {
+      case 1: e = run_lse<1, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
+      case 2: e = run_lse<2, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
+      case 3: e = run_lse<3, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
+      default: e = run_lse<4, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
+    }
+  } else {
+    const float* x = reinterpret_cast<const float*>(X);
+    switch (p.DT) {
+      case 1: e = run_lse<1, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
+      case 2: e = run_lse<2, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
+      case 3: e = run_lse<3, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
+      default: e = run_lse<4, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
+    }
+  }
+  if (e == hipSuccess && inertia) {
+    reduce_ll_kernel<false><<<1, 256, 0, stream>>>(p.ws.llpart, p.tiles, inertia, 0);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+__global__ void fill_kernel(float* __restrict__ a, int64_t n, float v) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t < n) a[t] = v;
+}
+
+hipError_t launch_fill(float* a, int64_t n, float v, hipStream_t stream) {
+  if (n > 0) fill_kernel<<<nblocks(n, 256), 256, 0, stream>>>(a, n, v);
+  return hipGetLastError();
 }
 
 hipError_t launch_mstep(const float* Nk, const float* Sx, const float* Sxx, int64_t N, int d, int K,

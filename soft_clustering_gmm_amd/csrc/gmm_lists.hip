@@ -49,7 +49,9 @@ __device__ __forceinline__ void digit_ballots(bool v, int dg, uint64_t* b, uint6
 
 // Items of point n: (idx[n][0], n) always, and (idx[n][1], n) when
 // idx[n][1] >= 0 and resp[n][1] >= thr (a border vector). Items of a block
-// are ordered by point, first pick before second pick.
+// are ordered by point, first pick before second pick. With resp == nullptr
+// idx is one list id per point (hard assignments) and there are no second
+// picks.
 
 // Histogram of the block's item digits -> H[digit * B + block].
 template <bool FROM_POINTS>
@@ -69,8 +71,13 @@ lists_hist_kernel(const int32_t* __restrict__ idx, const float* __restrict__ res
 #pragma unroll
     for (int r = 0; r < R; ++r) {  // all loads in flight at once
       const int64_t n = lo + 64 * r + lane;
-      pk[r] = n < hi ? reinterpret_cast<const int2*>(idx)[n] : make_int2(0, -1);
-      r1[r] = n < hi ? resp[2 * n + 1] : 0.f;
+      if (resp) {  // top-2 pairs
+        pk[r] = n < hi ? reinterpret_cast<const int2*>(idx)[n] : make_int2(0, -1);
+        r1[r] = n < hi ? resp[2 * n + 1] : 0.f;
+      } else {  // one assignment per point
+        pk[r] = make_int2(n < hi ? idx[n] : 0, -1);
+        r1[r] = 0.f;
+      }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -221,8 +228,13 @@ lists_scatter_kernel(const int32_t* __restrict__ idx, const float* __restrict__ 
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t n = lo + 64 * r + lane;
-      pk[r] = n < hi ? reinterpret_cast<const int2*>(idx)[n] : make_int2(0, -1);
-      r1[r] = n < hi ? resp[2 * n + 1] : 0.f;
+      if (resp) {  // top-2 pairs
+        pk[r] = n < hi ? reinterpret_cast<const int2*>(idx)[n] : make_int2(0, -1);
+        r1[r] = n < hi ? resp[2 * n + 1] : 0.f;
+      } else {  // one assignment per point
+        pk[r] = make_int2(n < hi ? idx[n] : 0, -1);
+        r1[r] = 0.f;
+      }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -376,6 +388,105 @@ hipError_t launch_border_lists(const int32_t* idx, const float* resp, int64_t N,
     lists_zero_total_kernel<<<1, 64, 0, stream>>>(total);
   }
   lists_offsets_kernel<<<(unsigned)((K + 1 + 255) / 256), 256, 0, stream>>>(keys, total, K, offsets);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Lloyd's k-means update through the sorted lists (sort-inverse update of
+// the Flash-KMeans articles): each list is summed as contiguous segments of
+// kSegRows members, segment sums are combined per list in segment order, and
+// the centre becomes sum / count (a list with no members keeps its centre).
+// Fixed orders throughout: deterministic.
+// ---------------------------------------------------------------------------
+
+constexpr int kSegRows = 1024;
+
+__global__ void kmeans_segcount_kernel(const int64_t* __restrict__ offsets, int K, int32_t* __restrict__ seg) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < K) seg[k] = (int32_t)((offsets[k + 1] - offsets[k] + kSegRows - 1) / kSegRows);
+}
+
+// Block b sums segment b: rows members[start, end) of list k, where k is the
+// last list whose first segment is <= b. Wave w takes rows start + w + 4i in
+// groups of 8 (their loads in flight together); lanes hold features lane and
+// lane + 64 in fp64; the four waves are combined in order.
+template <typename XT>
+__global__ void __launch_bounds__(256)
+kmeans_segsum_kernel(const XT* __restrict__ X, int d, const int64_t* __restrict__ offsets,
+                     const int32_t* __restrict__ members, const int64_t* __restrict__ segoff, int K,
+                     double* __restrict__ part) {
+  __shared__ double s[4][128];
+  const int64_t b = blockIdx.x;
+  if (b >= segoff[K]) return;
+  int lo = 0, hi = K - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (segoff[mid] <= b)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int k = lo;
+  const int64_t start = offsets[k] + (b - segoff[k]) * kSegRows;
+  const int64_t end = min(start + kSegRows, offsets[k + 1]);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int f0 = lane, f1 = lane + 64;
+  double a0 = 0.0, a1 = 0.0;
+  constexpr int G = 8;
+  for (int64_t i0 = start + wave; i0 < end; i0 += 4 * G) {
+    float v0[G], v1[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int64_t i = i0 + 4 * j;
+      const bool in = i < end;
+      const XT* row = X + (int64_t)(in ? members[i] : 0) * d;
+      v0[j] = in && f0 < d ? (float)row[f0] : 0.f;
+      v1[j] = in && f1 < d ? (float)row[f1] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      a0 += (double)v0[j];
+      a1 += (double)v1[j];
+    }
+  }
+  s[wave][f0] = a0;
+  s[wave][f1] = a1;
+  __syncthreads();
+  if (threadIdx.x < d)
+    part[b * d + threadIdx.x] = (s[0][threadIdx.x] + s[1][threadIdx.x]) + (s[2][threadIdx.x] + s[3][threadIdx.x]);
+}
+
+__global__ void kmeans_finalize_kernel(const double* __restrict__ part, const int64_t* __restrict__ segoff,
+                                       const int64_t* __restrict__ offsets, int K, int d, float* __restrict__ C,
+                                       int64_t* __restrict__ counts) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= (int64_t)K * d) return;
+  const int k = (int)(t / d), j = (int)(t - (int64_t)k * d);
+  const int64_t L = offsets[k + 1] - offsets[k];
+  if (j == 0 && counts) counts[k] = L;
+  if (L == 0) return;
+  double a = 0.0;
+  for (int64_t g = segoff[k]; g < segoff[k + 1]; ++g) a += part[g * d + j];
+  C[t] = (float)(a / (double)L);
+}
+
+int64_t kmeans_max_segments(int64_t N, int K) { return (N + kSegRows - 1) / kSegRows + K; }
+
+hipError_t launch_kmeans_update(const void* X, int x_dtype, int d, int K, const int64_t* offsets,
+                                const int32_t* members, int32_t* seg, int64_t* segoff, int64_t* scan_tmp,
+                                double* part, int64_t max_segments, float* C, int64_t* counts,
+                                hipStream_t stream) {
+  kmeans_segcount_kernel<<<(unsigned)((K + 255) / 256), 256, 0, stream>>>(offsets, K, seg);
+  hipError_t e = excl_scan(seg, K, segoff, scan_tmp, segoff + K, stream);
+  if (e != hipSuccess) return e;
+  if (x_dtype == 1)
+    kmeans_segsum_kernel<_Float16><<<(unsigned)max_segments, 256, 0, stream>>>(
+        reinterpret_cast<const _Float16*>(X), d, offsets, members, segoff, K, part);
+  else
+    kmeans_segsum_kernel<float><<<(unsigned)max_segments, 256, 0, stream>>>(reinterpret_cast<const float*>(X), d,
+                                                                              offsets, members, segoff, K, part);
+  const int64_t n = (int64_t)K * d;
+  kmeans_finalize_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(part, segoff, offsets, K, d, C, counts);
   return hipGetLastError();
 }
 

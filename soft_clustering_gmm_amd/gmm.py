@@ -24,6 +24,7 @@ EXPORTS = (
     "gmm_estep_stats_regime", "gmm_estep_resp", "gmm_mstep", "gmm_em_iterate", "gmm_assign_top2",
     "gmm_set_timing_events", "gmm_estep_stats_chunked", "gmm_workspace_bytes_chunked",
     "gmm_border_lists", "gmm_border_lists_workspace_bytes",
+    "gmm_kmeans_assign", "gmm_kmeans_update", "gmm_kmeans_iterate", "gmm_kmeans_workspace_bytes",
 )
 
 
@@ -67,6 +68,14 @@ def _load() -> ctypes.CDLL:
     L.gmm_border_lists.argtypes = [P, P, I64, I32, F32, P, P, I64, P, SZ, P]
     L.gmm_border_lists_workspace_bytes.restype = SZ
     L.gmm_border_lists_workspace_bytes.argtypes = [I64, I32]
+    L.gmm_kmeans_assign.restype = ctypes.c_int
+    L.gmm_kmeans_assign.argtypes = [P, I32, I64, I32, P, I32, P, P, P, P, SZ, P]
+    L.gmm_kmeans_update.restype = ctypes.c_int
+    L.gmm_kmeans_update.argtypes = [P, I32, I64, I32, P, I32, P, P, P, SZ, P]
+    L.gmm_kmeans_iterate.restype = ctypes.c_int
+    L.gmm_kmeans_iterate.argtypes = [P, I32, I64, I32, I32, I32, P, P, P, SZ, P]
+    L.gmm_kmeans_workspace_bytes.restype = SZ
+    L.gmm_kmeans_workspace_bytes.argtypes = [I64, I32, I32]
     return L
 
 
@@ -270,3 +279,53 @@ def border_lists(idx, resp, K: int, threshold: float, *, ws=None, members=None):
         _ptr(idx), _ptr(resp), N, K, float(threshold), _ptr(offsets), _ptr(members), members.numel(),
         _ptr(ws), ws.numel(), _stream(dev)))
     return offsets, members
+
+
+def kmeans_workspace(N: int, d: int, K: int, device) -> torch.Tensor:
+    nb = int(lib().gmm_kmeans_workspace_bytes(N, d, K))
+    if nb == 0:
+        raise ValueError(f"unsupported shape N={N} d={d} K={K}")
+    return torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+def _kmeans_args(X, C):
+    if X.dim() != 2 or not X.is_contiguous() or X.device.type != "cuda":
+        raise ValueError("X must be a contiguous N x d GPU tensor")
+    N, d = X.shape
+    K = C.shape[0]
+    _need(C, "C", torch.float32, (K, d), X.device)
+    return N, d, K, X.device
+
+
+def kmeans_assign(X, C, *, ws=None):
+    """Nearest centres: (assign[N] int32, dist2[N] float32, inertia 0-d float64)."""
+    N, d, K, dev = _kmeans_args(X, C)
+    assign = torch.empty(N, dtype=torch.int32, device=dev)
+    dist2 = torch.empty(N, dtype=torch.float32, device=dev)
+    inertia = torch.empty((), dtype=torch.float64, device=dev)
+    ws = kmeans_workspace(N, d, K, dev) if ws is None else ws
+    _check("gmm_kmeans_assign", lib().gmm_kmeans_assign(
+        _ptr(X), _xtype(X), N, d, _ptr(C), K, _ptr(assign), _ptr(dist2), _ptr(inertia), _ptr(ws), ws.numel(),
+        _stream(dev)))
+    return assign, dist2, inertia
+
+
+def kmeans_update(X, assign, C, *, ws=None):
+    """In-place centre update from a hard assignment; returns the counts (int64 K)."""
+    N, d, K, dev = _kmeans_args(X, C)
+    _need(assign, "assign", torch.int32, (N,), dev)
+    counts = torch.empty(K, dtype=torch.int64, device=dev)
+    ws = kmeans_workspace(N, d, K, dev) if ws is None else ws
+    _check("gmm_kmeans_update", lib().gmm_kmeans_update(
+        _ptr(X), _xtype(X), N, d, _ptr(assign), K, _ptr(C), _ptr(counts), _ptr(ws), ws.numel(), _stream(dev)))
+    return counts
+
+
+def kmeans_iterate(X, C, iters: int, *, ws=None):
+    """`iters` Lloyd iterations in place on C; returns the inertia history (device float64)."""
+    N, d, K, dev = _kmeans_args(X, C)
+    hist = torch.empty(max(iters, 1), dtype=torch.float64, device=dev)
+    ws = kmeans_workspace(N, d, K, dev) if ws is None else ws
+    _check("gmm_kmeans_iterate", lib().gmm_kmeans_iterate(
+        _ptr(X), _xtype(X), N, d, K, iters, _ptr(C), _ptr(hist), _ptr(ws), ws.numel(), _stream(dev)))
+    return hist[:iters]

@@ -142,3 +142,21 @@ def test_border_lists_argument_validation(L):
     assert call(wsb=8) == -3
     assert L.gmm_border_lists_workspace_bytes(100, 0) == 0
     assert L.gmm_border_lists_workspace_bytes(1 << 20, 1024) > L.gmm_border_lists_workspace_bytes(1 << 20, 256)
+
+
+def test_kmeans_argument_validation(L):
+    def assign(X=FAKE, xt=0, N=100, d=4, K=3, C=FAKE, out=FAKE, ws=FAKE, wsb=1 << 40):
+        return L.gmm_kmeans_assign(X, xt, N, d, C, K, out, None, None, ws, wsb, None)
+    assert assign(N=-1) == -1
+    assert assign(xt=9) == -1
+    assert assign(C=None) == -1
+    assert assign(out=None) == -1
+    assert assign(d=129) == -2
+    assert assign(N=1 << 31) == -2
+    assert assign(ws=None) == -3
+    assert assign(wsb=100) == -3
+    assert L.gmm_kmeans_update(FAKE, 0, 100, 4, None, 3, FAKE, None, FAKE, 1 << 40, None) == -1
+    assert L.gmm_kmeans_iterate(FAKE, 0, 0, 4, 3, 2, FAKE, FAKE, FAKE, 1 << 40, None) == -1   # N >= 1
+    assert L.gmm_kmeans_iterate(FAKE, 0, 10, 4, 3, 2, FAKE, None, FAKE, 1 << 40, None) == -1  # history needed
+    assert L.gmm_kmeans_workspace_bytes(100, 4, 0) == 0
+    assert L.gmm_kmeans_workspace_bytes(1000, 4, 3) > 0

@@ -1,0 +1,102 @@
+"""GPU parity of Lloyd's k-means (gmm_kmeans_assign / _update / _iterate)
+against the float64 oracle.
+
+The assignment is an integer decided in fp64 on both sides (the kernel's fp64
+MFMA distances, the oracle's fp64 differences), so it must match exactly
+except at near-ties, whose gap is below the fp64 rounding of the distances;
+those rows are counted and excluded. Centres are fp64 means rounded to
+float, checked to a few float ulps. Cases: each workload recipe at reduced N
+(fp16 X for the IVF recipe, K up to 4096), lists longer than one 1024-row
+segment, an empty cluster, and a device loop against the oracle loop.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from soft_clustering_gmm_amd import datagen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def G():
+    from soft_clustering_gmm_amd import gmm
+    gmm.lib()
+    return gmm
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def _near_ties(X, C):
+    X64, C64 = X.astype(np.float64), C.astype(np.float64)
+    D = ((X64[:, None, :] - C64[None, :, :]) ** 2).sum(axis=2)
+    Ds = np.sort(D, axis=1)
+    scale = (X64 ** 2).sum(axis=1) + (C64 ** 2).sum(axis=1).max()
+    return (Ds[:, 1] - Ds[:, 0]) <= 1e-12 * scale if C.shape[0] > 1 else np.zeros(X.shape[0], bool)
+
+
+def _check_assign(G, X, C, what):
+    a, d2, inertia = G.kmeans_assign(dev(X), dev(C))
+    torch.cuda.synchronize()
+    ra, rd = oracle.kmeans_assign(X, C)
+    tie = _near_ties(X, C)
+    ok = (host(a) == ra) | tie
+    assert ok.all(), f"{what}: {(~ok).sum()} rows assigned differently"
+    scale = np.maximum(rd, 1e-6 * (X.astype(np.float64) ** 2).sum(axis=1).max())
+    assert np.all(np.abs(host(d2) - rd) <= 1e-6 * scale), what
+    assert abs(float(host(inertia)) - rd.sum()) <= 1e-9 * abs(rd.sum()) + 1e-9, what
+    print(f"{what}: {int(tie.sum())} near-tie rows", flush=True)
+    return ra
+
+
+@pytest.mark.parametrize("name,N", [("tiny", None), ("ref", 3001), ("smallk", 5003), ("ivf", 2000), ("largek", 700)])
+def test_kmeans_assign_workloads(G, name, N):
+    X, mu, _, _ = datagen.make_workload(name, N=N)
+    _check_assign(G, X, mu, f"{name} N={X.shape[0]} K={mu.shape[0]}")
+
+
+def _check_update(G, X, assign, C, what):
+    Cg = dev(C.copy())
+    counts = G.kmeans_update(dev(X), dev(assign.astype(np.int32)), Cg)
+    torch.cuda.synchronize()
+    rC, rn = oracle.kmeans_update(X, assign, C)
+    assert np.array_equal(host(counts), rn), what
+    err = np.abs(host(Cg).astype(np.float64) - rC) / np.maximum(np.abs(rC), 1e-3)
+    assert err.max() <= 3e-7, f"{what}: centre rel err {err.max():.2e}"
+
+
+@pytest.mark.parametrize("name,N", [("tiny", None), ("ref", 3001), ("ivf", 2000), ("largek", 700)])
+def test_kmeans_update_workloads(G, name, N):
+    X, mu, _, _ = datagen.make_workload(name, N=N)
+    a, _ = oracle.kmeans_assign(X, mu)
+    _check_update(G, X, a, mu, f"{name} update")
+
+
+def test_kmeans_update_long_lists_and_empty_cluster(G):
+    """One cluster takes 5000 points (five 1024-row segments), one none."""
+    rng = np.random.default_rng(9)
+    X = rng.normal(size=(6000, 37)).astype(np.float32)
+    assign = np.where(np.arange(6000) < 5000, 2, rng.integers(0, 2, 6000)).astype(np.int64)
+    C = rng.normal(size=(4, 37)).astype(np.float32)
+    _check_update(G, X, assign, C, "long lists")
+
+
+def test_kmeans_device_loop_matches_oracle_loop(G):
+    X, mu, _, _ = datagen.make_workload("tiny")
+    C0 = mu.astype(np.float32)
+    Cg = dev(C0.copy())
+    hist = G.kmeans_iterate(dev(X), Cg, 6)
+    torch.cuda.synchronize()
+    rC, rh = oracle.kmeans(X, C0.astype(np.float64), 6)
+    h = host(hist)
+    assert np.all(np.diff(h) <= 1e-6 * h[:-1]), h
+    np.testing.assert_allclose(h, rh, rtol=1e-6)
+    np.testing.assert_allclose(host(Cg), rC, rtol=1e-5, atol=1e-5)
