@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "E-step+stats points×components/s (N=1M,d=128,K=256); % of MFMA/HBM peak"
 UNIT = "points×components/s"
 PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_FP64_MFMA_TFLOPS = 78.6
 PEAK_HBM_GBPS = 8000.0
 VAR_FLOOR = 1e-6
 KERNEL_SRC = os.path.join(ROOT, "soft_clustering_gmm_amd", "csrc", "gmm_kernels.hip")
@@ -152,6 +153,61 @@ def border_lists_bench(args, w, torch, gmm, dev):
     return 0
 
 
+def kmeans_bench(args, w, torch, gmm, dev):
+    """One step = one Lloyd iteration (fp64 nearest-centre assignment, then the
+    list-based centre update) from the workload's initial means, X in HBM.
+    Roofline: the assignment's 4NKd flops on the FP64 MFMA peak, timed with
+    events around the assignment call."""
+    from soft_clustering_gmm_amd import datagen
+    X, mu, _, _ = datagen.make_workload(args.workload)
+    N, d, K = X.shape[0], X.shape[1], mu.shape[0]
+    Xd = torch.from_numpy(X).to(dev)
+    C0 = torch.from_numpy(mu.copy()).to(dev)
+    C = C0.clone()
+    ws = gmm.kmeans_workspace(N, d, K, dev)
+    assign = torch.empty(N, dtype=torch.int32, device=dev)
+    lib = gmm.lib()
+    stream = gmm._stream(dev)
+
+    def step(ev=None):
+        C.copy_(C0)
+        if ev:
+            ev[0].record()
+        gmm._check("gmm_kmeans_assign", lib.gmm_kmeans_assign(
+            gmm._ptr(Xd), gmm._xtype(Xd), N, d, gmm._ptr(C), K, gmm._ptr(assign), None, None, gmm._ptr(ws),
+            ws.numel(), stream))
+        if ev:
+            ev[1].record()
+        gmm.kmeans_update(Xd, assign, C, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    a_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    flops = 4.0 * N * K * d
+    ach = flops / (a_ms * 1e-3) / 1e12
+    out = {
+        "metric": "k-means Lloyd iteration, points x centres/s", "value": N * K / (ms * 1e-3),
+        "unit": "points×centres/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"{w.name} recipe: N={N} d={d} K={K} {w.x_dtype}; centres = the K initial means; "
+                               f"step = assignment + update", "N": N, "d": d, "K": K},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP64_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_FP64_MFMA_TFLOPS, 4), "traffic": None,
+                     "kernel": "estep_lse_kernel (nearest-centre mode)", "flops_per_launch": flops,
+                     "avg_assign_ms": round(a_ms, 4)},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +223,8 @@ def main(argv=None):
                     help="time the border-vector inverted-list build on the workload's N and K from a "
                          "synthetic top-2 assignment resident in HBM")
     ap.add_argument("--border-threshold", type=float, default=0.05)
+    ap.add_argument("--kmeans", action="store_true",
+                    help="time Lloyd iterations of k-means on the workload's X with its K initial means as centres")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this E-step build runs on a "
@@ -181,6 +239,8 @@ def main(argv=None):
     w = datagen.WORKLOADS[args.workload]
     if args.border_lists:
         return border_lists_bench(args, w, torch, gmm, dev)
+    if args.kmeans:
+        return kmeans_bench(args, w, torch, gmm, dev)
     X, mu, var, logw = datagen.make_workload(args.workload)
     if args.x_on_host:
         return host_streamed(args, w, X, mu, var, logw, torch, gmm, dev)
