@@ -16,7 +16,9 @@
  *   which must hold at least gmm_workspace_bytes(N, d, K) bytes and be
  *   256-byte aligned (any hipMalloc / torch allocation is).
  * - Layouts are row-major and dense: X is N x d (x_dtype GMM_F32 = float,
- *   GMM_F16 = IEEE half), mu and var are K x d float, logw is K float,
+ *   GMM_F16 = IEEE half, GMM_BF16 = bfloat16; half and bfloat16 values are
+ *   widened exactly and all arithmetic is as for float X), mu and var are
+ *   K x d float, logw is K float,
  *   Sx and Sxx are K x d float, Nk is K float.
  * - The mixture is diagonal: component k has mean mu[k], variance var[k]
  *   (per feature, > 0) and log mixing weight logw[k] (-inf allowed; at least
@@ -50,7 +52,7 @@ enum gmm_status {
   GMM_EHIP = -4           /* a HIP launch failed (see hipGetLastError) */
 };
 
-enum gmm_dtype { GMM_F32 = 0, GMM_F16 = 1 };
+enum gmm_dtype { GMM_F32 = 0, GMM_F16 = 1, GMM_BF16 = 2 };
 
 /* Regime of the E-step (Turbo-GMM abstract: a single sweep over the component
  * axis kept on chip when it fits, a two-pass fallback otherwise).

@@ -132,7 +132,7 @@ static int check_ws(void* ws, size_t ws_bytes, int64_t N, int d, int K) {
 
 static int check_common(const void* X, int32_t xt, int64_t N, int32_t d, int32_t K, const float* mu,
                         const float* var, const float* logw) {
-  if (xt != GMM_F32 && xt != GMM_F16) return GMM_EINVAL;
+  if (xt != GMM_F32 && xt != GMM_F16 && xt != GMM_BF16) return GMM_EINVAL;
   if (N < 0 || d < 1 || K < 1) return GMM_EINVAL;
   if (d > kMaxD || K > kMaxK || N >= ((int64_t)1 << 40)) return GMM_EUNSUPPORTED;
   if ((N > 0 && !X) || !mu || !var || !logw) return GMM_EINVAL;
@@ -152,7 +152,7 @@ struct ChunkLayout {
 
 static int chunk_layout(int64_t N, int d, int K, int64_t chunk_rows, int x_dtype, ChunkLayout* L) {
   if (N < 0 || d < 1 || K < 1 || chunk_rows < 1) return GMM_EINVAL;
-  if (x_dtype != GMM_F32 && x_dtype != GMM_F16) return GMM_EINVAL;
+  if (x_dtype != GMM_F32 && x_dtype != GMM_F16 && x_dtype != GMM_BF16) return GMM_EINVAL;
   if (d > kMaxD || K > kMaxK || N >= ((int64_t)1 << 40)) return GMM_EUNSUPPORTED;
   const int64_t c = std::max<int64_t>(std::min(chunk_rows, N), 1);
   const int64_t tail = N % c;
@@ -160,7 +160,7 @@ static int chunk_layout(int64_t N, int d, int K, int64_t chunk_rows, int x_dtype
   if (tail) pb = std::max(pb, workspace_bytes(tail, d, K));
   L->chunk = c;
   L->plan_bytes = align_up(pb, 256);
-  L->stage_bytes = align_up((size_t)c * d * (x_dtype == GMM_F16 ? 2 : 4), 256);
+  L->stage_bytes = align_up((size_t)c * d * (x_dtype == GMM_F32 ? 4 : 2), 256);
   L->stage_off[0] = L->plan_bytes;
   L->stage_off[1] = L->plan_bytes + L->stage_bytes;
   L->acc_off = L->plan_bytes + 2 * L->stage_bytes;
@@ -309,7 +309,7 @@ int gmm_estep_stats_chunked(const void* X_host, int32_t x_dtype, int64_t N, int3
   char* base = static_cast<char*>(workspace);
   void* stage[2] = {base + L.stage_off[0], base + L.stage_off[1]};
   double* acc = reinterpret_cast<double*>(base + L.acc_off);
-  const size_t row_bytes = (size_t)d * (x_dtype == GMM_F16 ? 2 : 4);
+  const size_t row_bytes = (size_t)d * (x_dtype == GMM_F32 ? 4 : 2);
   const char* xh = static_cast<const char*>(X_host);
 
   std::lock_guard<std::mutex> lock(g_chunk_mutex);
@@ -408,7 +408,7 @@ size_t gmm_kmeans_workspace_bytes(int64_t N, int32_t d, int32_t K) {
 
 static int kmeans_check(const void* X, int32_t xt, int64_t N, int32_t d, int32_t K, const float* C, void* ws,
                         size_t ws_bytes) {
-  if (xt != GMM_F32 && xt != GMM_F16) return GMM_EINVAL;
+  if (xt != GMM_F32 && xt != GMM_F16 && xt != GMM_BF16) return GMM_EINVAL;
   if (N < 0 || d < 1 || K < 1) return GMM_EINVAL;
   if (!kmeans_args_ok(N, d, K)) return GMM_EUNSUPPORTED;
   if ((N > 0 && !X) || !C) return GMM_EINVAL;

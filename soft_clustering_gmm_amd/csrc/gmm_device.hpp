@@ -20,4 +20,12 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Calls f with X cast to its element type: 0 float, 1 IEEE half, 2 bfloat16.
+template <typename F>
+hipError_t with_x_type(int x_dtype, const void* X, F&& f) {
+  if (x_dtype == 1) return f(reinterpret_cast<const _Float16*>(X));
+  if (x_dtype == 2) return f(reinterpret_cast<const __bf16*>(X));
+  return f(reinterpret_cast<const float*>(X));
+}
+
 }  // namespace gmm

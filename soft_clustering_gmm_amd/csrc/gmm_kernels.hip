@@ -1395,8 +1395,7 @@ hipError_t launch_estep(const Plan& p, const void* X, int x_dtype, const float* 
   hipError_t e = hipSuccess;
   if (ev0) e = hipEventRecord(ev0, stream);
   if (e != hipSuccess) return e;
-  e = x_dtype == 1 ? estep_typed(p, reinterpret_cast<const _Float16*>(X), mu, loglik_point, R, stream)
-                   : estep_typed(p, reinterpret_cast<const float*>(X), mu, loglik_point, R, stream);
+  e = with_x_type(x_dtype, X, [&](auto x) { return estep_typed(p, x, mu, loglik_point, R, stream); });
   if (e != hipSuccess) return e;
   if (ev1) e = hipEventRecord(ev1, stream);
   if (e != hipSuccess) return e;
@@ -1415,8 +1414,8 @@ hipError_t launch_estep(const Plan& p, const void* X, int x_dtype, const float* 
 
 hipError_t launch_estep_accum(const Plan& p, const void* X, int x_dtype, const float* mu, double* acc, int first,
                               float* loglik_point, hipStream_t stream) {
-  hipError_t e = x_dtype == 1 ? estep_typed(p, reinterpret_cast<const _Float16*>(X), mu, loglik_point, nullptr, stream)
-                              : estep_typed(p, reinterpret_cast<const float*>(X), mu, loglik_point, nullptr, stream);
+  hipError_t e =
+      with_x_type(x_dtype, X, [&](auto x) { return estep_typed(p, x, mu, loglik_point, nullptr, stream); });
   if (e != hipSuccess) return e;
   const Workspace& w = p.ws;
   const int64_t n = (int64_t)p.K * (1 + 2 * p.d);
@@ -1436,49 +1435,28 @@ hipError_t launch_finalize_stats(const double* acc, int K, int d, float* Nk, flo
 hipError_t launch_top2(const Plan& p, const void* X, int x_dtype, int32_t* idx, float* resp,
                        hipStream_t stream) {
   if (p.N == 0) return hipSuccess;
-  hipError_t e = hipSuccess;
-  if (x_dtype == 1) {
-    const _Float16* x = reinterpret_cast<const _Float16*>(X);
+  return with_x_type(x_dtype, X, [&](auto x) {
     switch (p.DT) {
-      case 1: e = run_lse<1, true>(p, x, nullptr, idx, resp, stream); break;
-      case 2: e = run_lse<2, true>(p, x, nullptr, idx, resp, stream); break;
-      case 3: e = run_lse<3, true>(p, x, nullptr, idx, resp, stream); break;
-      default: e = run_lse<4, true>(p, x, nullptr, idx, resp, stream); break;
+      case 1: return run_lse<1, true>(p, x, nullptr, idx, resp, stream);
+      case 2: return run_lse<2, true>(p, x, nullptr, idx, resp, stream);
+      case 3: return run_lse<3, true>(p, x, nullptr, idx, resp, stream);
+      default: return run_lse<4, true>(p, x, nullptr, idx, resp, stream);
     }
-  } else {
-    const float* x = reinterpret_cast<const float*>(X);
-    switch (p.DT) {
-      case 1: e = run_lse<1, true>(p, x, nullptr, idx, resp, stream); break;
-      case 2: e = run_lse<2, true>(p, x, nullptr, idx, resp, stream); break;
-      case 3: e = run_lse<3, true>(p, x, nullptr, idx, resp, stream); break;
-      default: e = run_lse<4, true>(p, x, nullptr, idx, resp, stream); break;
-    }
-  }
-  return e;
+  });
 }
 
 hipError_t launch_kmeans_assign(const Plan& p, const void* X, int x_dtype, int32_t* assign, float* dist2,
                                 double* inertia, hipStream_t stream) {
   if (p.N == 0) return hipSuccess;
   const double kconst = -(double)p.d * kLog2Pi;  // the score's -d/2 log(2 pi), doubled
-  hipError_t e = hipSuccess;
-  if (x_dtype == 1) {
-    const _Float16* x = reinterpret_cast<const _Float16*>(X);
+  hipError_t e = with_x_type(x_dtype, X, [&](auto x) {
     switch (p.DT) {
-      case 1: e = run_lse<1, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
-      case 2: e = run_lse<2, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
-      case 3: e = run_lse<3, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
-      default: e = run_lse<4, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
+      case 1: return run_lse<1, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst);
+      case 2: return run_lse<2, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst);
+      case 3: return run_lse<3, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst);
+      default: return run_lse<4, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst);
     }
-  } else {
-    const float* x = reinterpret_cast<const float*>(X);
-    switch (p.DT) {
-      case 1: e = run_lse<1, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
-      case 2: e = run_lse<2, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
-      case 3: e = run_lse<3, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
-      default: e = run_lse<4, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst); break;
-    }
-  }
+  });
   if (e == hipSuccess && inertia) {
     reduce_ll_kernel<false><<<1, 256, 0, stream>>>(p.ws.llpart, p.tiles, inertia, 0);
     e = hipGetLastError();

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gmm_device.hpp"
 #include "gmm_internal.hpp"
 
@@ -479,12 +481,12 @@ hipError_t launch_kmeans_update(const void* X, int x_dtype, int d, int K, const 
   kmeans_segcount_kernel<<<(unsigned)((K + 255) / 256), 256, 0, stream>>>(offsets, K, seg);
   hipError_t e = excl_scan(seg, K, segoff, scan_tmp, segoff + K, stream);
   if (e != hipSuccess) return e;
-  if (x_dtype == 1)
-    kmeans_segsum_kernel<_Float16><<<(unsigned)max_segments, 256, 0, stream>>>(
-        reinterpret_cast<const _Float16*>(X), d, offsets, members, segoff, K, part);
-  else
-    kmeans_segsum_kernel<float><<<(unsigned)max_segments, 256, 0, stream>>>(reinterpret_cast<const float*>(X), d,
-                                                                              offsets, members, segoff, K, part);
+  e = with_x_type(x_dtype, X, [&](auto x) {
+    using XT = std::remove_cv_t<std::remove_pointer_t<decltype(x)>>;
+    kmeans_segsum_kernel<XT><<<(unsigned)max_segments, 256, 0, stream>>>(x, d, offsets, members, segoff, K, part);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
   const int64_t n = (int64_t)K * d;
   kmeans_finalize_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(part, segoff, offsets, K, d, C, counts);
   return hipGetLastError();

@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgmm_mi355x.so")
 
-GMM_F32, GMM_F16 = 0, 1
+GMM_F32, GMM_F16, GMM_BF16 = 0, 1, 2
 REGIME_AUTO, REGIME_SINGLE, REGIME_TWOPASS, REGIME_SMALLK = 0, 1, 2, 3
 
 EXPORTS = (
@@ -111,7 +111,9 @@ def _xtype(X: torch.Tensor) -> int:
         return GMM_F32
     if X.dtype == torch.float16:
         return GMM_F16
-    raise ValueError(f"X must be float32 or float16, got {X.dtype}")
+    if X.dtype == torch.bfloat16:
+        return GMM_BF16
+    raise ValueError(f"X must be float32, float16 or bfloat16, got {X.dtype}")
 
 
 def _need(t: torch.Tensor, name: str, dtype, shape, device):

@@ -96,3 +96,18 @@ def test_chunked_repeated_calls_share_workspace(G):
     for o in outs[1:]:
         for a, b in zip(o[:4], outs[0][:4]):
             assert np.array_equal(host(a), host(b))
+
+
+def test_chunked_bfloat16_host_x(G):
+    X, mu, var, logw = datagen.make_workload("ref", N=1800)
+    Xb = torch.from_numpy(X).to(torch.bfloat16)
+    Xv = Xb.float().numpy()
+    mud, vard, lwd = dev(mu), dev(var), dev(logw)
+    Nk, Sx, Sxx, L, lp = G.estep_stats_chunked(Xb.pin_memory(), mud, vard, lwd, 500, want_point_loglik=True)
+    _, _, _, _, lp0 = G.estep_stats(Xb.to("cuda"), mud, vard, lwd, want_point_loglik=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(lp), host(lp0))
+    ref = oracle.estep(Xv, mu, var, logw, keep_R=True)
+    X64 = Xv.astype(np.float64)
+    parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, X64, ref["R"].T @ np.abs(X64), "chunked bf16")
+    parity.check_total(host(L), ref, "chunked bf16")

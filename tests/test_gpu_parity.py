@@ -238,3 +238,49 @@ def test_top2_single_component(G):
     torch.cuda.synchronize()
     assert (host(idx)[:, 0] == 0).all() and (host(idx)[:, 1] == -1).all()
     assert np.abs(host(resp)[:, 0] - 1).max() <= 1e-6 and (host(resp)[:, 1] == 0).all()
+
+
+def _bf16(X):
+    """X rounded to bfloat16 (nearest even) by torch; the oracle gets the same values, widened."""
+    Xb = torch.from_numpy(np.ascontiguousarray(X, dtype=np.float32)).to(torch.bfloat16)
+    return Xb, Xb.float().numpy()
+
+
+@pytest.mark.parametrize("name,N", [("tiny", None), ("ref", 2001), ("smallk", 3001), ("largek", 500)])
+def test_estep_bfloat16_x(G, name, N):
+    X, mu, var, logw = _case(name, N=N)
+    Xb, Xv = _bf16(X)
+    K, d = mu.shape
+    for regime in _regimes(K, d):
+        rname = {1: "single", 2: "twopass", 3: "smallk"}[regime]
+        Xd, mud, vard, lwd = Xb.to("cuda"), dev(mu), dev(var), dev(logw)
+        Nk, Sx, Sxx, L, lp = G.estep_stats(Xd, mud, vard, lwd, regime=regime, want_point_loglik=True)
+        R, _ = G.estep_resp(Xd, mud, vard, lwd, regime=regime)
+        torch.cuda.synchronize()
+        ref = oracle.estep(Xv, mu, var, logw, keep_R=True)
+        X64 = Xv.astype(np.float64)
+        what = f"{name} bf16 {rname}"
+        parity.check_loglik_point(host(lp), ref["l"], what)
+        parity.check_resp(host(R), ref["R"], what)
+        parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, X64, ref["R"].T @ np.abs(X64), what)
+        parity.check_total(host(L), ref, what)
+
+
+def test_top2_and_kmeans_bfloat16_x(G):
+    X, mu, var, logw = _case("ivf", N=1500)
+    Xb, Xv = _bf16(X.astype(np.float32))
+    idx, resp = G.assign_top2(Xb.to("cuda"), dev(mu), dev(var), dev(logw))
+    a, _, _ = G.kmeans_assign(Xb.to("cuda"), dev(mu))
+    torch.cuda.synchronize()
+    ridx, rr = oracle.top2(Xv, mu, var, logw)
+    S = oracle.component_scores(Xv, mu, var, logw)
+    top = -np.sort(-S, axis=1)
+    tol = 1e-9 * np.maximum(np.abs(top[:, 0]), 1.0)
+    tie = ((top[:, 0] - top[:, 1]) <= tol) | ((top[:, 1] - top[:, 2]) <= tol)
+    assert ((host(idx) == ridx).all(axis=1) | tie).all()
+    assert np.abs(host(resp) - rr)[~tie].max() <= parity.R_TOL
+    ra, _ = oracle.kmeans_assign(Xv, mu)
+    D = ((Xv.astype(np.float64)[:, None, :] - mu.astype(np.float64)[None]) ** 2).sum(axis=2)
+    Ds = np.sort(D, axis=1)
+    ktie = (Ds[:, 1] - Ds[:, 0]) <= 1e-12 * (1.0 + Ds[:, 0])
+    assert ((host(a) == ra) | ktie).all()
