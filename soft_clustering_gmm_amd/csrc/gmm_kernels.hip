@@ -990,8 +990,11 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
 // First pass of the two-pass regime (also the top-2 kernel): fp64 MFMA scores
 // ---------------------------------------------------------------------------
 //
-// Block = 4 waves, one 64-point tile; wave w takes the 16-component tiles
-// w, w+4, ... . Scores come from 16x16x4 f64 MFMAs (layout: D[comp][point]),
+// Block = 4 waves, one 64-point tile. With NP = 4, wave w takes the
+// 16-component tiles w, w+4, ... for all four 16-point groups; with fewer
+// component tiles (NP = 2 or 1) the component tiles are dealt to NP wave
+// classes and each wave takes NP of the point groups, so that no wave idles.
+// Scores come from 16x16x4 f64 MFMAs (layout: D[comp][point]),
 // so each lane holds four components of one point per accumulator and keeps
 // an online (max, sum of exp) per point; lanes and waves are merged at the
 // end in a fixed order. Output per row: (m_ref, lZ) with m_ref = fp32 of the
@@ -1017,7 +1020,7 @@ __device__ __forceinline__ void top2_insert(double v, int i, double& v1, int& i1
   }
 }
 
-template <int DT, bool TOP2, typename XT>
+template <int DT, bool TOP2, typename XT, int NP>
 __global__ void __launch_bounds__(256)
 estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
                  const double* __restrict__ W64p, const double* __restrict__ c64e,
@@ -1039,28 +1042,31 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
   }
   __syncthreads();
 
-  double m[4], z[4], v1[4], v2[4];
-  int i1[4], i2[4];
+  // this wave's point groups: pg + i * (4 / NP), i < NP
+  constexpr int PS = 4 / NP;
+  const int pg = wave / NP;
+  double m[NP], z[NP], v1[NP], v2[NP];
+  int i1[NP], i2[NP];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
+  for (int p = 0; p < NP; ++p) {
     m[p] = -INFINITY;
     z[p] = 0.0;
     v1[p] = v2[p] = -INFINITY;
     i1[p] = i2[p] = 0x7fffffff;
   }
   const int Kt = Kp16 / 16;
-  for (int kt = wave; kt < Kt; kt += kLseWaves) {
-    v4d D[4];
+  for (int kt = wave % NP; kt < Kt; kt += NP) {
+    v4d D[NP];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) D[p] = (v4d){0.0, 0.0, 0.0, 0.0};
+    for (int p = 0; p < NP; ++p) D[p] = (v4d){0.0, 0.0, 0.0, 0.0};
     const double* Wk = W64p + (size_t)kt * S * 64 + lane;
 #pragma unroll 4
     for (int s = 0; s < S; ++s) {
       const double a = Wk[(size_t)s * 64];
       const int f = 2 * s + (g >> 1);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const double x = (double)xs[(p * 16 + c) * XS + f];
+      for (int p = 0; p < NP; ++p) {
+        const double x = (double)xs[((pg + p * PS) * 16 + c) * XS + f];
         const double b = (g & 1) ? x : x * x;
         D[p] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, D[p], 0, 0, 0);
       }
@@ -1073,7 +1079,7 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
       ce[j] = c64e[comp[j]];
     }
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < NP; ++p) {
       double s[4];
       double mx = -INFINITY;
 #pragma unroll
@@ -1098,7 +1104,7 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
 #pragma unroll
   for (int o = 16; o <= 32; o <<= 1) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < NP; ++p) {
       const double mo = __shfl_xor(m[p], o, 64), zo = __shfl_xor(z[p], o, 64);
       lse_merge(m[p], z[p], mo, zo);
       if (TOP2) {
@@ -1110,15 +1116,26 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
     }
   }
   if (g == 0) {
+    if (NP < 4)  // neutral values for the point groups this wave did not score
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      sm[wave][p * 16 + c] = m[p];
-      sz[wave][p * 16 + c] = z[p];
+      for (int q = 0; q < 4; ++q) {
+        sm[wave][q * 16 + c] = -INFINITY;
+        sz[wave][q * 16 + c] = 0.0;
+        if (TOP2) {
+          sv1[wave][q * 16 + c] = sv2[wave][q * 16 + c] = -INFINITY;
+          si1[wave][q * 16 + c] = si2[wave][q * 16 + c] = 0x7fffffff;
+        }
+      }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int q = pg + p * PS;
+      sm[wave][q * 16 + c] = m[p];
+      sz[wave][q * 16 + c] = z[p];
       if (TOP2) {
-        sv1[wave][p * 16 + c] = v1[p];
-        sv2[wave][p * 16 + c] = v2[p];
-        si1[wave][p * 16 + c] = i1[p];
-        si2[wave][p * 16 + c] = i2[p];
+        sv1[wave][q * 16 + c] = v1[p];
+        sv2[wave][q * 16 + c] = v2[p];
+        si1[wave][q * 16 + c] = i1[p];
+        si2[wave][q * 16 + c] = i2[p];
       }
     }
   }
@@ -1326,8 +1343,16 @@ static hipError_t run_lse(const Plan& p, const XT* X, float* ll_point, int32_t* 
                           hipStream_t stream, int32_t* kassign = nullptr, float* kdist2 = nullptr,
                           double kconst = 0.0) {
   const Workspace& w = p.ws;
-  estep_lse_kernel<DT, TOP2, XT><<<(unsigned)p.tiles, 256, 0, stream>>>(
-      X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp, kassign, kdist2, kconst);
+  const int Kt = p.Kp16 / 16;
+  if (Kt >= kLseWaves)
+    estep_lse_kernel<DT, TOP2, XT, 4><<<(unsigned)p.tiles, 256, 0, stream>>>(
+        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp, kassign, kdist2, kconst);
+  else if (Kt >= 2)
+    estep_lse_kernel<DT, TOP2, XT, 2><<<(unsigned)p.tiles, 256, 0, stream>>>(
+        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp, kassign, kdist2, kconst);
+  else
+    estep_lse_kernel<DT, TOP2, XT, 1><<<(unsigned)p.tiles, 256, 0, stream>>>(
+        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp, kassign, kdist2, kconst);
   return hipGetLastError();
 }
 
