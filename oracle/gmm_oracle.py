@@ -276,20 +276,27 @@ def border_lists(idx, resp, K, threshold):
 # Lloyd's k-means (hard-assignment workload)
 # ---------------------------------------------------------------------------
 
-def kmeans_assign(X, C, *, row_chunk=_ROW_CHUNK):
+def kmeans_assign(X, C, *, form="difference", row_chunk=_ROW_CHUNK):
     """Nearest-centre assignment (Flash-KMeans articles: the assignment step of
     Lloyd's algorithm, an argmin over point-centre distances).
 
     Returns (assign, dist2): assign[n] = argmin_k ||x_n - c_k||^2 with ties to
     the lower index, dist2[n] the minimum squared distance; float64 throughout.
+    form="expanded" evaluates ||x||^2 - 2 x.c + ||c||^2 with a float64 matrix
+    product (the same quantity, fast enough for full-size workloads).
     """
     X, C = _f64(X), _f64(C)
     N, K = X.shape[0], C.shape[0]
     assign = np.empty(N, dtype=np.int64)
     dist2 = np.empty(N)
+    cc = (C * C).sum(axis=1)
     for lo in range(0, N, row_chunk):
         hi = min(N, lo + row_chunk)
-        D = ((X[lo:hi, None, :] - C[None, :, :]) ** 2).sum(axis=2)
+        if form == "expanded":
+            x = X[lo:hi]
+            D = (x * x).sum(axis=1)[:, None] - 2.0 * (x @ C.T) + cc[None, :]
+        else:
+            D = ((X[lo:hi, None, :] - C[None, :, :]) ** 2).sum(axis=2)
         a = np.argmin(D, axis=1)  # first minimum: ties go to the lower index
         assign[lo:hi] = a
         dist2[lo:hi] = D[np.arange(hi - lo), a]

@@ -87,6 +87,13 @@ def test_full_size_workload(G, name):
         es = parity.check_stats((host(full[0]), host(full[1]), host(full[2])), ref, None, absx, name)
         parity.check_total(host(full[3]), ref, name)
         print(f"{name}: full stats vs oracle {es}, sampled |dr| {er:.2e}", flush=True)
+        # the row-chunked path over the same X in pinned host memory, in the benchmark's chunking
+        c = G.estep_stats_chunked(torch.from_numpy(X).pin_memory(), dev(mu), dev(var), dev(logw), 1 << 18,
+                                  want_point_loglik=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(c[4]), host(full[4])), f"{name}: chunked l_n differs"
+        parity.check_stats((host(c[0]), host(c[1]), host(c[2])), ref, None, absx, name + " chunked")
+        parity.check_total(host(c[3]), ref, name + " chunked")
     else:
         print(f"{name}: sampled |dr| {er:.2e} (stats checked by properties)", flush=True)
 
@@ -128,3 +135,28 @@ def test_ivf_em_then_top2(G):
     # the E-step at the final parameters, sampled
     full = _full(G, X, m, v, w)
     _sampled_rows(G, "ivf after 5 EM", X, m, v, w, full[4])
+
+
+def test_kmeans_full_size_ref(G):
+    """One Lloyd iteration on the ref recipe at full size: the assignment
+    against the oracle's (expanded form, ties excluded), and the update
+    from the oracle's assignment against the oracle's update."""
+    X, mu, _, _ = datagen.make_workload("ref")
+    N, K = X.shape[0], mu.shape[0]
+    a, d2, inertia = G.kmeans_assign(dev(X), dev(mu))
+    torch.cuda.synchronize()
+    ra, rd = oracle.kmeans_assign(X, mu, form="expanded", row_chunk=1 << 16)
+    diff = np.nonzero(host(a) != ra)[0]
+    if diff.size:  # only near-ties may differ: re-check those rows in the difference form
+        D = ((X[diff].astype(np.float64)[:, None, :] - mu.astype(np.float64)[None]) ** 2).sum(axis=2)
+        gap = np.abs(D[np.arange(diff.size), host(a)[diff]] - D[np.arange(diff.size), ra[diff]])
+        assert (gap <= 1e-9 * D.min(axis=1)).all(), f"{diff.size} rows differ beyond near-ties"
+    assert abs(float(host(inertia)) - rd.sum()) <= 1e-8 * rd.sum()
+    C = dev(mu.copy())
+    counts = G.kmeans_update(dev(X), dev(ra.astype(np.int32)), C)
+    torch.cuda.synchronize()
+    rC, rn = oracle.kmeans_update(X, ra, mu)
+    assert np.array_equal(host(counts), rn) and rn.sum() == N
+    err = np.abs(host(C).astype(np.float64) - rC) / np.maximum(np.abs(rC), 1e-3)
+    assert err.max() <= 3e-7, err.max()
+    print(f"kmeans full size: {diff.size} near-tie rows, {int((rn == 0).sum())} empty clusters", flush=True)

@@ -344,3 +344,14 @@ def test_kmeans_inertia_non_increasing():
     X, mu, _, _ = datagen.make_workload("tiny")
     _, hist = oracle.kmeans(X, mu.astype(np.float64), 8)
     assert (np.diff(hist) <= 1e-9 * hist[:-1]).all(), hist
+
+
+def test_kmeans_expanded_form_matches_difference_form():
+    X, mu, _, _ = datagen.make_workload("ref", N=3000)
+    a1, d1 = oracle.kmeans_assign(X, mu)
+    a2, d2 = oracle.kmeans_assign(X, mu, form="expanded", row_chunk=1000)
+    D = ((X.astype(np.float64)[:, None, :] - mu.astype(np.float64)[None]) ** 2).sum(axis=2)
+    Ds = np.sort(D, axis=1)
+    tie = (Ds[:, 1] - Ds[:, 0]) <= 1e-9 * Ds[:, 1]
+    assert ((a1 == a2) | tie).all()
+    np.testing.assert_allclose(d2, d1, rtol=1e-9, atol=1e-9)
