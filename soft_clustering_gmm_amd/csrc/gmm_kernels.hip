@@ -198,7 +198,7 @@ __global__ void comp_consts_kernel(const float* __restrict__ mu, const float* __
     const double ce = cd - 0.5 * sm2;
     c64d[k] = cd;
     c64e[k] = ce;
-    c32[k] = (float)ce;
+    c32[k] = (float)(ce * kLog2E);  // base 2: the fp32 pass evaluates 2^(s / ln 2)
     compmax[4 * k + 0] = (float)amax;
     compmax[4 * k + 1] = (float)bmax;
     compmax[4 * k + 2] = isfinite(ce) ? (float)fabs(ce) : 0.0f;
@@ -227,8 +227,8 @@ __global__ void pack_kernel(const float* __restrict__ mu, const float* __restric
   {
     const int kt = k >> 5, c = k & 31, q = f >> 2, u = f & 3, Q = DP >> 2;
     const size_t base = (((size_t)kt * Q + q) * 64 + c) * 4 + u;
-    W32p[base] = (float)A;
-    W32p[base + 32 * 4] = (float)B;
+    W32p[base] = (float)(A * kLog2E);  // base-2 scaled, like c32
+    W32p[base + 32 * 4] = (float)(B * kLog2E);
   }
   if (k < Kp16) {
     const int kt = k >> 4, c = k & 15, s = f >> 1, S = DP >> 1, g0 = 2 * (f & 1);
@@ -372,8 +372,12 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     }
     __syncthreads();
 
-    // 3. row phase. The score tile is rewritten in place: first to
-    //    e = exp(s - m) (MODE 0) or directly to r (MODE 1), then to r.
+    // 3. row phase. The score tile holds s / ln 2 (operands and constants are
+    //    base-2 scaled, so one hardware exp2 per entry); it is rewritten in
+    //    place: first to e = exp(s - m) (MODE 0) or directly to r (MODE 1),
+    //    then to r. m, lZ and the LDS row references are in base 2 as well;
+    //    the error bound E stays in natural units (scaling by log2(e) and
+    //    back cancels in the bound).
     {
       const int row = prow;
       const int64_t grow = r0 + row;
@@ -407,10 +411,10 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
 #pragma unroll 2
         for (int i = 0; i < 8; ++i) {
           float4 v = srow4[psub + tpr * i];
-          v.x = expf(v.x - m);
-          v.y = expf(v.y - m);
-          v.z = expf(v.z - m);
-          v.w = expf(v.w - m);
+          v.x = __builtin_amdgcn_exp2f(v.x - m);
+          v.y = __builtin_amdgcn_exp2f(v.y - m);
+          v.z = __builtin_amdgcn_exp2f(v.z - m);
+          v.w = __builtin_amdgcn_exp2f(v.w - m);
           srow4[psub + tpr * i] = v;
           z += ((double)v.x + (double)v.y) + ((double)v.z + (double)v.w);
         }
@@ -421,10 +425,10 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
 #pragma unroll 2
         for (int i = 0; i < 8; ++i) {
           float4 v = srow4[psub + tpr * i];
-          v.x = expf((v.x - m) - lZ);
-          v.y = expf((v.y - m) - lZ);
-          v.z = expf((v.z - m) - lZ);
-          v.w = expf((v.w - m) - lZ);
+          v.x = __builtin_amdgcn_exp2f((v.x - m) - lZ);
+          v.y = __builtin_amdgcn_exp2f((v.y - m) - lZ);
+          v.z = __builtin_amdgcn_exp2f((v.z - m) - lZ);
+          v.w = __builtin_amdgcn_exp2f((v.w - m) - lZ);
           srow4[psub + tpr * i] = v;
         }
       }
@@ -472,7 +476,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         }
       } else {
         const float thr = kGateTau / Ebound;
-        if (valid && expf(-lZ) > thr)
+        if (valid && __builtin_amdgcn_exp2f(-lZ) > thr)
 #pragma unroll 4
           for (int i = 0; i < 8; ++i) {
             const float4 v = srow4[psub + tpr * i];
@@ -526,8 +530,9 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
             }
             acc = row16_sum_d(acc);  // the 16 lanes of an entry form one DPP row
             if (act && sl == 0) {
-              const double dl = (c64d[kg] - 0.5 * acc) - (double)rv[2 * er];  // exact s - m
-              sc[er * SCS + ek] = MODE == 0 ? expf((float)dl) : expf((float)(dl - (double)rv[2 * er + 1]));
+              // exact (s - m) / ln 2
+              const double dl = (c64d[kg] - 0.5 * acc) * kLog2E - (double)rv[2 * er];
+              sc[er * SCS + ek] = __builtin_amdgcn_exp2f(MODE == 0 ? (float)dl : (float)(dl - (double)rv[2 * er + 1]));
             }
           }
           wave_lds_sync();
@@ -544,12 +549,12 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           }
         z2 = group_sum_d(z2, tpr);
         if (redo) z = z2;
-        // z is in [1, K]: an fp32 log is exact to ~1e-7 absolute, far inside the
-        // 1e-4 relative bar of l_n; r itself uses 1/z.
-        const double lZd = (double)logf((float)z);
+        // z is in [1, K]: the fp32 hardware log2 is good to ~1e-7 absolute, far
+        // inside the 1e-4 relative bar of l_n; r itself uses 1/z.
+        const double lZd = (double)__builtin_amdgcn_logf((float)z);  // log2
         const float invz = valid ? (float)(1.0 / z) : 0.f;
         if (valid && psub == 0) {
-          const double l = (double)m + lZd;
+          const double l = ((double)m + lZd) * kLn2;
           ll_acc += l;
           if (ll_point) ll_point[grow] = (float)l;
         }
@@ -1162,8 +1167,9 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
       kassign[gr] = b1;
       if (kdist2) kdist2[gr] = (float)d2;
     } else if (gr < N) {
-      const float mref = (float)mm;
-      if (rowref) rowref[gr] = make_float2(mref, (float)(l - (double)mref));
+      // (m, lZ) in base 2 for the fp32 second pass
+      const float mref = (float)(mm * kLog2E);
+      if (rowref) rowref[gr] = make_float2(mref, (float)(l * kLog2E - (double)mref));
       if (ll_point) ll_point[gr] = (float)l;
       if (TOP2) {
         tidx[2 * gr] = b1;
