@@ -88,6 +88,8 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
   const size_t o_c64e = take((size_t)p.Kp16 * sizeof(double));
   const size_t o_iv64 = take((size_t)K * d * sizeof(double));
   const size_t o_c64d = take((size_t)K * sizeof(double));
+  const size_t o_mup = take((size_t)p.Kp * p.DP * sizeof(float));
+  const size_t o_ivp = take((size_t)p.Kp * p.DP * sizeof(double));
   const size_t o_cmax = take((size_t)K * 4 * sizeof(float));
   const size_t o_errc = take(4 * sizeof(float));
   const size_t o_rowref = take((size_t)std::max<int64_t>(N, 1) * sizeof(float2));
@@ -103,6 +105,8 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
     p.ws.c64e = reinterpret_cast<double*>(b + o_c64e);
     p.ws.iv64 = reinterpret_cast<double*>(b + o_iv64);
     p.ws.c64d = reinterpret_cast<double*>(b + o_c64d);
+    p.ws.mup = reinterpret_cast<float*>(b + o_mup);
+    p.ws.ivp = reinterpret_cast<double*>(b + o_ivp);
     p.ws.compmax = reinterpret_cast<float*>(b + o_cmax);
     p.ws.errc = reinterpret_cast<float*>(b + o_errc);
     p.ws.rowref = reinterpret_cast<float2*>(b + o_rowref);

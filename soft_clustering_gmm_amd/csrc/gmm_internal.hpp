@@ -28,6 +28,8 @@ struct Workspace {
   double* c64e;     // [Kp16] expanded-form constant (fp64), -inf for padding
   double* iv64;     // [K][d] 1/var in fp64 (exact re-score)
   double* c64d;     // [K] difference-form constant (fp64)
+  float* mup;       // [Kp][DP] means, zero padded (exact re-score of the fp32 kernels)
+  double* ivp;      // [Kp][DP] 1/var in fp64, zero padded
   float* compmax;   // [K][4] per-component max|A|, max|B|, |c|, ||B||_2 (error bound inputs)
   float* errc;      // [4] a_max, b_max, c_max, b2_max
   float2* rowref;   // [N] per-row (m_ref, lZ) from the fp64 pass

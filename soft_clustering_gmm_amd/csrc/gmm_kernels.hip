@@ -34,6 +34,7 @@
 namespace gmm {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 constexpr double kLog2Pi = 1.83787706640934548356065947281;
@@ -46,6 +47,9 @@ constexpr float kGateTau = 5e-7f;  // re-score a row when 2 E_n * r_max could ex
 // 2^-23, which also covers an accumulator that truncates rather than rounds.
 constexpr float kUnitRound = 1.1920928955078125e-7f;
 constexpr int kRefCap = 128;       // re-score list entries per wave and pass
+// Word 3 of a raw buffer resource on CDNA (32-bit data format, no swizzle):
+// loads at offsets past the record count return zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // Row of the 32x32 MFMA accumulator held in slot j by lanes of half h:
 // D[row][col] with col = lane % 32 and row = 8*(j/4) + 4*h + j%4.
@@ -77,12 +81,6 @@ __device__ __forceinline__ double dpp_d(double v) {
 // the row with the sum over the row (the quad sums, then the half-row sums,
 // then the row sum), bitwise identical on all 16 lanes.
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-__device__ __forceinline__ double row16_sum_d(double v) {
-  v += dpp_d<kDppXor1>(v);
-  v += dpp_d<kDppXor2>(v);
-  v += dpp_d<kDppHalfMirror>(v);
-  return v + dpp_d<kDppMirror>(v);
-}
 
 // All-reduce over aligned groups of tpr consecutive lanes (tpr a power of two
 // <= 8) with the DPP steps above; every lane of a group ends with the same
@@ -211,19 +209,26 @@ __global__ void comp_consts_kernel(const float* __restrict__ mu, const float* __
 //        4q..4q+3 of component 32*kt + c; h = 0 -> A, h = 1 -> B.
 //  W64p: double index ((kt*S + s)*4 + g)*16 + c holds feature 2s + g/2 of
 //        component 16*kt + c; g even -> A, g odd -> B.
+//  mup, ivp: [Kp][DP] mean and 1/var, zero past d and K (aligned rows for the
+//        exact re-score of the fp32 kernels).
 __global__ void pack_kernel(const float* __restrict__ mu, const float* __restrict__ var, int K, int d,
                             int Kp, int Kp16, int DP, float* __restrict__ W32p,
-                            double* __restrict__ W64p, double* __restrict__ iv64) {
+                            double* __restrict__ W64p, double* __restrict__ iv64,
+                            float* __restrict__ mup, double* __restrict__ ivp) {
   const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (t >= (int64_t)Kp * DP) return;
   const int k = (int)(t / DP), f = (int)(t - (int64_t)k * DP);
-  double A = 0.0, B = 0.0;
+  double A = 0.0, B = 0.0, iv = 0.0;
+  float m = 0.f;
   if (k < K && f < d) {
-    const double iv = 1.0 / (double)var[(size_t)k * d + f];
+    iv = 1.0 / (double)var[(size_t)k * d + f];
+    m = mu[(size_t)k * d + f];
     A = -0.5 * iv;
-    B = (double)mu[(size_t)k * d + f] * iv;
+    B = (double)m * iv;
     iv64[(size_t)k * d + f] = iv;
   }
+  mup[t] = m;
+  ivp[t] = iv;
   {
     const int kt = k >> 5, c = k & 31, q = f >> 2, u = f & 3, Q = DP >> 2;
     const size_t base = (((size_t)kt * Q + q) * 64 + c) * 4 + u;
@@ -264,7 +269,8 @@ __global__ void errc_kernel(const float* __restrict__ compmax, int K, float* __r
 //   1. X tile -> LDS (zero padded to DP features and 64 rows)
 //   2. scores: two 32x32 fp32 MFMA accumulators per wave -> LDS score tile
 //   3. row phase (`waves` threads per row): max, log-sum-exp (MODE 0) or the
-//      first pass's (m, lZ) (MODE 1), gated exact re-score, r in place
+//      first pass's (m, lZ) (MODE 1), gated exact re-score; the tile then
+//      holds e = exp(s - m) and a per-row 1/z (MODE 0) or r itself (MODE 1)
 //   4. statistics: r (re-read in accumulator layout) is the A operand and
 //      [x | x^2] from the LDS tile the B operand of 32x32x2 MFMAs that
 //      accumulate Sx, Sxx for the wave's 32 components in registers.
@@ -274,7 +280,7 @@ template <int DT, int MODE, typename XT>
 __global__ void __launch_bounds__(512)
 estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, int waves, int kslabs,
                    int64_t rows_per_chunk, const float4* __restrict__ W32p, const float* __restrict__ c32,
-                   const float* __restrict__ mu, const double* __restrict__ iv64,
+                   const float* __restrict__ mup, const double* __restrict__ ivp,
                    const double* __restrict__ c64d, const float* __restrict__ errc,
                    const float2* __restrict__ rowref, float* __restrict__ partials,
                    double* __restrict__ llpart, float* __restrict__ ll_point, float* __restrict__ R,
@@ -291,7 +297,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   float* xsb = smem;             // [2][64][XS]: current and next X tile
   float* sc = xsb + 2 * 64 * XS; // [64][SCS]
   float* rv = sc + 64 * SCS;     // [64][2]
-  double* lls = reinterpret_cast<double*>(rv + 128);  // [nthr]
+  float* xq = rv + 128;          // [64][2] |x|^2 and |x|_1 of the tile's rows
+  double* lls = reinterpret_cast<double*>(xq + 128);  // [nthr]
   uint32_t* reflist = reinterpret_cast<uint32_t*>(lls + nthr);  // [waves][kRefCap]
 
   const int tpr = waves;  // threads per row in the row phase
@@ -316,7 +323,13 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
 
   const int64_t lo = chunk * rows_per_chunk;
   const int64_t hi = min(N, lo + rows_per_chunk);
-  const float4* Wt = W32p + (size_t)(kw >> 5) * Q * 64 + lane;
+  // The score operands are read through a buffer resource over this wave's
+  // slab: the loads are then opaque to the IR optimiser, which would otherwise
+  // fold the rotating prefetch registers below into one load per use.
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float4*>(W32p) + (size_t)(__builtin_amdgcn_readfirstlane(kw) >> 5) * Q * 64, (short)0,
+      Q * 64 * 16, kBufferRsrcWord3);
+  auto wload = [&](int q) { return __builtin_amdgcn_raw_buffer_load_b128(wrs, (q * 64 + lane) * 16, 0, 0); };
   const float ck = c32[kw + c];
 
   // The next tile's X streams straight into the other LDS buffer (16-byte
@@ -342,40 +355,76 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         acc0[j] = 0.f;
         acc1[j] = 0.f;
       }
-      // two-ahead register prefetch of the (L2-resident) score operands
-      float4 w = Wt[0];
-      float4 wn = Wt[(1 < Q ? 1 : 0) * 64];
-#pragma unroll 1
-      for (int q = 0; q < Q; ++q) {
-        const float4 wnn = Wt[(q + 2 < Q ? q + 2 : Q - 1) * 64];
-        const float4 x0 = *reinterpret_cast<const float4*>(xs + c * XS + 4 * q);
-        const float4 x1 = *reinterpret_cast<const float4*>(xs + (c + 32) * XS + 4 * q);
-        const float wv[4] = {w.x, w.y, w.z, w.w};
+      // Score operands (L2-resident) are prefetched two steps ahead in two
+      // register pairs that swap roles every two steps, so the loop needs no
+      // register rotation (which would wait for the loads in flight).
+      float sqab0 = 0.f, sqab1 = 0.f;  // error-bound inputs, summed alongside the MFMAs
+      auto xld = [&](int q, float4& x0, float4& x1) {
+        x0 = *reinterpret_cast<const float4*>(xs + c * XS + 4 * q);
+        x1 = *reinterpret_cast<const float4*>(xs + (c + 32) * XS + 4 * q);
+      };
+      auto step = [&](const float4& x0, const float4& x1, v4f w) {
         const float xv0[4] = {x0.x, x0.y, x0.z, x0.w};
         const float xv1[4] = {x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const float a0 = h ? xv0[u] : xv0[u] * xv0[u];
           const float a1 = h ? xv1[u] : xv1[u] * xv1[u];
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, wv[u], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, wv[u], acc1, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, w[u], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, w[u], acc1, 0, 0, 0);
+          sqab0 += fabsf(a0);  // h = 0: |x|^2, h = 1: |x|_1 of rows c and c + 32
+          sqab1 += fabsf(a1);
         }
-        w = wn;
-        wn = wnn;
+      };
+      // The X operands of the next step are read from LDS before this step's
+      // MFMAs issue; the scheduling barriers keep every load where it is.
+      static_assert(Q % 4 == 0, "the score loop takes four steps at a time");
+      v4f wa = wload(0), wb = wload(1);
+      float4 pa0, pa1, pb0, pb1;
+      xld(0, pa0, pa1);
+#pragma unroll 1
+      for (int q = 0; q < Q; q += 4) {
+        const v4f wc = wload(q + 2), wd = wload(q + 3);
+        xld(q + 1, pb0, pb1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(pa0, pa1, wa);
+        __builtin_amdgcn_sched_barrier(0);
+        xld(q + 2, pa0, pa1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(pb0, pb1, wb);
+        __builtin_amdgcn_sched_barrier(0);
+        wa = wload(q + 4 < Q ? q + 4 : 0);
+        wb = wload(q + 5 < Q ? q + 5 : 1);
+        xld(q + 3, pb0, pb1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(pa0, pa1, wc);
+        __builtin_amdgcn_sched_barrier(0);
+        xld(q + 4 < Q ? q + 4 : 0, pa0, pa1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(pb0, pb1, wd);
+      }
+      // The store base goes through an empty asm so that the 32 store
+      // addresses are formed here, per tile, instead of being hoisted out of
+      // the tile loop and held (or spilled) across it.
+      int scb = 4 * h * SCS + wave * 32 + c;
+      asm volatile("" : "+v"(scb));
+      if (wave == 0) {
+        xq[2 * c + h] = sqab0;
+        xq[2 * (c + 32) + h] = sqab1;
       }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int r = acc_row(h, j);
-        sc[r * SCS + wave * 32 + c] = acc0[j] + ck;
-        sc[(r + 32) * SCS + wave * 32 + c] = acc1[j] + ck;
+        const int r = ((j >> 2) << 3) + (j & 3);  // acc_row(h, j) - 4 h
+        sc[scb + r * SCS] = acc0[j] + ck;
+        sc[scb + (r + 32) * SCS] = acc1[j] + ck;
       }
     }
     __syncthreads();
 
     // 3. row phase. The score tile holds s / ln 2 (operands and constants are
     //    base-2 scaled, so one hardware exp2 per entry); it is rewritten in
-    //    place: first to e = exp(s - m) (MODE 0) or directly to r (MODE 1),
-    //    then to r. m, lZ and the LDS row references are in base 2 as well;
+    //    place to e = exp(s - m) with 1/z beside each row (MODE 0) or
+    //    directly to r (MODE 1). m, lZ and the LDS row references are in base 2;
     //    the error bound E stays in natural units (scaling by log2(e) and
     //    back cancels in the bound).
     {
@@ -383,16 +432,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       const int64_t grow = r0 + row;
       const bool valid = grow < hi;
       float* srow = sc + row * SCS;
-      const float* xrow = xs + row * XS;
-      float sq = 0.f, ab = 0.f;
-#pragma unroll 4
-      for (int f = psub; f < d; f += tpr) {
-        const float x = xrow[f];
-        sq += x * x;
-        ab += fabsf(x);
-      }
-      sq = group_sum(sq, tpr);
-      ab = group_sum(ab, tpr);
+      const float sq = xq[2 * row], ab = xq[2 * row + 1];  // from the score loop
       const float Ebound = gam * (a_max * sq + fminf(b_max * ab, b2_max * sqrtf(sq))) + 2.f * kUnitRound * c_max;
 
       // Each thread owns the 16-byte chunks psub + tpr*i (i < 8) of its row,
@@ -487,7 +527,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           }
       }
       // Exact re-score of the window entries. Each wave pools the entries of
-      // its rows into an LDS list and re-scores four at a time, sixteen lanes
+      // its rows into an LDS list and re-scores eight at a time, eight lanes
       // per entry splitting the features (fp64, difference form).
       if (MODE == 0 && psub == 0) rv[2 * row] = m;
       {
@@ -508,30 +548,44 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           }
           wave_lds_sync();
           const int n = min(total - p0, kRefCap);
-          for (int e0 = 0; e0 < n; e0 += 4) {
-            const int e = e0 + (lane >> 4), sl = lane & 15;
+          // eight lanes per entry, 4*DT contiguous features each; every load
+          // is issued before the arithmetic (inactive lanes read entry 0)
+          constexpr int FPL = DP / 8;
+          for (int e0 = 0; e0 < n; e0 += 8) {
+            const int e = e0 + (lane >> 3), sl = lane & 7;
             const bool act = e < n;
             const uint32_t ent = act ? wl[e] : 0u;
             const int er = (int)(ent >> 16), ek = (int)(ent & 0xffffu), kg = k0 + ek;
-            double acc = 0.0;
-            if (act) {
-              const float* xr = xs + er * XS;
-              const float* mk = mu + (size_t)kg * d;
-              const double* ivk = iv64 + (size_t)kg * d;
-              // unconditional (clamped) loads so that all of them are in flight at once
+            const float4* xr = reinterpret_cast<const float4*>(xs + er * XS + sl * FPL);
+            const float4* mr = reinterpret_cast<const float4*>(mup + (size_t)kg * DP + sl * FPL);
+            const double2* ir = reinterpret_cast<const double2*>(ivp + (size_t)kg * DP + sl * FPL);
+            float4 mv[FPL / 4];
+            double2 iv[FPL / 2];
 #pragma unroll
-              for (int i = 0; i < DP / 16; ++i) {
-                const int f = sl + 16 * i;
-                const int fc = f < d ? f : d - 1;
-                const double t = (double)xr[fc] - (double)mk[fc];
-                const double w = f < d ? ivk[fc] : 0.0;
-                acc += t * t * w;
-              }
+            for (int i = 0; i < FPL / 4; ++i) mv[i] = mr[i];
+#pragma unroll
+            for (int i = 0; i < FPL / 2; ++i) iv[i] = ir[i];
+            // the sum starts from -2 c_k (one lane), so that the constant's load
+            // is in flight with the others
+            double a0 = sl == 0 ? -2.0 * c64d[kg] : 0.0, a1 = 0.0;  // features past d carry 1/var = 0
+            __builtin_amdgcn_sched_barrier(0);  // all global loads in flight before the arithmetic
+#pragma unroll
+            for (int i = 0; i < FPL / 4; ++i) {
+              const float4 xv = xr[i];
+              const double t0 = (double)xv.x - (double)mv[i].x, t1 = (double)xv.y - (double)mv[i].y;
+              const double t2 = (double)xv.z - (double)mv[i].z, t3 = (double)xv.w - (double)mv[i].w;
+              a0 = fma(t0 * t0, iv[2 * i].x, a0);
+              a1 = fma(t1 * t1, iv[2 * i].y, a1);
+              a0 = fma(t2 * t2, iv[2 * i + 1].x, a0);
+              a1 = fma(t3 * t3, iv[2 * i + 1].y, a1);
             }
-            acc = row16_sum_d(acc);  // the 16 lanes of an entry form one DPP row
+            double acc = a0 + a1;
+            acc += dpp_d<kDppXor1>(acc);  // the eight lanes of an entry: half a DPP row
+            acc += dpp_d<kDppXor2>(acc);
+            acc += dpp_d<kDppHalfMirror>(acc);
             if (act && sl == 0) {
-              // exact (s - m) / ln 2
-              const double dl = (c64d[kg] - 0.5 * acc) * kLog2E - (double)rv[2 * er];
+              // exact (s - m) / ln 2: acc = sum_j (x_j - mu_j)^2 / var_j - 2 c_k
+              const double dl = (-0.5 * acc) * kLog2E - (double)rv[2 * er];
               sc[er * SCS + ek] = __builtin_amdgcn_exp2f(MODE == 0 ? (float)dl : (float)(dl - (double)rv[2 * er + 1]));
             }
           }
@@ -558,20 +612,19 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           ll_acc += l;
           if (ll_point) ll_point[grow] = (float)l;
         }
-#pragma unroll 4
-        for (int i = 0; i < 8; ++i) {
-          float4 v = srow4[psub + tpr * i];
-          v.x *= invz;
-          v.y *= invz;
-          v.z *= invz;
-          v.w *= invz;
-          srow4[psub + tpr * i] = v;
-        }
+        // the tile keeps e; the statistics loop applies r = e / z as it reads it
+        if (psub == 0) rv[2 * row + 1] = invz;
+        if (R && valid)
+#pragma unroll 1
+          for (int i = 0; i < 32; ++i) {
+            const int kl = 4 * (psub + tpr * (i >> 2)) + (i & 3);
+            if (k0 + kl < K) R[grow * K + k0 + kl] = srow[kl] * invz;
+          }
       } else if (!valid) {
 #pragma unroll 1
         for (int i = 0; i < 8; ++i) srow4[psub + tpr * i] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      if (R && valid)
+      if (MODE == 1 && R && valid)
 #pragma unroll 1
         for (int i = 0; i < 32; ++i) {
           const int kl = 4 * (psub + tpr * (i >> 2)) + (i & 3);
@@ -584,30 +637,44 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     const int64_t rn = r0 + 64;
     if (async_x && rn < hi) async_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, reinterpret_cast<const float*>(X),
                                              rn, hi, d, wave, waves, lane);
-#pragma unroll 1
-    for (int g = 0; g < 2; ++g) {
-#pragma unroll 2
-      for (int j = 0; j < 16; ++j) {
-        const int row = g * 32 + acc_row(h, j);
-        const float r = sc[row * SCS + wave * 32 + c];
-        nk += r;
+    {
+      // Step s takes point acc_row(h, s % 16) of row half s / 16. The operands
+      // of the next step are read from LDS before this step's MFMAs issue.
+      auto sload = [&](int s, float& r, float(&xv)[DT]) {
+        const int row = (s >> 4) * 32 + acc_row(h, s & 15);
+        r = sc[row * SCS + wave * 32 + c];
+        if (MODE == 0) r *= rv[2 * row + 1];  // e -> r = e / z (0 past the last row)
         const float* xr = xs + row * XS + DT * c;
-        float xv[DT];
 #pragma unroll
         for (int t = 0; t < DT; ++t) xv[t] = xr[t];
+      };
+      auto smfma = [&](float r, const float(&xv)[DT]) {
+        nk += r;
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
           SX[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(r, xv[t], SX[t], 0, 0, 0);
           SXX[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(r, xv[t] * xv[t], SXX[t], 0, 0, 0);
         }
+      };
+      float ra, rb, xa[DT], xb[DT];
+      sload(0, ra, xa);
+#pragma unroll 1
+      for (int s = 0; s < 32; s += 2) {
+        sload(s + 1, rb, xb);
+        __builtin_amdgcn_sched_barrier(0);
+        smfma(ra, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        sload(s + 2 < 32 ? s + 2 : 0, ra, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        smfma(rb, xb);
       }
     }
-    if (rn < hi) {
-      if (async_x)
-        __builtin_amdgcn_s_waitcnt(0);  // this thread's async tile loads have landed
-      else
-        load_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, X, rn, hi, d, DP, tid, nthr, vec);
-    }
+    if (rn < hi && !async_x) load_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, X, rn, hi, d, DP, tid, nthr, vec);
+    // This thread's async tile loads have landed. The wait is unconditional so
+    // that no global->LDS load counts as in flight at the top of the loop:
+    // the compiler would otherwise drain every global load before each LDS
+    // read of the score loop.
+    __builtin_amdgcn_s_waitcnt(0);
     cur ^= 1;
   }
 
@@ -655,7 +722,6 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
 //     r = e / z goes back to the score tile;
 //  4. statistics: 16x16x4 MFMAs with r (component c, point slot g) as the A
 //     operand and x or x^2 of those points as B.
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 // exp(x) for x <= ~0 through the hardware exp2 (1 ulp): the relative error is
 // ~|x| * 2^-24 * log2(e) from rounding x*log2(e), i.e. an absolute error in
@@ -1319,7 +1385,7 @@ hipError_t launch_precompute(const Plan& p, const float* mu, const float* var, c
   comp_consts_kernel<<<nblocks(p.Kp, 4), 256, 0, stream>>>(mu, var, logw, p.K, p.d, p.Kp, p.Kp16, w.c32,
                                                                w.c64e, w.c64d, w.compmax);
   pack_kernel<<<nblocks((int64_t)p.Kp * p.DP, 256), 256, 0, stream>>>(mu, var, p.K, p.d, p.Kp, p.Kp16, p.DP,
-                                                                        w.W32p, w.W64p, w.iv64);
+                                                                        w.W32p, w.W64p, w.iv64, w.mup, w.ivp);
   errc_kernel<<<1, 256, 0, stream>>>(w.compmax, p.K, w.errc);
   return hipGetLastError();
 }
@@ -1330,7 +1396,7 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
   const Workspace& w = p.ws;
   const int nthr = p.waves * 64;
   const int KS = p.waves * 32;
-  const size_t lds = (size_t)(2 * 64 * (32 * DT + 4) + 64 * (KS + 8) + 128) * sizeof(float) +
+  const size_t lds = (size_t)(2 * 64 * (32 * DT + 4) + 64 * (KS + 8) + 256) * sizeof(float) +
                      (size_t)nthr * sizeof(double) + (size_t)p.waves * kRefCap * sizeof(uint32_t);
   auto fn = estep_stats_kernel<DT, MODE, XT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
@@ -1339,7 +1405,7 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
   const unsigned grid = (unsigned)(p.P * p.kslabs);
   const int vec = (sizeof(XT) == 4 && p.d % 4 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0) ? 1 : 0;
   fn<<<grid, nthr, lds, stream>>>(X, p.N, p.d, p.K, p.Kp, p.waves, p.kslabs, p.rows_per_chunk,
-                                  reinterpret_cast<const float4*>(w.W32p), w.c32, mu, w.iv64, w.c64d, w.errc,
+                                  reinterpret_cast<const float4*>(w.W32p), w.c32, w.mup, w.ivp, w.c64d, w.errc,
                                   w.rowref, w.partials, w.llpart, ll_point, R, vec);
   return hipGetLastError();
 }
