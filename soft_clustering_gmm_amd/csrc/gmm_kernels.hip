@@ -456,7 +456,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           v.z = __builtin_amdgcn_exp2f(v.z - m);
           v.w = __builtin_amdgcn_exp2f(v.w - m);
           srow4[psub + tpr * i] = v;
-          z += ((double)v.x + (double)v.y) + ((double)v.z + (double)v.w);
+          // fp32 sums of four e <= 1, gathered in fp64: |dz| <= 2 u z
+          z += (double)((v.x + v.y) + (v.z + v.w));
         }
         z = group_sum_d(z, tpr);
       } else {
@@ -487,7 +488,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         const float thr2 = kGateTau * zf * zf / (2.f * Ebound);  // on e (z - e)
         const float maxq = zf >= 2.f ? zf - 1.f : 0.25f * zf * zf;
         const bool refine = valid && maxq > thr2;
-        double unref = 0.0;
+        float flagged = 0.f;
         if (refine)
 #pragma unroll 4
           for (int i = 0; i < 8; ++i) {
@@ -495,13 +496,14 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
             const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              if (vv[u] * (zf - vv[u]) > thr2)
-                mask |= 1u << (4 * i + u);
-              else
-                unref += (double)vv[u];
+              const bool fl = vv[u] * (zf - vv[u]) > thr2;
+              mask |= (fl ? 1u : 0u) << (4 * i + u);
+              flagged += fl ? vv[u] : 0.f;
             }
           }
-        unref = group_sum_d(unref, tpr);
+        // Upper bound on the unrefined mass z - (flagged mass): the fp32 sum of
+        // at most K flagged e <= 1 is off by <= (32 + 3) u z, z itself by 2 u z.
+        const double unref = fmax(0.0, z - (double)group_sum(flagged, tpr)) + 64.0 * (double)kUnitRound * z;
         const float anyflag = group_max(mask ? 1.f : 0.f, tpr);
         if (refine && anyflag > 0.f && (double)Ebound * unref / z > (double)kGateTau) {
           mask = 0;
@@ -599,7 +601,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
 #pragma unroll 4
           for (int i = 0; i < 8; ++i) {
             const float4 v = srow4[psub + tpr * i];
-            z2 += ((double)v.x + (double)v.y) + ((double)v.z + (double)v.w);
+            z2 += (double)((v.x + v.y) + (v.z + v.w));
           }
         z2 = group_sum_d(z2, tpr);
         if (redo) z = z2;
