@@ -1128,14 +1128,30 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
     i1[p] = i2[p] = 0x7fffffff;
   }
   const int Kt = Kp16 / 16;
-  for (int kt = wave % NP; kt < Kt; kt += NP) {
+  // Score operands through a buffer resource (opaque to the IR optimiser, so
+  // the prefetch below stays a prefetch), two steps ahead in two register
+  // pairs that swap roles; the last steps of a component tile prefetch the
+  // first steps of the wave's next tile (offsets past the end read zero).
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<double*>(W64p), (short)0, Kt * S * 64 * 8, kBufferRsrcWord3);
+  auto wl = [&](int kt, int s) {
+    return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(wrs, ((kt * S + s) * 64 + lane) * 8, 0, 0));
+  };
+  static_assert(S % 4 == 0, "the score loop takes four steps at a time");
+  int kt = wave % NP;
+  double wa = wl(kt, 0), wb = wl(kt, 1);
+  for (; kt < Kt; kt += NP) {
+    double ce[4];
+    int comp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      comp[j] = kt * 16 + 4 * j + g;
+      ce[j] = c64e[comp[j]];
+    }
     v4d D[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) D[p] = (v4d){0.0, 0.0, 0.0, 0.0};
-    const double* Wk = W64p + (size_t)kt * S * 64 + lane;
-#pragma unroll 4
-    for (int s = 0; s < S; ++s) {
-      const double a = Wk[(size_t)s * 64];
+    auto step = [&](int s, double a) {
       const int f = 2 * s + (g >> 1);
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
@@ -1143,13 +1159,19 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
         const double b = (g & 1) ? x : x * x;
         D[p] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, D[p], 0, 0, 0);
       }
-    }
-    double ce[4];
-    int comp[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      comp[j] = kt * 16 + 4 * j + g;
-      ce[j] = c64e[comp[j]];
+    };
+#pragma unroll 1
+    for (int s = 0; s < S; s += 4) {
+      const double wc = wl(kt, s + 2), wd = wl(kt, s + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      step(s, wa);
+      step(s + 1, wb);
+      __builtin_amdgcn_sched_barrier(0);
+      wa = s + 4 < S ? wl(kt, s + 4) : wl(kt + NP, 0);
+      wb = s + 4 < S ? wl(kt, s + 5) : wl(kt + NP, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      step(s + 2, wc);
+      step(s + 3, wd);
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
