@@ -225,6 +225,8 @@ def main(argv=None):
     ap.add_argument("--border-threshold", type=float, default=0.05)
     ap.add_argument("--kmeans", action="store_true",
                     help="time Lloyd iterations of k-means on the workload's X with its K initial means as centres")
+    ap.add_argument("--stats-precision", default="fp32", choices=["fp32", "split-bf16"],
+                    help="statistics contraction of the small-K regime (split-bf16: bf16 matrix cores)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this E-step build runs on a "
@@ -235,6 +237,7 @@ def main(argv=None):
     from soft_clustering_gmm_amd import datagen, gmm
     gmm.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    gmm.set_stats_precision(gmm.STATS_SPLIT_BF16 if args.stats_precision == "split-bf16" else gmm.STATS_FP32)
 
     w = datagen.WORKLOADS[args.workload]
     if args.border_lists:
@@ -279,12 +282,18 @@ def main(argv=None):
     flops = 8.0 * N * K * d
     xbytes = N * d * X.itemsize + K * (2 * d + 1) * 4
     achieved = flops / (k_avg * 1e-3) / 1e12
+    small = K <= 16 and d <= 64
     single = K <= 256
+    regime = "small-K" if small else "single-sweep" if single else "two-pass"
+    ctype = {"f32": "float", "f16": "_Float16"}[w.x_dtype]
+    kernel = (f"estep_small_kernel<{-(-d // 16)},{ctype},{str(args.stats_precision == 'split-bf16').lower()}> "
+              f"(small K)" if small
+              else f"estep_stats_kernel<{-(-d // 32)},0,{ctype}> (single sweep)" if single
+              else "estep_lse_kernel + estep_stats_kernel (two-pass)")
     roof = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": committed_traffic(args.workload),
-        "kernel": "estep_stats_kernel<4,0,float> (single sweep)" if single
-        else "estep_lse_kernel + estep_stats_kernel (two-pass)",
+        "kernel": kernel,
         "flops_per_launch": flops, "avg_launch_ms": round(k_avg, 4),
         "p90_launch_ms": round(float(np.percentile(k_ms, 90)), 4),
         "hbm_algorithmic_bytes_per_launch": xbytes,
@@ -294,13 +303,14 @@ def main(argv=None):
     out = {
         "metric": METRIC, "value": N * K / (ms_step * 1e-3), "unit": UNIT, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32+bf16x3" if (small and args.stats_precision == "split-bf16") else "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: N={N} d={d} K={K} {w.x_dtype} Gaussian blobs (seed {w.seed}); "
                                f"step = one EM iteration from the initial parameters (precompute, fused E-step+stats, "
                                f"reduction, M-step)",
-                   "N": N, "d": d, "K": K, "x_dtype": w.x_dtype,
-                   "regime": "single-sweep" if single else "two-pass"},
+                   "N": N, "d": d, "K": K, "x_dtype": w.x_dtype, "regime": regime,
+                   "stats_precision": args.stats_precision if small else "fp32"},
         "roofline": roof,
     }
     if args.cpu_rows > 0:

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <map>
 #include <mutex>
@@ -13,6 +14,9 @@
 #include "gmm_internal.hpp"
 
 namespace gmm {
+
+// Statistics contraction of the small-K kernel (gmm_set_stats_precision).
+static std::atomic<int> g_stats_precision{GMM_STATS_FP32};
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -74,6 +78,8 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
   }
   p.Kp16 = (int)ceil_div(K, 16) * 16;
   p.E = 1 + 2 * p.DP;
+  p.stats_split = regime == GMM_REGIME_SMALLK &&
+                  g_stats_precision.load(std::memory_order_relaxed) == GMM_STATS_SPLIT_BF16;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -485,6 +491,12 @@ int gmm_kmeans_iterate(const void* X, int32_t x_dtype, int64_t N, int32_t d, int
     if (e == hipSuccess) e = kmeans_update_impl(X, x_dtype, N, d, assign, K, C, nullptr, w, L, s);
     if (e != hipSuccess) return GMM_EHIP;
   }
+  return GMM_OK;
+}
+
+int gmm_set_stats_precision(int32_t mode) {
+  if (mode != GMM_STATS_FP32 && mode != GMM_STATS_SPLIT_BF16) return GMM_EINVAL;
+  g_stats_precision.store(mode, std::memory_order_relaxed);
   return GMM_OK;
 }
 

@@ -35,6 +35,7 @@ namespace gmm {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 constexpr double kLog2Pi = 1.83787706640934548356065947281;
@@ -730,6 +731,16 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
 // exp(x) of at most ~3e-8 over x <= 0.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 
+// v = hi + lo + d for eight fp32 values: hi and lo round to nearest bf16, so
+// |lo| <= 2^-9 |v| and |d| <= 2^-18 |v|.
+__device__ __forceinline__ void split_bf16(const float (&v)[8], v8bf& hi, v8bf& lo) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    hi[t] = (__bf16)v[t];
+    lo[t] = (__bf16)(v[t] - (float)hi[t]);
+  }
+}
+
 // Per wave: a 64-point tile of X [64][XS] and a score/responsibility tile
 // [64][SS] in LDS. Scores come from four 16x16x4 blocks; the row phase then
 // runs one point per lane (in-lane max / sum over the <= 16 components), and
@@ -743,7 +754,7 @@ struct SmallTile {
   static constexpr int LPE = DS == 1 ? 1 : (DS == 2 ? 2 : 4), FPL = DP / LPE;
 };
 
-template <int DS, typename XT>
+template <int DS, typename XT, bool SPLIT>
 __global__ void __launch_bounds__(256)
 estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wave_rows,
                    const double* __restrict__ W64p, const double* __restrict__ c64e,
@@ -1011,21 +1022,60 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
     wave_lds_sync();
 
     __builtin_amdgcn_s_setprio(1);
-    // 4. statistics: step j of block b uses r of point 16b + 4g + j (component c)
+    if constexpr (!SPLIT) {
+      // 4. statistics: step j of block b uses r of point 16b + 4g + j (component c)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int p = 16 * b + 4 * g + j;
-        const float r = sc[p * SS + c];
-        nk += r;
+        for (int j = 0; j < 4; ++j) {
+          const int p = 16 * b + 4 * g + j;
+          const float r = sc[p * SS + c];
+          nk += r;
 #pragma unroll
-        for (int t = 0; t < DS; ++t) {
-          const float xv = xs[p * XS + 16 * t + c];
-          SX[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(r, xv, SX[t], 0, 0, 0);
-          SXX[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(r, xv * xv, SXX[t], 0, 0, 0);
+          for (int t = 0; t < DS; ++t) {
+            const float xv = xs[p * XS + 16 * t + c];
+            SX[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(r, xv, SX[t], 0, 0, 0);
+            SXX[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(r, xv * xv, SXX[t], 0, 0, 0);
+          }
+        }
+    } else {
+      // 4. statistics as split-bf16 products on the bf16 MFMA (16x16x32): each
+      //    fp32 operand v = hi + lo + d with hi = bf16(v), lo = bf16(v - hi),
+      //    |d| <= 2^-18 |v|, and a*b is taken as hi*hi + hi*lo + lo*hi (exact
+      //    products, fp32 accumulation): per product |error| <= 3 * 2^-18 |a b|
+      //    before the accumulation's rounding. Block kb covers points
+      //    32 kb + 8 g + t (t < 8) of lane (g, c): r of component c is the A
+      //    operand, x or x^2 of feature 16 t2 + c the B operand.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float rr[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          rr[t] = sc[(32 * kb + 8 * g + t) * SS + c];
+          nk += rr[t];
+        }
+        v8bf rh, rl;
+        split_bf16(rr, rh, rl);
+#pragma unroll
+        for (int t2 = 0; t2 < DS; ++t2) {
+          float xx[8], x2[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            xx[t] = xs[(32 * kb + 8 * g + t) * XS + 16 * t2 + c];
+            x2[t] = xx[t] * xx[t];
+          }
+          v8bf xh, xl, qh, ql;
+          split_bf16(xx, xh, xl);
+          split_bf16(x2, qh, ql);
+          SX[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rh, xh, SX[t2], 0, 0, 0);
+          SXX[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rh, qh, SXX[t2], 0, 0, 0);
+          SX[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rh, xl, SX[t2], 0, 0, 0);
+          SXX[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rh, ql, SXX[t2], 0, 0, 0);
+          SX[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rl, xh, SX[t2], 0, 0, 0);
+          SXX[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rl, qh, SXX[t2], 0, 0, 0);
         }
       }
+    }
     __builtin_amdgcn_s_setprio(0);
     wave_lds_sync();  // the tiles are rewritten by the next iteration
   }
@@ -1457,9 +1507,10 @@ static hipError_t run_small(const Plan& p, const XT* X, const float* mu, float* 
                             hipStream_t stream) {
   const Workspace& w = p.ws;
   const int vec = (sizeof(XT) == 4 && p.d % 4 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0) ? 1 : 0;
-  estep_small_kernel<DS, XT><<<(unsigned)p.P, 64 * kSmallWaves, 0, stream>>>(
-      X, p.N, p.d, p.K, p.rows_per_chunk / kSmallWaves, w.W64p, w.c64e, mu, w.iv64, w.c64d, w.errc, w.partials,
-      w.llpart, ll_point, R, vec);
+  auto fn = p.stats_split ? estep_small_kernel<DS, XT, true> : estep_small_kernel<DS, XT, false>;
+  fn<<<(unsigned)p.P, 64 * kSmallWaves, 0, stream>>>(X, p.N, p.d, p.K, p.rows_per_chunk / kSmallWaves, w.W64p,
+                                                      w.c64e, mu, w.iv64, w.c64d, w.errc, w.partials, w.llpart,
+                                                      ll_point, R, vec);
   return hipGetLastError();
 }
 

@@ -18,11 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libgmm_mi355x.so")
 
 GMM_F32, GMM_F16, GMM_BF16 = 0, 1, 2
 REGIME_AUTO, REGIME_SINGLE, REGIME_TWOPASS, REGIME_SMALLK = 0, 1, 2, 3
+STATS_FP32, STATS_SPLIT_BF16 = 0, 1
 
 EXPORTS = (
     "gmm_version", "gmm_error_string", "gmm_workspace_bytes", "gmm_estep_stats",
     "gmm_estep_stats_regime", "gmm_estep_resp", "gmm_mstep", "gmm_em_iterate", "gmm_assign_top2",
-    "gmm_set_timing_events", "gmm_estep_stats_chunked", "gmm_workspace_bytes_chunked",
+    "gmm_set_timing_events", "gmm_set_stats_precision", "gmm_estep_stats_chunked", "gmm_workspace_bytes_chunked",
     "gmm_border_lists", "gmm_border_lists_workspace_bytes",
     "gmm_kmeans_assign", "gmm_kmeans_update", "gmm_kmeans_iterate", "gmm_kmeans_workspace_bytes",
 )
@@ -60,6 +61,8 @@ def _load() -> ctypes.CDLL:
     L.gmm_assign_top2.argtypes = [P, I32, I64, I32, P, P, P, I32, P, P, P, SZ, P]
     L.gmm_set_timing_events.restype = ctypes.c_int
     L.gmm_set_timing_events.argtypes = [P, P]
+    L.gmm_set_stats_precision.restype = ctypes.c_int
+    L.gmm_set_stats_precision.argtypes = [ctypes.c_int32]
     L.gmm_estep_stats_chunked.restype = ctypes.c_int
     L.gmm_estep_stats_chunked.argtypes = [P, I32, I64, I32, P, P, P, I32, P, P, P, P, P, I64, P, SZ, P]
     L.gmm_workspace_bytes_chunked.restype = SZ
@@ -247,6 +250,12 @@ def set_timing_events(start, stop) -> None:
     _check("gmm_set_timing_events", lib().gmm_set_timing_events(
         None if start is None else ctypes.c_void_p(start.cuda_event),
         None if stop is None else ctypes.c_void_p(stop.cuda_event)))
+
+
+def set_stats_precision(mode: int) -> None:
+    """Statistics contraction of the small-K regime, process-wide:
+    STATS_FP32 (default) or STATS_SPLIT_BF16 (split-bf16 products)."""
+    _check("gmm_set_stats_precision", lib().gmm_set_stats_precision(int(mode)))
 
 
 def assign_top2(X, mu, var, logw, *, ws=None):

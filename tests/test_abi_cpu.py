@@ -43,6 +43,14 @@ def test_version_and_error_strings(L):
     assert L.gmm_error_string(-99) == b"unknown status"
 
 
+def test_stats_precision_setting(L):
+    # host-only: the setting is validated and stored, nothing is enqueued
+    assert L.gmm_set_stats_precision(7) == -1
+    assert L.gmm_set_stats_precision(-1) == -1
+    assert L.gmm_set_stats_precision(1) == 0
+    assert L.gmm_set_stats_precision(0) == 0
+
+
 def test_workspace_bytes(L):
     assert L.gmm_workspace_bytes(0, 0, 8) == 0
     assert L.gmm_workspace_bytes(10, 129, 8) == 0

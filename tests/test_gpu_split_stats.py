@@ -1,0 +1,116 @@
+"""GPU parity of the split-bf16 statistics contraction (small-K regime).
+
+With gmm_set_stats_precision(GMM_STATS_SPLIT_BF16) the small-K kernel forms
+Nk, Sx, Sxx from split-bf16 products on the bf16 matrix cores. Each product is
+off by at most 3 * 2^-18 of its magnitude, so the statistics must meet the same
+1e-4 bars against the float64 oracle, while l_n, L and the responsibilities
+(which do not go through that contraction) must be bitwise those of the
+default fp32 contraction.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from soft_clustering_gmm_amd import datagen
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture()
+def G():
+    from soft_clustering_gmm_amd import gmm
+    gmm.lib()
+    yield gmm
+    gmm.set_stats_precision(gmm.STATS_FP32)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def _both(G, X, mu, var, logw):
+    args = (dev(X), dev(mu), dev(var), dev(logw))
+    G.set_stats_precision(G.STATS_FP32)
+    a = G.estep_stats(*args, regime=G.REGIME_SMALLK, want_point_loglik=True)
+    G.set_stats_precision(G.STATS_SPLIT_BF16)
+    b = G.estep_stats(*args, regime=G.REGIME_SMALLK, want_point_loglik=True)
+    torch.cuda.synchronize()
+    return a, b
+
+
+def _check(G, X, mu, var, logw, what):
+    a, b = _both(G, X, mu, var, logw)
+    assert np.array_equal(host(a[4]), host(b[4])), f"{what}: l_n differs between the two contractions"
+    assert float(a[3]) == float(b[3]), f"{what}: L differs between the two contractions"
+    ref = oracle.estep(X, mu, var, logw, keep_R=True)
+    X64 = X.astype(np.float64)
+    es = parity.check_stats((host(b[0]), host(b[1]), host(b[2])), ref, X64, ref["R"].T @ np.abs(X64), what)
+    parity.check_total(host(b[3]), ref, what)
+    print(f"{what}: split-bf16 stats {es[0]:.1e}/{es[1]:.1e}/{es[2]:.1e}", flush=True)
+    return es
+
+
+@pytest.mark.parametrize("name,N", [("tiny", None), ("smallk", 5003)])
+def test_split_stats_workloads(G, name, N):
+    X, mu, var, logw = datagen.make_workload(name, N=N)
+    _check(G, X, mu, var, logw, f"{name} N={len(X)}")
+
+
+@pytest.mark.parametrize("N,d,K", [(1, 3, 1), (63, 5, 3), (65, 1, 2), (300, 48, 16), (33, 64, 11),
+                                   (1000, 20, 13), (640, 16, 16)])
+def test_split_stats_edge_shapes(G, N, d, K):
+    X, mu, var, logw = datagen.random_problem(2000 + N + d + K, N, d, K)
+    _check(G, X, mu, var, logw, f"edge N={N} d={d} K={K}")
+
+
+def test_split_stats_bfloat16_x(G):
+    X, mu, var, logw = datagen.make_workload("smallk", N=3001)
+    Xb = torch.from_numpy(X).to(torch.bfloat16)
+    X = Xb.to(torch.float32).numpy()  # the values the kernel sees, exactly
+    args = (Xb.to("cuda"), dev(mu), dev(var), dev(logw))
+    G.set_stats_precision(G.STATS_SPLIT_BF16)
+    Nk, Sx, Sxx, L, _ = G.estep_stats(*args, regime=G.REGIME_SMALLK)
+    torch.cuda.synchronize()
+    ref = oracle.estep(X, mu, var, logw, keep_R=True)
+    X64 = X.astype(np.float64)
+    parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, X64, ref["R"].T @ np.abs(X64), "bf16 X split")
+
+
+def test_split_stats_setting(G):
+    from soft_clustering_gmm_amd.gmm import GmmError
+    with pytest.raises(GmmError):
+        G.set_stats_precision(7)
+    # the two-pass and single-sweep regimes ignore the setting: bitwise equal results
+    X, mu, var, logw = datagen.make_workload("ref", N=2001)
+    args = (dev(X), dev(mu), dev(var), dev(logw))
+    for regime in (G.REGIME_SINGLE, G.REGIME_TWOPASS):
+        G.set_stats_precision(G.STATS_FP32)
+        a = G.estep_stats(*args, regime=regime)
+        G.set_stats_precision(G.STATS_SPLIT_BF16)
+        b = G.estep_stats(*args, regime=regime)
+        torch.cuda.synchronize()
+        for x, y in zip(a[:3], b[:3]):
+            assert torch.equal(x, y)
+
+
+def test_split_stats_full_size_smallk(G):
+    X, mu, var, logw = datagen.make_workload("smallk")
+    G.set_stats_precision(G.STATS_SPLIT_BF16)
+    Nk, Sx, Sxx, L, _ = G.estep_stats(dev(X), dev(mu), dev(var), dev(logw))
+    torch.cuda.synchronize()
+    ref = oracle.estep(X, mu, var, logw, form="expanded", row_chunk=1 << 16)
+    absx = np.zeros(mu.shape)
+    for lo in range(0, X.shape[0], 1 << 16):
+        x = X[lo:lo + (1 << 16)].astype(np.float64)
+        R = oracle.responsibilities(oracle.component_scores(x, mu, var, logw, "expanded"))
+        absx += R.T @ np.abs(x)
+    es = parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, None, absx, "smallk full size, split-bf16")
+    parity.check_total(host(L), ref, "smallk full size, split-bf16")
+    print(f"smallk full size, split-bf16 stats {es}", flush=True)
