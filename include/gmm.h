@@ -131,7 +131,7 @@ int gmm_em_iterate(const void* X, int32_t x_dtype, int64_t N, int32_t d, int32_t
 int gmm_set_timing_events(void* start, void* stop);
 
 /* Precision of the statistics contraction (Nk, Sx, Sxx = sums of r * [1, x,
- * x^2]) in the small-K regime (K <= 16, d <= 64). The pages measure their
+ * x^2]) of the fused E-step kernels, in every regime. The pages measure their
  * kernels with half-precision data ("Flash-KMeans" article, test setup); this
  * option moves that contraction onto the bf16 matrix cores instead:
  *   GMM_STATS_FP32      - fp32 MFMA products (default);
@@ -143,10 +143,9 @@ int gmm_set_timing_events(void* start, void* stop);
  *                          relative), inside the 1e-4 bar on the statistics.
  * Scores, responsibilities, l_n and L are unchanged (fp32 MFMA scores with the
  * exact re-score). The setting is process-wide and read when an E-step is
- * enqueued (gmm_estep_stats*, gmm_estep_resp, gmm_em_iterate); other regimes
- * ignore it. Returns GMM_OK, or GMM_EINVAL for an unknown mode (setting
- * unchanged). Not synchronised with calls enqueued concurrently from other
- * threads. */
+ * enqueued (gmm_estep_stats*, gmm_estep_resp, gmm_em_iterate). Returns GMM_OK,
+ * or GMM_EINVAL for an unknown mode (setting unchanged). Not synchronised with
+ * calls enqueued concurrently from other threads. */
 enum gmm_stats_precision { GMM_STATS_FP32 = 0, GMM_STATS_SPLIT_BF16 = 1 };
 int gmm_set_stats_precision(int32_t mode);
 

@@ -78,8 +78,7 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
   }
   p.Kp16 = (int)ceil_div(K, 16) * 16;
   p.E = 1 + 2 * p.DP;
-  p.stats_split = regime == GMM_REGIME_SMALLK &&
-                  g_stats_precision.load(std::memory_order_relaxed) == GMM_STATS_SPLIT_BF16;
+  p.stats_split = g_stats_precision.load(std::memory_order_relaxed) == GMM_STATS_SPLIT_BF16;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {

@@ -51,7 +51,7 @@ struct Plan {
   int64_t rows_per_chunk;
   int64_t tiles;    // ceil(N / 64)
   int E;            // 1 + 2*DP floats per component in a partial
-  int stats_split;  // statistics contraction as split-bf16 products (small-K kernel)
+  int stats_split;  // statistics contraction as split-bf16 products on the bf16 MFMA
   size_t bytes;     // workspace bytes this plan uses
   Workspace ws;
 };

@@ -52,6 +52,16 @@ constexpr int kRefCap = 128;       // re-score list entries per wave and pass
 // loads at offsets past the record count return zero.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
+// v = hi + lo + d for eight fp32 values: hi and lo round to nearest bf16, so
+// |lo| <= 2^-9 |v| and |d| <= 2^-18 |v|.
+__device__ __forceinline__ void split_bf16(const float (&v)[8], v8bf& hi, v8bf& lo) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    hi[t] = (__bf16)v[t];
+    lo[t] = (__bf16)(v[t] - (float)hi[t]);
+  }
+}
+
 // Row of the 32x32 MFMA accumulator held in slot j by lanes of half h:
 // D[row][col] with col = lane % 32 and row = 8*(j/4) + 4*h + j%4.
 __device__ __forceinline__ int acc_row(int h, int j) { return ((j >> 2) << 3) + (h << 2) + (j & 3); }
@@ -277,7 +287,7 @@ __global__ void errc_kernel(const float* __restrict__ compmax, int K, float* __r
 //      accumulate Sx, Sxx for the wave's 32 components in registers.
 // At the end each block writes its statistics partial; a separate kernel
 // sums the partials in a fixed order (no atomics anywhere).
-template <int DT, int MODE, typename XT>
+template <int DT, int MODE, typename XT, bool SPLIT>
 __global__ void __launch_bounds__(512)
 estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, int waves, int kslabs,
                    int64_t rows_per_chunk, const float4* __restrict__ W32p, const float* __restrict__ c32,
@@ -640,7 +650,47 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     const int64_t rn = r0 + 64;
     if (async_x && rn < hi) async_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, reinterpret_cast<const float*>(X),
                                              rn, hi, d, wave, waves, lane);
-    {
+    if constexpr (SPLIT) {
+      // Split-bf16 products on the 32x32x16 bf16 MFMA (see the small-K
+      // kernel for the error of a product): block pb covers points
+      // 16 pb + 8 h + t (t < 8) of lane (h, c), r of component c as the A
+      // operand and x or x^2 of feature DT c + t2 of the same points as B, so
+      // the accumulators keep the layout of the fp32 path.
+#pragma unroll 1
+      for (int pb = 0; pb < 4; ++pb) {
+        float rr[8], xv[8][DT];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int row = 16 * pb + 8 * h + t;
+          rr[t] = sc[row * SCS + wave * 32 + c];
+          if (MODE == 0) rr[t] *= rv[2 * row + 1];  // e -> r = e / z (0 past the last row)
+          nk += rr[t];
+          const float* xr = xs + row * XS + DT * c;
+#pragma unroll
+          for (int t2 = 0; t2 < DT; ++t2) xv[t][t2] = xr[t2];
+        }
+        v8bf rh, rl;
+        split_bf16(rr, rh, rl);
+#pragma unroll
+        for (int t2 = 0; t2 < DT; ++t2) {
+          float xx[8], x2[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            xx[t] = xv[t][t2];
+            x2[t] = xx[t] * xx[t];
+          }
+          v8bf xh, xl, qh, ql;
+          split_bf16(xx, xh, xl);
+          split_bf16(x2, qh, ql);
+          SX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rh, xh, SX[t2], 0, 0, 0);
+          SXX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rh, qh, SXX[t2], 0, 0, 0);
+          SX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rh, xl, SX[t2], 0, 0, 0);
+          SXX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rh, ql, SXX[t2], 0, 0, 0);
+          SX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rl, xh, SX[t2], 0, 0, 0);
+          SXX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rl, qh, SXX[t2], 0, 0, 0);
+        }
+      }
+    } else {
       // Step s takes point acc_row(h, s % 16) of row half s / 16. The operands
       // of the next step are read from LDS before this step's MFMAs issue.
       auto sload = [&](int s, float& r, float(&xv)[DT]) {
@@ -730,16 +780,6 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
 // ~|x| * 2^-24 * log2(e) from rounding x*log2(e), i.e. an absolute error in
 // exp(x) of at most ~3e-8 over x <= 0.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
-
-// v = hi + lo + d for eight fp32 values: hi and lo round to nearest bf16, so
-// |lo| <= 2^-9 |v| and |d| <= 2^-18 |v|.
-__device__ __forceinline__ void split_bf16(const float (&v)[8], v8bf& hi, v8bf& lo) {
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    hi[t] = (__bf16)v[t];
-    lo[t] = (__bf16)(v[t] - (float)hi[t]);
-  }
-}
 
 // Per wave: a 64-point tile of X [64][XS] and a score/responsibility tile
 // [64][SS] in LDS. Scores come from four 16x16x4 blocks; the row phase then
@@ -1472,7 +1512,7 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
   const int KS = p.waves * 32;
   const size_t lds = (size_t)(2 * 64 * (32 * DT + 4) + 64 * (KS + 8) + 256) * sizeof(float) +
                      (size_t)nthr * sizeof(double) + (size_t)p.waves * kRefCap * sizeof(uint32_t);
-  auto fn = estep_stats_kernel<DT, MODE, XT>;
+  auto fn = p.stats_split ? estep_stats_kernel<DT, MODE, XT, true> : estep_stats_kernel<DT, MODE, XT, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -253,7 +253,7 @@ def set_timing_events(start, stop) -> None:
 
 
 def set_stats_precision(mode: int) -> None:
-    """Statistics contraction of the small-K regime, process-wide:
+    """Statistics contraction of the fused E-step kernels, process-wide:
     STATS_FP32 (default) or STATS_SPLIT_BF16 (split-bf16 products)."""
     _check("gmm_set_stats_precision", lib().gmm_set_stats_precision(int(mode)))
 

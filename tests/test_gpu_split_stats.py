@@ -1,6 +1,6 @@
-"""GPU parity of the split-bf16 statistics contraction (small-K regime).
+"""GPU parity of the split-bf16 statistics contraction, in every regime.
 
-With gmm_set_stats_precision(GMM_STATS_SPLIT_BF16) the small-K kernel forms
+With gmm_set_stats_precision(GMM_STATS_SPLIT_BF16) the fused kernels form
 Nk, Sx, Sxx from split-bf16 products on the bf16 matrix cores. Each product is
 off by at most 3 * 2^-18 of its magnitude, so the statistics must meet the same
 1e-4 bars against the float64 oracle, while l_n, L and the responsibilities
@@ -35,18 +35,18 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
-def _both(G, X, mu, var, logw):
+def _both(G, X, mu, var, logw, regime):
     args = (dev(X), dev(mu), dev(var), dev(logw))
     G.set_stats_precision(G.STATS_FP32)
-    a = G.estep_stats(*args, regime=G.REGIME_SMALLK, want_point_loglik=True)
+    a = G.estep_stats(*args, regime=regime, want_point_loglik=True)
     G.set_stats_precision(G.STATS_SPLIT_BF16)
-    b = G.estep_stats(*args, regime=G.REGIME_SMALLK, want_point_loglik=True)
+    b = G.estep_stats(*args, regime=regime, want_point_loglik=True)
     torch.cuda.synchronize()
     return a, b
 
 
-def _check(G, X, mu, var, logw, what):
-    a, b = _both(G, X, mu, var, logw)
+def _check(G, X, mu, var, logw, regime, what):
+    a, b = _both(G, X, mu, var, logw, regime)
     assert np.array_equal(host(a[4]), host(b[4])), f"{what}: l_n differs between the two contractions"
     assert float(a[3]) == float(b[3]), f"{what}: L differs between the two contractions"
     ref = oracle.estep(X, mu, var, logw, keep_R=True)
@@ -57,17 +57,30 @@ def _check(G, X, mu, var, logw, what):
     return es
 
 
-@pytest.mark.parametrize("name,N", [("tiny", None), ("smallk", 5003)])
+def _regimes(G, K, d):
+    out = [G.REGIME_TWOPASS]
+    if K <= 256:
+        out.append(G.REGIME_SINGLE)
+    if K <= 16 and d <= 64:
+        out.append(G.REGIME_SMALLK)
+    return out
+
+
+@pytest.mark.parametrize("name,N", [("tiny", None), ("smallk", 5003), ("ref", 3001), ("largek", 700),
+                                    ("ivf", 1500)])
 def test_split_stats_workloads(G, name, N):
     X, mu, var, logw = datagen.make_workload(name, N=N)
-    _check(G, X, mu, var, logw, f"{name} N={len(X)}")
+    for r in _regimes(G, mu.shape[0], X.shape[1]):
+        _check(G, X, mu, var, logw, r, f"{name} N={len(X)} regime={r}")
 
 
 @pytest.mark.parametrize("N,d,K", [(1, 3, 1), (63, 5, 3), (65, 1, 2), (300, 48, 16), (33, 64, 11),
-                                   (1000, 20, 13), (640, 16, 16)])
+                                   (1000, 20, 13), (640, 16, 16), (130, 33, 33), (129, 128, 64),
+                                   (97, 17, 257), (150, 96, 129)])
 def test_split_stats_edge_shapes(G, N, d, K):
     X, mu, var, logw = datagen.random_problem(2000 + N + d + K, N, d, K)
-    _check(G, X, mu, var, logw, f"edge N={N} d={d} K={K}")
+    for r in _regimes(G, K, d):
+        _check(G, X, mu, var, logw, r, f"edge N={N} d={d} K={K} regime={r}")
 
 
 def test_split_stats_bfloat16_x(G):
@@ -87,21 +100,11 @@ def test_split_stats_setting(G):
     from soft_clustering_gmm_amd.gmm import GmmError
     with pytest.raises(GmmError):
         G.set_stats_precision(7)
-    # the two-pass and single-sweep regimes ignore the setting: bitwise equal results
-    X, mu, var, logw = datagen.make_workload("ref", N=2001)
-    args = (dev(X), dev(mu), dev(var), dev(logw))
-    for regime in (G.REGIME_SINGLE, G.REGIME_TWOPASS):
-        G.set_stats_precision(G.STATS_FP32)
-        a = G.estep_stats(*args, regime=regime)
-        G.set_stats_precision(G.STATS_SPLIT_BF16)
-        b = G.estep_stats(*args, regime=regime)
-        torch.cuda.synchronize()
-        for x, y in zip(a[:3], b[:3]):
-            assert torch.equal(x, y)
 
 
-def test_split_stats_full_size_smallk(G):
-    X, mu, var, logw = datagen.make_workload("smallk")
+@pytest.mark.parametrize("name", ["smallk", "ref"])
+def test_split_stats_full_size(G, name):
+    X, mu, var, logw = datagen.make_workload(name)
     G.set_stats_precision(G.STATS_SPLIT_BF16)
     Nk, Sx, Sxx, L, _ = G.estep_stats(dev(X), dev(mu), dev(var), dev(logw))
     torch.cuda.synchronize()
@@ -111,6 +114,6 @@ def test_split_stats_full_size_smallk(G):
         x = X[lo:lo + (1 << 16)].astype(np.float64)
         R = oracle.responsibilities(oracle.component_scores(x, mu, var, logw, "expanded"))
         absx += R.T @ np.abs(x)
-    es = parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, None, absx, "smallk full size, split-bf16")
-    parity.check_total(host(L), ref, "smallk full size, split-bf16")
-    print(f"smallk full size, split-bf16 stats {es}", flush=True)
+    es = parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, None, absx, f"{name} full size, split-bf16")
+    parity.check_total(host(L), ref, f"{name} full size, split-bf16")
+    print(f"{name} full size, split-bf16 stats {es}", flush=True)
