@@ -451,17 +451,19 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       float4* srow4 = reinterpret_cast<float4*>(srow);
       float m, lZ = 0.f;
       double z = 0.0;
+      // The thread's 32 entries stay in registers from one LDS read (all
+      // eight loads in flight) through the max, exp and flag passes.
+      float4 ev[8];
       if (MODE == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ev[i] = srow4[psub + tpr * i];
         float mx = -INFINITY;
-#pragma unroll 4
-        for (int i = 0; i < 8; ++i) {
-          const float4 v = srow4[psub + tpr * i];
-          mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
-        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fmaxf(fmaxf(ev[i].x, ev[i].y), fmaxf(ev[i].z, ev[i].w)));
         m = group_max(mx, tpr);
-#pragma unroll 2
+#pragma unroll
         for (int i = 0; i < 8; ++i) {
-          float4 v = srow4[psub + tpr * i];
+          float4& v = ev[i];
           v.x = __builtin_amdgcn_exp2f(v.x - m);
           v.y = __builtin_amdgcn_exp2f(v.y - m);
           v.z = __builtin_amdgcn_exp2f(v.z - m);
@@ -474,9 +476,11 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       } else {
         m = rv[2 * row];
         lZ = rv[2 * row + 1];
-#pragma unroll 2
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ev[i] = srow4[psub + tpr * i];
+#pragma unroll
         for (int i = 0; i < 8; ++i) {
-          float4 v = srow4[psub + tpr * i];
+          float4& v = ev[i];
           v.x = __builtin_amdgcn_exp2f((v.x - m) - lZ);
           v.y = __builtin_amdgcn_exp2f((v.y - m) - lZ);
           v.z = __builtin_amdgcn_exp2f((v.z - m) - lZ);
@@ -501,9 +505,9 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         const bool refine = valid && maxq > thr2;
         float flagged = 0.f;
         if (refine)
-#pragma unroll 4
+#pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const float4 v = srow4[psub + tpr * i];
+            const float4 v = ev[i];
             const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -518,9 +522,9 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         const float anyflag = group_max(mask ? 1.f : 0.f, tpr);
         if (refine && anyflag > 0.f && (double)Ebound * unref / z > (double)kGateTau) {
           mask = 0;
-#pragma unroll 4
+#pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const float4 v = srow4[psub + tpr * i];
+            const float4 v = ev[i];
             mask |= (v.x >= kExpWindow ? 1u : 0u) << (4 * i);
             mask |= (v.y >= kExpWindow ? 1u : 0u) << (4 * i + 1);
             mask |= (v.z >= kExpWindow ? 1u : 0u) << (4 * i + 2);
@@ -530,9 +534,9 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       } else {
         const float thr = kGateTau / Ebound;
         if (valid && __builtin_amdgcn_exp2f(-lZ) > thr)
-#pragma unroll 4
+#pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const float4 v = srow4[psub + tpr * i];
+            const float4 v = ev[i];
             mask |= (v.x >= thr ? 1u : 0u) << (4 * i);
             mask |= (v.y >= thr ? 1u : 0u) << (4 * i + 1);
             mask |= (v.z >= thr ? 1u : 0u) << (4 * i + 2);
