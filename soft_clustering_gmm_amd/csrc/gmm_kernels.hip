@@ -1187,8 +1187,10 @@ __device__ __forceinline__ void top2_insert(double v, int i, double& v1, int& i1
   }
 }
 
+// Four waves per SIMD (at most 128 registers): the fp64 MFMA chains of four
+// blocks per CU hide each other's LDS and L2 latency.
 template <int DT, bool TOP2, typename XT, int NP>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 4)
 estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
                  const double* __restrict__ W64p, const double* __restrict__ c64e,
                  float2* __restrict__ rowref, float* __restrict__ ll_point, double* __restrict__ llpart,
