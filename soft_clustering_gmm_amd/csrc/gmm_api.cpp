@@ -101,6 +101,13 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
   const size_t o_part = take((size_t)std::max<int64_t>(p.P, 1) * p.Kp * p.E * sizeof(float));
   const size_t o_ll = take((size_t)std::max<int64_t>(std::max(p.P, p.tiles), 1) * sizeof(double));
   const size_t o_stats = take((size_t)K * (1 + 2 * d) * sizeof(float));
+  // Few outputs (small K x d) give the one-stage reduction too few threads, each
+  // summing many partials in sequence: split the partials into G segments.
+  {
+    const int64_t n = (int64_t)K * (1 + 2 * d);
+    p.G = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)262144 / n, (int64_t)64, std::max<int64_t>(p.P, 1)}));
+  }
+  const size_t o_red = take(p.G > 1 ? (size_t)p.G * K * (1 + 2 * d) * sizeof(double) : 0);
   p.bytes = off;
   if (base) {
     char* b = static_cast<char*>(base);
@@ -118,6 +125,7 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
     p.ws.partials = reinterpret_cast<float*>(b + o_part);
     p.ws.llpart = reinterpret_cast<double*>(b + o_ll);
     p.ws.stats = reinterpret_cast<float*>(b + o_stats);
+    p.ws.redtmp = reinterpret_cast<double*>(b + o_red);
   }
   *plan = p;
   return GMM_OK;

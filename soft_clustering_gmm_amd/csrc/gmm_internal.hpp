@@ -36,6 +36,7 @@ struct Workspace {
   float* partials;  // [P][Kp][E] per-chunk statistics
   double* llpart;   // [max(P, tiles)] per-block log-likelihood sums
   float* stats;     // [K][1 + 2d] Nk | Sx | Sxx scratch for the EM loop
+  double* redtmp;   // [G][K (1 + 2d)] segment sums of the two-stage statistics reduction (G > 1)
 };
 
 struct Plan {
@@ -48,6 +49,7 @@ struct Plan {
   int Kp;           // padded K of the statistics kernel = 32*waves*kslabs
   int Kp16;         // K rounded up to 16 (fp64 pass)
   int64_t P;        // row chunks of the statistics kernel
+  int G;            // partial segments of the statistics reduction (1: one stage)
   int64_t rows_per_chunk;
   int64_t tiles;    // ceil(N / 64)
   int E;            // 1 + 2*DP floats per component in a partial

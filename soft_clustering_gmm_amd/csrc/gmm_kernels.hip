@@ -1413,6 +1413,39 @@ __global__ void reduce_stats_kernel(const float* __restrict__ partials, int64_t 
     Sxx[(size_t)k * d + e - 1 - d] = s;
 }
 
+// Two-stage form for few outputs: segment g of the partials (in order) per
+// thread, then the G segment sums per output, in order.
+__global__ void reduce_stats_seg_kernel(const float* __restrict__ partials, int64_t P, int G, int Kp, int E,
+                                        int DP, int K, int d, double* __restrict__ tmp) {
+  const int W = 1 + 2 * d;
+  const int64_t n = (int64_t)K * W;
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int g = blockIdx.y;
+  if (t >= n) return;
+  const int k = (int)(t / W), e = (int)(t - (int64_t)k * W);
+  const int64_t p0 = P * g / G, p1 = P * (g + 1) / G;
+  const size_t stride = (size_t)Kp * E;
+  tmp[g * n + t] = sum_partials(partials + p0 * stride, p1 - p0, Kp, E, DP, d, k, e);
+}
+
+__global__ void reduce_stats_final_kernel(const double* __restrict__ tmp, int G, int K, int d,
+                                          float* __restrict__ Nk, float* __restrict__ Sx,
+                                          float* __restrict__ Sxx) {
+  const int W = 1 + 2 * d;
+  const int64_t n = (int64_t)K * W;
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  double s = 0.0;
+  for (int g = 0; g < G; ++g) s += tmp[g * n + t];
+  const int k = (int)(t / W), e = (int)(t - (int64_t)k * W);
+  if (e == 0)
+    Nk[k] = (float)s;
+  else if (e <= d)
+    Sx[(size_t)k * d + e - 1] = (float)s;
+  else
+    Sxx[(size_t)k * d + e - 1 - d] = (float)s;
+}
+
 // Row-chunked E-step: the statistics of one chunk of rows are added (in
 // chunk order) to fp64 accumulators acc[k * (1 + 2d) + e], e as above.
 __global__ void accum_stats_kernel(const float* __restrict__ partials, int64_t P, int Kp, int E, int DP, int K,
@@ -1620,8 +1653,14 @@ hipError_t launch_estep(const Plan& p, const void* X, int x_dtype, const float* 
   const Workspace& w = p.ws;
   if (Nk && Sx && Sxx) {
     const int64_t n = (int64_t)p.K * (1 + 2 * p.d);
-    reduce_stats_kernel<<<nblocks(n, 256), 256, 0, stream>>>(w.partials, p.P, p.Kp, p.E, p.DP, p.K, p.d, Nk,
-                                                               Sx, Sxx);
+    if (p.G > 1) {
+      reduce_stats_seg_kernel<<<dim3(nblocks(n, 256), p.G), 256, 0, stream>>>(w.partials, p.P, p.G, p.Kp, p.E,
+                                                                              p.DP, p.K, p.d, w.redtmp);
+      reduce_stats_final_kernel<<<nblocks(n, 256), 256, 0, stream>>>(w.redtmp, p.G, p.K, p.d, Nk, Sx, Sxx);
+    } else {
+      reduce_stats_kernel<<<nblocks(n, 256), 256, 0, stream>>>(w.partials, p.P, p.Kp, p.E, p.DP, p.K, p.d, Nk,
+                                                                 Sx, Sxx);
+    }
   }
   if (loglik_total) {
     const int64_t nll = p.regime == 2 ? p.tiles : p.P;
