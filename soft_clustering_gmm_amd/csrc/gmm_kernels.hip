@@ -86,12 +86,11 @@ __device__ __forceinline__ double dpp_d(double v) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
-// DPP lane permutations within a row of 16 lanes: quad xor 1, quad xor 2,
-// mirror within each half row (i <-> 7 - i), mirror within the row
-// (i <-> 15 - i). Applied in this order as add steps they leave every lane of
-// the row with the sum over the row (the quad sums, then the half-row sums,
-// then the row sum), bitwise identical on all 16 lanes.
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+// DPP lane permutations within a row of 16 lanes: quad xor 1, quad xor 2 and
+// the mirror within each half row (i <-> 7 - i). Applied in this order as add
+// steps they leave every lane of an aligned group of 8 with the group's sum
+// (the quad sums, then the half-row sums), bitwise identical on all 8 lanes.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141;
 
 // All-reduce over aligned groups of tpr consecutive lanes (tpr a power of two
 // <= 8) with the DPP steps above; every lane of a group ends with the same
