@@ -16,16 +16,21 @@
 // Precision. FP32 accumulation of the expanded form loses ~1e-4 absolute on
 // scores of magnitude ~10^2, which is too coarse for responsibilities near
 // 0.5. Each row therefore carries an a-priori bound E_n on the fp32 score
-// error; when 2 E_n / Z_n (Z_n = sum_k exp(s_nk - max)) could exceed a small
-// threshold, every component within kWindow of the row maximum is re-scored
-// exactly (fp64, difference form) before the normalisation. Components
-// outside the window have r < e^-20, so their fp32 error cannot matter.
+// error, and the entries whose responsibility that error could move by more
+// than a small tau are re-scored exactly (fp64, difference form) before the
+// normalisation: with l_n from the same fp32 scores (single sweep, small K)
+// those with 2 E_n r (1 - r) > tau, widened to every component within 20 of
+// the row maximum when the unrefined mass could still matter; with an
+// exact l_n (second pass of the two-pass regime) those with E_n r > tau. The
+// fp32 operands are scaled by log2(e), so scores come out in base 2 and every
+// exponential is one hardware exp2.
 //
 // Regimes (Turbo-GMM abstract): the single sweep keeps the whole component
 // axis of a 64-point tile on chip (K <= 256) and does max, log-sum-exp and
 // statistics in one traversal. The two-pass fallback computes l_n first in a
-// fp64-MFMA pass (exact, so it needs no re-score), then recomputes the fp32
-// scores per 256-component slab and accumulates the statistics.
+// fp64-MFMA pass, then recomputes the fp32 scores per 256-component slab and
+// accumulates the statistics. A small-K kernel (K <= 16, d <= 64) gives each
+// wave its own rows and keeps the whole mixture in registers.
 #include "gmm_device.hpp"
 #include "gmm_internal.hpp"
 
@@ -41,9 +46,12 @@ typedef double v4d __attribute__((ext_vector_type(4)));
 constexpr double kLog2Pi = 1.83787706640934548356065947281;
 constexpr double kLog2E = 1.44269504088896340735992468100;  // 1 / ln 2
 constexpr double kLn2 = 0.693147180559945309417232121458;
-constexpr float kWindow = 20.0f;   // re-score components with s >= max - kWindow
-constexpr float kExpWindow = 2.0611536e-9f;  // exp(-kWindow)
-constexpr float kGateTau = 5e-7f;  // re-score a row when 2 E_n * r_max could exceed this
+// The window of the fallback rule: components with s >= max - 20, i.e.
+// e = exp(s - max) >= exp(-20).
+constexpr float kExpWindow = 2.0611536e-9f;
+// tau: the largest change of a responsibility that the fp32 score error may
+// cause in an entry left unrefined (20x below the 1e-5 bar).
+constexpr float kGateTau = 5e-7f;
 // Per-operation relative error assumed for fp32 arithmetic in the bound below:
 // 2^-23, which also covers an accumulator that truncates rather than rounds.
 constexpr float kUnitRound = 1.1920928955078125e-7f;
@@ -493,7 +501,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       //   2 E r_k (1 - r_k) > tau are refined (a nearly one-hot row needs
       //   nothing). Refined entries are then off by at most E * U, U = the
       //   unrefined mass; if that could exceed tau the window widens to every
-      //   entry within kWindow of the row maximum.
+      //   entry within 20 of the row maximum (e >= kExpWindow).
       //  MODE 1: l_n is exact (first pass), an unrefined entry is off by
       //   <= E r_k, and entries with r_k > tau / E are refined.
       uint32_t mask = 0;
@@ -962,7 +970,7 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
         sq += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
       }
       // re-score rule of the single sweep (see the main kernel): refine entries
-      // with 2 E r (1 - r) > tau; widen to the kWindow window if the unrefined
+      // with 2 E r (1 - r) > tau; widen to the e >= kExpWindow window if the unrefined
       // mass could still move the refined ones by more than tau.
       const float Eb = gam * (a_max * sq + b2_max * __builtin_sqrtf(sq)) + 2.f * kUnitRound * c_max;
       const float thr2 = kGateTau * z * z * __builtin_amdgcn_rcpf(2.f * Eb);  // on e (z - e)
