@@ -117,3 +117,20 @@ def test_split_stats_full_size(G, name):
     es = parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, None, absx, f"{name} full size, split-bf16")
     parity.check_total(host(L), ref, f"{name} full size, split-bf16")
     print(f"{name} full size, split-bf16 stats {es}", flush=True)
+
+
+@pytest.mark.parametrize("name,N,chunk", [("smallk", 5003, 1024), ("ref", 3001, 640), ("ivf", 1500, 512)])
+def test_split_stats_chunked_host_x(G, name, N, chunk):
+    # the row-chunked path over host-resident X honours the setting as well
+    X, mu, var, logw = datagen.make_workload(name, N=N)
+    Xh = torch.from_numpy(X).pin_memory()
+    G.set_stats_precision(G.STATS_SPLIT_BF16)
+    Nk, Sx, Sxx, L, lp = G.estep_stats_chunked(Xh, dev(mu), dev(var), dev(logw), chunk, want_point_loglik=True)
+    torch.cuda.synchronize()
+    X32 = X.astype(np.float32)  # fp16 X is widened exactly on both sides
+    ref = oracle.estep(X32, mu, var, logw, keep_R=True)
+    X64 = X32.astype(np.float64)
+    what = f"{name} N={N} chunk={chunk} split-bf16"
+    parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, X64, ref["R"].T @ np.abs(X64), what)
+    parity.check_total(host(L), ref, what)
+    parity.check_loglik_point(host(lp), ref["l"], what)
