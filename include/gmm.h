@@ -137,10 +137,11 @@ int gmm_set_timing_events(void* start, void* stop);
  *   GMM_STATS_FP32      - fp32 MFMA products (default);
  *   GMM_STATS_SPLIT_BF16 - every fp32 operand v is split as v = hi + lo + d
  *                          with hi = bf16(v), lo = bf16(v - hi), |d| <=
- *                          2^-18 |v|, and a*b is taken as hi*hi + hi*lo +
+ *                          2^-16 |v|, and a*b is taken as hi*hi + hi*lo +
  *                          lo*hi, exact products accumulated in fp32: each
- *                          product is off by <= 3 * 2^-18 |a b| (~1.1e-5
- *                          relative), inside the 1e-4 bar on the statistics.
+ *                          product is off by <= 3.0001 * 2^-16 |a b| (4.6e-5
+ *                          relative) before the accumulation's rounding,
+ *                          inside the 1e-4 bar on the statistics.
  * Scores, responsibilities, l_n and L are unchanged (fp32 MFMA scores with the
  * exact re-score). The setting is process-wide and read when an E-step is
  * enqueued (gmm_estep_stats*, gmm_estep_resp, gmm_em_iterate). Returns GMM_OK,

@@ -61,7 +61,7 @@ constexpr int kRefCap = 128;       // re-score list entries per wave and pass
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // v = hi + lo + d for eight fp32 values: hi and lo round to nearest bf16, so
-// |lo| <= 2^-9 |v| and |d| <= 2^-18 |v|.
+// |lo| <= 2^-8 |v| and |d| <= 2^-16 |v|.
 __device__ __forceinline__ void split_bf16(const float (&v)[8], v8bf& hi, v8bf& lo) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -1092,8 +1092,8 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
     } else {
       // 4. statistics as split-bf16 products on the bf16 MFMA (16x16x32): each
       //    fp32 operand v = hi + lo + d with hi = bf16(v), lo = bf16(v - hi),
-      //    |d| <= 2^-18 |v|, and a*b is taken as hi*hi + hi*lo + lo*hi (exact
-      //    products, fp32 accumulation): per product |error| <= 3 * 2^-18 |a b|
+      //    |d| <= 2^-16 |v|, and a*b is taken as hi*hi + hi*lo + lo*hi (exact
+      //    products, fp32 accumulation): per product |error| <= 3.0001 * 2^-16 |a b|
       //    before the accumulation's rounding. Block kb covers points
       //    32 kb + 8 g + t (t < 8) of lane (g, c): r of component c is the A
       //    operand, x or x^2 of feature 16 t2 + c the B operand.

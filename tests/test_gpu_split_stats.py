@@ -2,7 +2,7 @@
 
 With gmm_set_stats_precision(GMM_STATS_SPLIT_BF16) the fused kernels form
 Nk, Sx, Sxx from split-bf16 products on the bf16 matrix cores. Each product is
-off by at most 3 * 2^-18 of its magnitude, so the statistics must meet the same
+off by at most 3.0001 * 2^-16 of its magnitude, so the statistics must meet the same
 1e-4 bars against the float64 oracle, while l_n, L and the responsibilities
 (which do not go through that contraction) must be bitwise those of the
 default fp32 contraction.
