@@ -213,8 +213,11 @@ size_t gmm_border_lists_workspace_bytes(int64_t N, int32_t K);
  * gmm_kmeans_workspace_bytes(N, d, K) bytes, 256-byte aligned.
  *
  * gmm_kmeans_assign: assign[n] = argmin_k ||x_n - c_k||^2 (ties to the lower
- * index), computed from fp64 distances; dist2[n] (nullable) the minimum
- * squared distance as float; *inertia (nullable, device double) their sum. */
+ * index). fp32 matrix-core scores select, per row, every centre that the
+ * fp32 rounding bound cannot rule out; those get exact fp64 distances
+ * (difference form) and decide. dist2[n] (nullable) is the minimum squared
+ * distance rounded to float; *inertia (nullable, device double) the fp64 sum
+ * of the unrounded minima. */
 int gmm_kmeans_assign(const void* X, int32_t x_dtype, int64_t N, int32_t d, const float* C, int32_t K,
                       int32_t* assign, float* dist2, double* inertia,
                       void* workspace, size_t ws_bytes, void* stream);

@@ -31,9 +31,16 @@
 // fp64-MFMA pass, then recomputes the fp32 scores per 256-component slab and
 // accumulates the statistics. A small-K kernel (K <= 16, d <= 64) gives each
 // wave its own rows and keeps the whole mixture in registers.
+//
+// Lloyd's k-means assignment (Flash-KMeans articles) reuses the fp32 score
+// tile: with unit variances the highest score is the nearest centre, and the
+// fp32 error bound limits the exact fp64 distance check to the centres that
+// rounding could have put first.
 #include "gmm_device.hpp"
 #include "gmm_internal.hpp"
 
+#include <algorithm>
+#include <limits.h>
 #include <math.h>
 
 namespace gmm {
@@ -278,6 +285,89 @@ __global__ void errc_kernel(const float* __restrict__ compmax, int K, float* __r
   if (threadIdx.x < 4) errc[threadIdx.x] = s[threadIdx.x][0];
 }
 
+// Score tile of one wave: s_k(x) = sum_j (A_kj x_j^2 + B_kj x_j) + c_k for the
+// 64 rows of the LDS tile `xs` and the wave's 32 components (operands W from
+// the buffer resource `wrs`, constant `ck` of component c of this lane), on
+// two 32x32x2 fp32 MFMA accumulators (rows 0-31 and 32-63). The scores go to
+// the wave's 32 columns of the LDS score tile `sc` (row stride SCS); wave 0
+// also writes |x|^2 and |x|_1 of each row to `xq` (inputs of the error bound).
+template <int DT>
+__device__ __forceinline__ void score_tile(const float* xs, float* sc, float* xq, __amdgpu_buffer_rsrc_t wrs,
+                                           float ck, int wave, int lane, int SCS) {
+  constexpr int DP = 32 * DT, Q = DP / 4, XS = DP + 4;
+  const int h = lane >> 5, c = lane & 31;
+  auto wload = [&](int q) { return __builtin_amdgcn_raw_buffer_load_b128(wrs, (q * 64 + lane) * 16, 0, 0); };
+  v16f acc0, acc1;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    acc0[j] = 0.f;
+    acc1[j] = 0.f;
+  }
+  // Score operands (L2-resident) are prefetched two steps ahead in two
+  // register pairs that swap roles every two steps, so the loop needs no
+  // register rotation (which would wait for the loads in flight).
+  float sqab0 = 0.f, sqab1 = 0.f;  // error-bound inputs, summed alongside the MFMAs
+  auto xld = [&](int q, float4& x0, float4& x1) {
+    x0 = *reinterpret_cast<const float4*>(xs + c * XS + 4 * q);
+    x1 = *reinterpret_cast<const float4*>(xs + (c + 32) * XS + 4 * q);
+  };
+  auto step = [&](const float4& x0, const float4& x1, v4f w) {
+    const float xv0[4] = {x0.x, x0.y, x0.z, x0.w};
+    const float xv1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float a0 = h ? xv0[u] : xv0[u] * xv0[u];
+      const float a1 = h ? xv1[u] : xv1[u] * xv1[u];
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, w[u], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, w[u], acc1, 0, 0, 0);
+      sqab0 += fabsf(a0);  // h = 0: |x|^2, h = 1: |x|_1 of rows c and c + 32
+      sqab1 += fabsf(a1);
+    }
+  };
+  // The X operands of the next step are read from LDS before this step's
+  // MFMAs issue; the scheduling barriers keep every load where it is.
+  static_assert(Q % 4 == 0, "the score loop takes four steps at a time");
+  v4f wa = wload(0), wb = wload(1);
+  float4 pa0, pa1, pb0, pb1;
+  xld(0, pa0, pa1);
+#pragma unroll 1
+  for (int q = 0; q < Q; q += 4) {
+    const v4f wc = wload(q + 2), wd = wload(q + 3);
+    xld(q + 1, pb0, pb1);
+    __builtin_amdgcn_sched_barrier(0);
+    step(pa0, pa1, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    xld(q + 2, pa0, pa1);
+    __builtin_amdgcn_sched_barrier(0);
+    step(pb0, pb1, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    wa = wload(q + 4 < Q ? q + 4 : 0);
+    wb = wload(q + 5 < Q ? q + 5 : 1);
+    xld(q + 3, pb0, pb1);
+    __builtin_amdgcn_sched_barrier(0);
+    step(pa0, pa1, wc);
+    __builtin_amdgcn_sched_barrier(0);
+    xld(q + 4 < Q ? q + 4 : 0, pa0, pa1);
+    __builtin_amdgcn_sched_barrier(0);
+    step(pb0, pb1, wd);
+  }
+  // The store base goes through an empty asm so that the 32 store
+  // addresses are formed here, per tile, instead of being hoisted out of
+  // the tile loop and held (or spilled) across it.
+  int scb = 4 * h * SCS + wave * 32 + c;
+  asm volatile("" : "+v"(scb));
+  if (wave == 0) {
+    xq[2 * c + h] = sqab0;
+    xq[2 * (c + 32) + h] = sqab1;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = ((j >> 2) << 3) + (j & 3);  // acc_row(h, j) - 4 h
+    sc[scb + r * SCS] = acc0[j] + ck;
+    sc[scb + (r + 32) * SCS] = acc1[j] + ck;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Statistics kernel: single sweep (MODE 0) or the second pass (MODE 1)
 // ---------------------------------------------------------------------------
@@ -347,7 +437,6 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float4*>(W32p) + (size_t)(__builtin_amdgcn_readfirstlane(kw) >> 5) * Q * 64, (short)0,
       Q * 64 * 16, kBufferRsrcWord3);
-  auto wload = [&](int q) { return __builtin_amdgcn_raw_buffer_load_b128(wrs, (q * 64 + lane) * 16, 0, 0); };
   const float ck = c32[kw + c];
 
   // The next tile's X streams straight into the other LDS buffer (16-byte
@@ -366,77 +455,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     }
 
     // 2. scores
-    {
-      v16f acc0, acc1;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        acc0[j] = 0.f;
-        acc1[j] = 0.f;
-      }
-      // Score operands (L2-resident) are prefetched two steps ahead in two
-      // register pairs that swap roles every two steps, so the loop needs no
-      // register rotation (which would wait for the loads in flight).
-      float sqab0 = 0.f, sqab1 = 0.f;  // error-bound inputs, summed alongside the MFMAs
-      auto xld = [&](int q, float4& x0, float4& x1) {
-        x0 = *reinterpret_cast<const float4*>(xs + c * XS + 4 * q);
-        x1 = *reinterpret_cast<const float4*>(xs + (c + 32) * XS + 4 * q);
-      };
-      auto step = [&](const float4& x0, const float4& x1, v4f w) {
-        const float xv0[4] = {x0.x, x0.y, x0.z, x0.w};
-        const float xv1[4] = {x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float a0 = h ? xv0[u] : xv0[u] * xv0[u];
-          const float a1 = h ? xv1[u] : xv1[u] * xv1[u];
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, w[u], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, w[u], acc1, 0, 0, 0);
-          sqab0 += fabsf(a0);  // h = 0: |x|^2, h = 1: |x|_1 of rows c and c + 32
-          sqab1 += fabsf(a1);
-        }
-      };
-      // The X operands of the next step are read from LDS before this step's
-      // MFMAs issue; the scheduling barriers keep every load where it is.
-      static_assert(Q % 4 == 0, "the score loop takes four steps at a time");
-      v4f wa = wload(0), wb = wload(1);
-      float4 pa0, pa1, pb0, pb1;
-      xld(0, pa0, pa1);
-#pragma unroll 1
-      for (int q = 0; q < Q; q += 4) {
-        const v4f wc = wload(q + 2), wd = wload(q + 3);
-        xld(q + 1, pb0, pb1);
-        __builtin_amdgcn_sched_barrier(0);
-        step(pa0, pa1, wa);
-        __builtin_amdgcn_sched_barrier(0);
-        xld(q + 2, pa0, pa1);
-        __builtin_amdgcn_sched_barrier(0);
-        step(pb0, pb1, wb);
-        __builtin_amdgcn_sched_barrier(0);
-        wa = wload(q + 4 < Q ? q + 4 : 0);
-        wb = wload(q + 5 < Q ? q + 5 : 1);
-        xld(q + 3, pb0, pb1);
-        __builtin_amdgcn_sched_barrier(0);
-        step(pa0, pa1, wc);
-        __builtin_amdgcn_sched_barrier(0);
-        xld(q + 4 < Q ? q + 4 : 0, pa0, pa1);
-        __builtin_amdgcn_sched_barrier(0);
-        step(pb0, pb1, wd);
-      }
-      // The store base goes through an empty asm so that the 32 store
-      // addresses are formed here, per tile, instead of being hoisted out of
-      // the tile loop and held (or spilled) across it.
-      int scb = 4 * h * SCS + wave * 32 + c;
-      asm volatile("" : "+v"(scb));
-      if (wave == 0) {
-        xq[2 * c + h] = sqab0;
-        xq[2 * (c + 32) + h] = sqab1;
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = ((j >> 2) << 3) + (j & 3);  // acc_row(h, j) - 4 h
-        sc[scb + r * SCS] = acc0[j] + ck;
-        sc[scb + (r + 32) * SCS] = acc1[j] + ck;
-      }
-    }
+    score_tile<DT>(xs, sc, xq, wrs, ck, wave, lane, SCS);
     __syncthreads();
 
     // 3. row phase. The score tile holds s / ln 2 (operands and constants are
@@ -764,6 +783,240 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       for (int i = 0; i < nthr; ++i) s += lls[i];
       llpart[chunk] = s;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Nearest-centre assignment (Lloyd's k-means): fp32 scores, exact fp64 check
+// ---------------------------------------------------------------------------
+//
+// With unit variances and zero log-weights the mixture score of centre k is
+// s_k = -|x - c_k|^2 / 2 - (d/2) log 2 pi, so the nearest centre has the
+// highest score. A block walks the 64-point tiles of its row chunk and, per
+// tile, every slab of KS = 32 * waves centres (X stays in LDS across slabs):
+//   1. scores of the slab on the fp32 matrix cores (score_tile);
+//   2. per row (`waves` threads per row): every centre whose fp32 score is
+//      within twice the score error bound of the slab's best fp32 score may be
+//      the slab's nearest centre. Those candidates get |x - c_k|^2 exactly in
+//      fp64 (difference form, eight lanes per candidate) and the smallest
+//      wins, ties to the lower index;
+//   3. the slab's winner replaces the row's best so far only when strictly
+//      nearer, so across slabs ties also go to the lower index.
+// Outputs per row: the index and |x - c|^2 (rounded to fp32); per block the
+// fp64 sum of the exact |x - c|^2 (the inertia partial).
+template <int DT, typename XT>
+__global__ void __launch_bounds__(512)
+kmeans_assign_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int waves, int kslabs,
+                     int64_t rows_per_chunk, const float4* __restrict__ W32p, const float* __restrict__ c32,
+                     const float* __restrict__ mup, const float* __restrict__ errc, int32_t* __restrict__ assign,
+                     float* __restrict__ dist2, double* __restrict__ llpart, int vec) {
+  constexpr int DP = 32 * DT, Q = DP / 4, XS = DP + 4;
+  extern __shared__ __align__(16) float smem[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c = lane & 31;
+  const int nthr = blockDim.x;
+  const int KS = waves * 32, SCS = KS + 8;
+  const int64_t chunk = blockIdx.x;
+  float* xs = smem;                                      // [64][XS] X tile
+  float* sc = xs + 64 * XS;                              // [64][SCS] scores of one slab
+  float* xq = sc + 64 * SCS;                             // [64][2] |x|^2 and |x|_1 of the tile's rows
+  double* bestd = reinterpret_cast<double*>(xq + 128);   // [64] the row's nearest distance so far
+  double* lls = bestd + 64;                              // [nthr]
+  double* rd2 = lls + nthr;                              // [waves][kRefCap] exact candidate distances
+  int* bestk = reinterpret_cast<int*>(rd2 + waves * kRefCap);        // [64] and its centre
+  uint32_t* reflist = reinterpret_cast<uint32_t*>(bestk + 64);      // [waves][kRefCap]
+
+  const int tpr = waves;
+  const int prow = tid / tpr, psub = tid - prow * tpr;
+  const float a_max = errc[0], b_max = errc[1], c_max = errc[2], b2_max = errc[3];
+  // fp32 score error bound in natural units (as in the statistics kernel);
+  // the base-2 scores are off by at most log2(e) times that
+  const float gam = (float)(2 * DP + 4) * kUnitRound;
+  double ll_acc = 0.0;
+
+  const int64_t lo = chunk * rows_per_chunk;
+  const int64_t hi = min(N, lo + rows_per_chunk);
+  // fp32 rows: the next tile is fetched into registers (16-byte chunks
+  // tid + nthr * i) while the rows of this one are decided, and written to
+  // LDS once the tile is done; other inputs load at the end of the tile.
+  const int nch = 16 * DP / nthr;
+  const bool pref = vec && sizeof(XT) == 4 && nch <= 8 && nch * nthr == 16 * DP;
+  float4 xpre[8];
+  auto chunk_at = [&](int i, int& row, int& q) {
+    const int ch = tid + nthr * i;
+    row = ch / Q;
+    q = ch - row * Q;
+  };
+  load_x_tile<XS>(xs, X, lo, hi, d, DP, tid, nthr, vec);
+  for (int64_t r0 = lo; r0 < hi; r0 += 64) {
+    const int64_t rn = r0 + 64;
+    for (int slab = 0; slab < kslabs; ++slab) {
+      const int k0 = slab * KS, kw = k0 + wave * 32;
+      __syncthreads();  // the tile's X is in LDS; the previous slab is done with the score tile
+      const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float4*>(W32p) + (size_t)(__builtin_amdgcn_readfirstlane(kw) >> 5) * Q * 64, (short)0,
+          Q * 64 * 16, kBufferRsrcWord3);
+      score_tile<DT>(xs, sc, xq, wrs, c32[kw + c], wave, lane, SCS);
+      __syncthreads();
+      if (slab == 0 && pref && rn < hi) {
+        const float* Xf = reinterpret_cast<const float*>(X);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < nch) {
+            int row, q;
+            chunk_at(i, row, q);
+            const int64_t gr = rn + row;
+            xpre[i] = (gr < hi && 4 * q < d) ? *reinterpret_cast<const float4*>(Xf + gr * d + 4 * q)
+                                             : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+      }
+
+      const int row = prow;
+      const bool valid = r0 + row < hi;
+      const float sq = xq[2 * row], ab = xq[2 * row + 1];
+      const float Ebound = gam * (a_max * sq + fminf(b_max * ab, b2_max * sqrtf(sq))) + 2.f * kUnitRound * c_max;
+      const float4* srow4 = reinterpret_cast<const float4*>(sc + row * SCS);
+      float4 ev[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ev[i] = srow4[psub + tpr * i];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fmaxf(fmaxf(ev[i].x, ev[i].y), fmaxf(ev[i].z, ev[i].w)));
+      const float m = group_max(mx, tpr);
+      // Two base-2 scores, each off by at most log2(e) E < 1.45 E, can swap
+      // order only within 2.9 E; the subtraction's own rounding is covered by
+      // the last term. Padding centres score -inf and never qualify.
+      const float thr = m - (2.9f * Ebound + 4.f * kUnitRound * fabsf(m));
+      uint32_t mask = 0;
+      if (valid)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          mask |= (ev[i].x >= thr ? 1u : 0u) << (4 * i);
+          mask |= (ev[i].y >= thr ? 1u : 0u) << (4 * i + 1);
+          mask |= (ev[i].z >= thr ? 1u : 0u) << (4 * i + 2);
+          mask |= (ev[i].w >= thr ? 1u : 0u) << (4 * i + 3);
+        }
+      double bd = INFINITY;
+      int bk = INT_MAX;
+      {
+        const int cnt = __popc(mask);
+        const int incl = wave_incl_scan(cnt);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        const int base = incl - cnt;
+        uint32_t* wl = reflist + wave * kRefCap;
+        double* wd = rd2 + wave * kRefCap;
+        for (int p0 = 0; p0 < total; p0 += kRefCap) {
+          {
+            uint32_t m2 = mask;
+            int pos = base;
+            while (m2) {
+              const int i = __ffs(m2) - 1;
+              m2 &= m2 - 1u;
+              if (pos >= p0 && pos < p0 + kRefCap)
+                wl[pos - p0] = ((uint32_t)row << 16) | (uint32_t)(4 * (psub + tpr * (i >> 2)) + (i & 3));
+              ++pos;
+            }
+          }
+          wave_lds_sync();
+          const int n = min(total - p0, kRefCap);
+          // eight lanes per candidate, DP / 8 contiguous features each; all
+          // loads are issued before the arithmetic (inactive lanes read entry 0)
+          constexpr int FPL = DP / 8;
+          for (int e0 = 0; e0 < n; e0 += 8) {
+            const int e = e0 + (lane >> 3), sl = lane & 7;
+            const bool act = e < n;
+            const uint32_t ent = act ? wl[e] : 0u;
+            const int er = (int)(ent >> 16), kg = k0 + (int)(ent & 0xffffu);
+            const float4* xr = reinterpret_cast<const float4*>(xs + er * XS + sl * FPL);
+            const float4* mr = reinterpret_cast<const float4*>(mup + (size_t)kg * DP + sl * FPL);
+            float4 mv[FPL / 4];
+#pragma unroll
+            for (int i = 0; i < FPL / 4; ++i) mv[i] = mr[i];
+            __builtin_amdgcn_sched_barrier(0);
+            // features past d are skipped
+            double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+            for (int i = 0; i < FPL / 4; ++i) {
+              const float4 xv = xr[i];
+              const int f = sl * FPL + 4 * i;
+              const double t0 = f < d ? (double)xv.x - (double)mv[i].x : 0.0;
+              const double t1 = f + 1 < d ? (double)xv.y - (double)mv[i].y : 0.0;
+              const double t2 = f + 2 < d ? (double)xv.z - (double)mv[i].z : 0.0;
+              const double t3 = f + 3 < d ? (double)xv.w - (double)mv[i].w : 0.0;
+              a0 = fma(t0, t0, a0);
+              a1 = fma(t1, t1, a1);
+              a0 = fma(t2, t2, a0);
+              a1 = fma(t3, t3, a1);
+            }
+            double acc = a0 + a1;
+            acc += dpp_d<kDppXor1>(acc);
+            acc += dpp_d<kDppXor2>(acc);
+            acc += dpp_d<kDppHalfMirror>(acc);
+            if (act && sl == 0) wd[e] = acc;
+          }
+          wave_lds_sync();
+          // each thread takes the distances of its own candidates of this pass,
+          // in increasing centre order (a strict < keeps the lower index)
+          {
+            uint32_t m2 = mask;
+            int pos = base;
+            while (m2) {
+              const int i = __ffs(m2) - 1;
+              m2 &= m2 - 1u;
+              if (pos >= p0 && pos < p0 + kRefCap) {
+                const double dd = wd[pos - p0];
+                if (dd < bd) {
+                  bd = dd;
+                  bk = k0 + 4 * (psub + tpr * (i >> 2)) + (i & 3);
+                }
+              }
+              ++pos;
+            }
+          }
+          wave_lds_sync();
+        }
+      }
+      // the row's threads are `tpr` consecutive lanes of one wave
+      for (int o = 1; o < tpr; o <<= 1) {
+        const double od = __shfl_xor(bd, o, 64);
+        const int ok = __shfl_xor(bk, o, 64);
+        if (od < bd || (od == bd && ok < bk)) {
+          bd = od;
+          bk = ok;
+        }
+      }
+      if (psub == 0 && (slab == 0 || bd < bestd[row])) {
+        bestd[row] = bd;
+        bestk[row] = bk;
+      }
+    }
+    __syncthreads();
+    if (tid < 64 && r0 + tid < hi) {
+      const double b = bestd[tid];
+      const int k = bestk[tid];
+      assign[r0 + tid] = k < K ? k : -1;  // -1 only for a row with a NaN score
+      if (dist2) dist2[r0 + tid] = (float)b;  // optional output
+      ll_acc += b;
+    }
+    if (rn < hi) {
+      if (pref) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < nch) {
+            int row, q;
+            chunk_at(i, row, q);
+            *reinterpret_cast<float4*>(xs + row * XS + 4 * q) = xpre[i];
+          }
+      } else {
+        load_x_tile<XS>(xs, X, rn, hi, d, DP, tid, nthr, vec);
+      }
+    }
+  }
+  lls[tid] = ll_acc;
+  __syncthreads();
+  if (tid == 0) {
+    double s = 0.0;
+    for (int i = 0; i < nthr; ++i) s += lls[i];
+    llpart[chunk] = s;
   }
 }
 
@@ -1201,8 +1454,7 @@ __global__ void __launch_bounds__(256, 4)
 estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
                  const double* __restrict__ W64p, const double* __restrict__ c64e,
                  float2* __restrict__ rowref, float* __restrict__ ll_point, double* __restrict__ llpart,
-                 int32_t* __restrict__ tidx, float* __restrict__ tresp, int32_t* __restrict__ kassign,
-                 float* __restrict__ kdist2, double kconst) {
+                 int32_t* __restrict__ tidx, float* __restrict__ tresp) {
   constexpr int DP = 32 * DT, S = DP / 2, XS = DP + 1;
   __shared__ float xs[64 * XS];
   __shared__ double sm[kLseWaves][64], sz[kLseWaves][64], sv1[kLseWaves][64], sv2[kLseWaves][64];
@@ -1351,15 +1603,8 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
     }
     const double l = mm + log(zz);
     const int64_t gr = r0 + tid;
-    // nearest-centre mode (unit variances, zero log-weights): the top score is
-    // -dist^2 / 2 + const, so dist^2 = -2 * top + kconst; block sums of dist^2
-    // replace those of l
-    const double d2 = -2.0 * a1 + kconst;
-    sl[tid] = gr < N ? (kassign ? d2 : l) : 0.0;
-    if (gr < N && kassign) {
-      kassign[gr] = b1;
-      if (kdist2) kdist2[gr] = (float)d2;
-    } else if (gr < N) {
+    sl[tid] = gr < N ? l : 0.0;
+    if (gr < N) {
       // (m, lZ) in base 2 for the fp32 second pass
       const float mref = (float)(mm * kLog2E);
       if (rowref) rowref[gr] = make_float2(mref, (float)(l * kLog2E - (double)mref));
@@ -1572,19 +1817,18 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
 
 template <int DT, bool TOP2, typename XT>
 static hipError_t run_lse(const Plan& p, const XT* X, float* ll_point, int32_t* idx, float* resp,
-                          hipStream_t stream, int32_t* kassign = nullptr, float* kdist2 = nullptr,
-                          double kconst = 0.0) {
+                          hipStream_t stream) {
   const Workspace& w = p.ws;
   const int Kt = p.Kp16 / 16;
   if (Kt >= kLseWaves)
     estep_lse_kernel<DT, TOP2, XT, 4><<<(unsigned)p.tiles, 256, 0, stream>>>(
-        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp, kassign, kdist2, kconst);
+        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp);
   else if (Kt >= 2)
     estep_lse_kernel<DT, TOP2, XT, 2><<<(unsigned)p.tiles, 256, 0, stream>>>(
-        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp, kassign, kdist2, kconst);
+        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp);
   else
     estep_lse_kernel<DT, TOP2, XT, 1><<<(unsigned)p.tiles, 256, 0, stream>>>(
-        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp, kassign, kdist2, kconst);
+        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp);
   return hipGetLastError();
 }
 
@@ -1709,20 +1953,46 @@ hipError_t launch_top2(const Plan& p, const void* X, int x_dtype, int32_t* idx, 
   });
 }
 
+template <int DT, typename XT>
+static hipError_t run_kmeans_assign(const Plan& p, const XT* X, int32_t* assign, float* dist2, int64_t rows_per_chunk,
+                                    int64_t chunks, hipStream_t stream) {
+  const Workspace& w = p.ws;
+  const int nthr = p.waves * 64;
+  const int KS = p.waves * 32;
+  const size_t lds = (size_t)(64 * (32 * DT + 4) + 64 * (KS + 8) + 128) * sizeof(float) +
+                     (size_t)(64 + nthr + p.waves * kRefCap) * sizeof(double) + 64 * sizeof(int) +
+                     (size_t)p.waves * kRefCap * sizeof(uint32_t);
+  auto fn = kmeans_assign_kernel<DT, XT>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int vec = (sizeof(XT) == 4 && p.d % 4 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0) ? 1 : 0;
+  fn<<<(unsigned)chunks, nthr, lds, stream>>>(X, p.N, p.d, p.K, p.waves, p.kslabs, rows_per_chunk,
+                                              reinterpret_cast<const float4*>(w.W32p), w.c32, w.mup, w.errc,
+                                              assign, dist2, w.llpart, vec);
+  return hipGetLastError();
+}
+
 hipError_t launch_kmeans_assign(const Plan& p, const void* X, int x_dtype, int32_t* assign, float* dist2,
                                 double* inertia, hipStream_t stream) {
   if (p.N == 0) return hipSuccess;
-  const double kconst = -(double)p.d * kLog2Pi;  // the score's -d/2 log(2 pi), doubled
+  // One block walks every slab of its rows, so the row chunks are cut for
+  // one resident block per SIMD-set (8 waves per CU) over 256 CUs whatever
+  // the number of slabs. There are at most `tiles` chunks, which the
+  // workspace's per-chunk sums hold.
+  const int64_t target = std::max<int64_t>(1, std::min<int64_t>(256 * std::max(1, 8 / p.waves), p.tiles));
+  const int64_t rows_per_chunk = (p.tiles + target - 1) / target * 64;
+  const int64_t chunks = (p.N + rows_per_chunk - 1) / rows_per_chunk;
   hipError_t e = with_x_type(x_dtype, X, [&](auto x) {
     switch (p.DT) {
-      case 1: return run_lse<1, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst);
-      case 2: return run_lse<2, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst);
-      case 3: return run_lse<3, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst);
-      default: return run_lse<4, true>(p, x, nullptr, nullptr, nullptr, stream, assign, dist2, kconst);
+      case 1: return run_kmeans_assign<1>(p, x, assign, dist2, rows_per_chunk, chunks, stream);
+      case 2: return run_kmeans_assign<2>(p, x, assign, dist2, rows_per_chunk, chunks, stream);
+      case 3: return run_kmeans_assign<3>(p, x, assign, dist2, rows_per_chunk, chunks, stream);
+      default: return run_kmeans_assign<4>(p, x, assign, dist2, rows_per_chunk, chunks, stream);
     }
   });
   if (e == hipSuccess && inertia) {
-    reduce_ll_kernel<false><<<1, 256, 0, stream>>>(p.ws.llpart, p.tiles, inertia, 0);
+    reduce_ll_kernel<false><<<1, 256, 0, stream>>>(p.ws.llpart, chunks, inertia, 0);
     e = hipGetLastError();
   }
   return e;

@@ -1,10 +1,11 @@
 """GPU parity of Lloyd's k-means (gmm_kmeans_assign / _update / _iterate)
 against the float64 oracle.
 
-The assignment is an integer decided in fp64 on both sides (the kernel's fp64
-MFMA distances, the oracle's fp64 differences), so it must match exactly
-except at near-ties, whose gap is below the fp64 rounding of the distances;
-those rows are counted and excluded. Centres are fp64 means rounded to
+The assignment is an integer decided in fp64 on both sides (the kernel's exact
+fp64 distances of the candidates its fp32 scores cannot rule out, the
+oracle's fp64 differences), so it must match exactly except at near-ties,
+whose gap is below the fp64 rounding of the distances; those rows are counted
+and excluded. Centres are fp64 means rounded to
 float, checked to a few float ulps. Cases: each workload recipe at reduced N
 (fp16 X for the IVF recipe, K up to 4096), lists longer than one 1024-row
 segment, an empty cluster, and a device loop against the oracle loop.
@@ -47,7 +48,9 @@ def _check_assign(G, X, C, what):
     a, d2, inertia = G.kmeans_assign(dev(X), dev(C))
     torch.cuda.synchronize()
     ra, rd = oracle.kmeans_assign(X, C)
-    tie = _near_ties(X, C)
+    # a zero distance is exact on both sides, so duplicate centres at distance
+    # 0 must resolve to the same (lowest) index: no exclusion there
+    tie = _near_ties(X, C) & (rd != 0.0)
     ok = (host(a) == ra) | tie
     assert ok.all(), f"{what}: {(~ok).sum()} rows assigned differently"
     scale = np.maximum(rd, 1e-6 * (X.astype(np.float64) ** 2).sum(axis=1).max())
@@ -100,3 +103,61 @@ def test_kmeans_device_loop_matches_oracle_loop(G):
     assert np.all(np.diff(h) <= 1e-6 * h[:-1]), h
     np.testing.assert_allclose(h, rh, rtol=1e-6)
     np.testing.assert_allclose(host(Cg), rC, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("N,d,K", [(1, 1, 1), (65, 1, 2), (130, 33, 33), (1000, 17, 300), (97, 128, 257),
+                                   (300, 96, 64), (2100, 7, 513)])
+def test_kmeans_assign_shapes(G, N, d, K):
+    # ragged tiles, features not a multiple of 4 (scalar X loads), a partial
+    # last slab of centres, a single centre
+    X, mu, _, _ = datagen.random_problem(4000 + N + d + K, N, d, K)
+    _check_assign(G, X, mu, f"shape N={N} d={d} K={K}")
+
+
+def test_kmeans_assign_duplicate_centres_take_lower_index(G):
+    rng = np.random.default_rng(31)
+    X = rng.normal(0.0, 2.0, (3000, 40)).astype(np.float32)
+    C = rng.normal(0.0, 2.0, (300, 40)).astype(np.float32)
+    for dup in (7, 150, 299):  # in the first slab, a later slab, the last centre
+        C[dup] = C[3]
+    a, _, _ = G.kmeans_assign(dev(X), dev(C))
+    torch.cuda.synchronize()
+    a = host(a)
+    ra, _ = oracle.kmeans_assign(X, C)
+    assert not np.isin(a, [7, 150, 299]).any()
+    assert (ra == 3).sum() > 0
+    keep = np.ones(300, bool)
+    keep[[7, 150, 299]] = False
+    tie = _near_ties(X, C[keep])
+    assert ((a == ra) | tie).all()
+
+
+def test_kmeans_assign_many_candidates(G):
+    """Centres packed tightly far from the points: the fp32 scores cannot
+    separate most centres, so nearly every centre of every row is checked in
+    fp64 (candidate lists of several passes per wave)."""
+    rng = np.random.default_rng(32)
+    X = (rng.normal(0.0, 10.0, (400, 128)) + 20.0).astype(np.float32)
+    C = rng.normal(0.0, 1e-3, (256, 128)).astype(np.float32)
+    _check_assign(G, X, C, "tight centres")
+
+
+@pytest.mark.parametrize("name", ["ref", "smallk"])
+def test_kmeans_assign_full_size(G, name):
+    """The recipe at full size in the launch configuration the benchmark
+    times: 4000 sampled rows against the difference-form oracle, the inertia
+    against the oracle's fp64 matrix-product form over every row."""
+    X, mu, _, _ = datagen.make_workload(name)
+    a, d2, inertia = G.kmeans_assign(dev(X), dev(mu))
+    torch.cuda.synchronize()
+    a, d2 = host(a), host(d2)
+    idx = np.sort(np.random.default_rng(41).choice(X.shape[0], 4000, replace=False))
+    ra, rd = oracle.kmeans_assign(X[idx], mu)
+    tie = _near_ties(X[idx], mu) & (rd != 0.0)
+    assert ((a[idx] == ra) | tie).all(), f"{name}: {(~((a[idx] == ra) | tie)).sum()} sampled rows differ"
+    scale = np.maximum(rd, 1e-6 * (X[idx].astype(np.float64) ** 2).sum(axis=1).max())
+    assert np.all(np.abs(d2[idx] - rd) <= 1e-6 * scale), name
+    assert a.min() >= 0 and a.max() < mu.shape[0]
+    _, rall = oracle.kmeans_assign(X, mu, form="expanded", row_chunk=1 << 16)
+    assert abs(float(host(inertia)) - rall.sum()) <= 1e-9 * rall.sum(), name
+    print(f"{name} full size: inertia {float(host(inertia)):.9e} vs {rall.sum():.9e}", flush=True)
