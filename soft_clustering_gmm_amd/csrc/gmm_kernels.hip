@@ -731,13 +731,16 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
 #pragma unroll
         for (int t = 0; t < DT; ++t) xv[t] = xr[t];
       };
+      // A step whose 64 responsibilities (two points x the wave's 32
+      // components) are all exactly zero adds exactly zero: it is skipped.
       auto smfma = [&](float r, const float(&xv)[DT]) {
         nk += r;
+        if (__builtin_amdgcn_ballot_w64(r != 0.f))
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          SX[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(r, xv[t], SX[t], 0, 0, 0);
-          SXX[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(r, xv[t] * xv[t], SXX[t], 0, 0, 0);
-        }
+          for (int t = 0; t < DT; ++t) {
+            SX[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(r, xv[t], SX[t], 0, 0, 0);
+            SXX[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(r, xv[t] * xv[t], SXX[t], 0, 0, 0);
+          }
       };
       float ra, rb, xa[DT], xb[DT];
       sload(0, ra, xa);
