@@ -45,6 +45,7 @@
 
 namespace gmm {
 
+typedef float v32f __attribute__((ext_vector_type(32)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -379,9 +380,10 @@ __device__ __forceinline__ void score_tile(const float* xs, float* sc, float* xq
 //   3. row phase (`waves` threads per row): max, log-sum-exp (MODE 0) or the
 //      first pass's (m, lZ) (MODE 1), gated exact re-score; the tile then
 //      holds e = exp(s - m) and a per-row 1/z (MODE 0) or r itself (MODE 1)
-//   4. statistics: r (re-read in accumulator layout) is the A operand and
-//      [x | x^2] from the LDS tile the B operand of 32x32x2 MFMAs that
-//      accumulate Sx, Sxx for the wave's 32 components in registers.
+//   4. statistics, one point per step: r of the wave's 32 components is the
+//      A operand and x (block 0) or x^2 (block 1) the B operand of two-block
+//      32x32x1 MFMAs that accumulate Sx and Sxx in registers; a point whose
+//      32 responsibilities are all exactly zero is skipped.
 // At the end each block writes its statistics partial; a separate kernel
 // sums the partials in a fixed order (no atomics anywhere).
 template <int DT, int MODE, typename XT, bool SPLIT>
@@ -418,14 +420,21 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   //   sum_i |F_i W_i| <= a_max |x|^2 + min(b_max |x|_1, b2_max |x|_2).
   const float gam = (float)(2 * DP + 4) * kUnitRound;
 
+  // Statistics accumulators, feature block t: Sx and Sxx of component
+  // kw + acc_row(h, j), feature DT c + t at element j. The fp32 path keeps
+  // both in one two-block accumulator (Sx in elements 0-15, Sxx in 16-31).
   v16f SX[DT], SXX[DT];
+  v32f S2[DT];
 #pragma unroll
-  for (int t = 0; t < DT; ++t)
+  for (int t = 0; t < DT; ++t) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       SX[t][j] = 0.f;
       SXX[t][j] = 0.f;
     }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) S2[t][j] = 0.f;
+  }
   float nk = 0.f;
   double ll_acc = 0.0;
 
@@ -721,36 +730,36 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         }
       }
     } else {
-      // Step s takes point acc_row(h, s % 16) of row half s / 16. The operands
-      // of the next step are read from LDS before this step's MFMAs issue.
-      auto sload = [&](int s, float& r, float(&xv)[DT]) {
-        const int row = (s >> 4) * 32 + acc_row(h, s & 15);
-        r = sc[row * SCS + wave * 32 + c];
-        if (MODE == 0) r *= rv[2 * row + 1];  // e -> r = e / z (0 past the last row)
-        const float* xr = xs + row * XS + DT * c;
+      // One point per step on the two-block 32x32x1 MFMA: both halves of the
+      // wave hold r of component c of point p (the A operand of either block),
+      // lanes h = 0 hold x and lanes h = 1 hold x^2 of feature DT c + t (the B
+      // operands), so one instruction adds r x to block 0 (Sx) and r x^2 to
+      // block 1 (Sxx). A point whose 32 responsibilities for this wave are
+      // all exactly zero adds exactly zero and is skipped. The operands of
+      // the next point are read from LDS before this point's MFMAs issue.
+      auto sload = [&](int p, float& r, float(&xv)[DT]) {
+        r = sc[p * SCS + wave * 32 + c];
+        if (MODE == 0) r *= rv[2 * p + 1];  // e -> r = e / z (0 past the last row)
+        const float* xr = xs + p * XS + DT * c;
 #pragma unroll
         for (int t = 0; t < DT; ++t) xv[t] = xr[t];
       };
-      // A step whose 64 responsibilities (two points x the wave's 32
-      // components) are all exactly zero adds exactly zero: it is skipped.
       auto smfma = [&](float r, const float(&xv)[DT]) {
         nk += r;
         if (__builtin_amdgcn_ballot_w64(r != 0.f))
 #pragma unroll
-          for (int t = 0; t < DT; ++t) {
-            SX[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(r, xv[t], SX[t], 0, 0, 0);
-            SXX[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(r, xv[t] * xv[t], SXX[t], 0, 0, 0);
-          }
+          for (int t = 0; t < DT; ++t)
+            S2[t] = __builtin_amdgcn_mfma_f32_32x32x1f32(r, h ? xv[t] * xv[t] : xv[t], S2[t], 0, 0, 0);
       };
       float ra, rb, xa[DT], xb[DT];
       sload(0, ra, xa);
 #pragma unroll 1
-      for (int s = 0; s < 32; s += 2) {
-        sload(s + 1, rb, xb);
+      for (int p = 0; p < 64; p += 2) {
+        sload(p + 1, rb, xb);
         __builtin_amdgcn_sched_barrier(0);
         smfma(ra, xa);
         __builtin_amdgcn_sched_barrier(0);
-        sload(s + 2 < 32 ? s + 2 : 0, ra, xa);
+        sload(p + 2 < 64 ? p + 2 : 0, ra, xa);
         __builtin_amdgcn_sched_barrier(0);
         smfma(rb, xb);
       }
@@ -772,10 +781,11 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     for (int j = 0; j < 16; ++j) {
       const int comp = kw + acc_row(h, j);
       const int f = DT * c + t;
-      part[(size_t)comp * E + 1 + f] = SX[t][j];
-      part[(size_t)comp * E + 1 + DP + f] = SXX[t][j];
+      part[(size_t)comp * E + 1 + f] = SPLIT ? SX[t][j] : S2[t][j];
+      part[(size_t)comp * E + 1 + DP + f] = SPLIT ? SXX[t][j] : S2[t][16 + j];
     }
-  nk += __shfl_xor(nk, 32, 64);
+  // the split path's halves saw different points; the fp32 path's the same ones
+  if (SPLIT) nk += __shfl_xor(nk, 32, 64);
   if (h == 0) part[(size_t)(kw + c) * E] = nk;
 
   if (MODE == 0) {
