@@ -410,6 +410,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   float* xq = rv + 128;          // [64][2] |x|^2 and |x|_1 of the tile's rows
   double* lls = reinterpret_cast<double*>(xq + 128);  // [nthr]
   uint32_t* reflist = reinterpret_cast<uint32_t*>(lls + nthr);  // [waves][kRefCap]
+  uint32_t* nzrow = reflist + waves * kRefCap;  // [64]: bit w = row has a nonzero r for wave w
 
   const int tpr = waves;  // threads per row in the row phase
   const int prow = tid / tpr, psub = tid - prow * tpr;
@@ -522,6 +523,21 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           v.w = __builtin_amdgcn_exp2f((v.w - m) - lZ);
           srow4[psub + tpr * i] = v;
         }
+      }
+      // Which waves' component slices hold a nonzero e (or r) in this row.
+      // Entry chunk psub + tpr i belongs to wave (i * waves) / 8. An exact
+      // zero is never re-scored (every flag rule needs e > 0), so the bits
+      // are final; rows past the end take none (their r is zero).
+      if constexpr (!SPLIT) {
+        uint32_t nzb = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 v = ev[i];
+          const bool nz = (v.x != 0.f) | (v.y != 0.f) | (v.z != 0.f) | (v.w != 0.f);
+          nzb |= (nz ? 1u : 0u) << ((i * waves) >> 3);
+        }
+        for (int o = 1; o < tpr; o <<= 1) nzb |= (uint32_t)__shfl_xor((int)nzb, o, 64);
+        if (psub == 0) nzrow[row] = valid ? nzb : 0u;
       }
       // Which entries need the exact re-score (E = Ebound, r_k = e_k / z)?
       //  MODE 0: l_n comes from the same fp32 scores, so an unrefined entry is
@@ -734,34 +750,58 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       // wave hold r of component c of point p (the A operand of either block),
       // lanes h = 0 hold x and lanes h = 1 hold x^2 of feature DT c + t (the B
       // operands), so one instruction adds r x to block 0 (Sx) and r x^2 to
-      // block 1 (Sxx). A point whose 32 responsibilities for this wave are
-      // all exactly zero adds exactly zero and is skipped. The operands of
-      // the next point are read from LDS before this point's MFMAs issue.
-      auto sload = [&](int p, float& r, float(&xv)[DT]) {
-        r = sc[p * SCS + wave * 32 + c];
-        if (MODE == 0) r *= rv[2 * p + 1];  // e -> r = e / z (0 past the last row)
+      // block 1 (Sxx). Only the points with a nonzero r for this wave are
+      // visited (a zero r adds exactly zero); the operands of the next such
+      // point are read from LDS before this point's MFMAs issue.
+      // A point's operands are prepared (r = e / z, x or x^2) before the next
+      // point's LDS reads issue, so the wait for them never covers those.
+      auto sload = [&](int p, float& e, float& iz, float(&xv)[DT]) {
+        e = sc[p * SCS + wave * 32 + c];
+        iz = MODE == 0 ? rv[2 * p + 1] : 1.f;
         const float* xr = xs + p * XS + DT * c;
 #pragma unroll
         for (int t = 0; t < DT; ++t) xv[t] = xr[t];
       };
-      auto smfma = [&](float r, const float(&xv)[DT]) {
+      float r, bv[DT];
+      auto prep = [&](float e, float iz, const float(&xv)[DT]) {
+        r = MODE == 0 ? e * iz : e;  // e -> r = e / z
         nk += r;
-        if (__builtin_amdgcn_ballot_w64(r != 0.f))
 #pragma unroll
-          for (int t = 0; t < DT; ++t)
-            S2[t] = __builtin_amdgcn_mfma_f32_32x32x1f32(r, h ? xv[t] * xv[t] : xv[t], S2[t], 0, 0, 0);
+        for (int t = 0; t < DT; ++t) bv[t] = h ? xv[t] * xv[t] : xv[t];
       };
-      float ra, rb, xa[DT], xb[DT];
-      sload(0, ra, xa);
+      auto smfma = [&]() {
+#pragma unroll
+        for (int t = 0; t < DT; ++t) S2[t] = __builtin_amdgcn_mfma_f32_32x32x1f32(r, bv[t], S2[t], 0, 0, 0);
+      };
+      // Active points in increasing order, two per iteration (no register
+      // rotation). An odd count is padded with the lowest inactive point,
+      // whose r is exactly zero; past the end the loads read point 0, unused.
+      uint64_t am = __builtin_amdgcn_ballot_w64((nzrow[lane] >> wave) & 1u);
+      const int na = __builtin_popcountll(am);
+      if (na & 1) am |= ~am & (am + 1);
+      auto pop = [&]() {
+        const int p = am ? __builtin_ctzll(am) : 0;
+        am &= am - 1;
+        return p;
+      };
+      if (na) {
+        float ea, ia, xa[DT], eb, ib, xb[DT];
+        sload(pop(), ea, ia, xa);
 #pragma unroll 1
-      for (int p = 0; p < 64; p += 2) {
-        sload(p + 1, rb, xb);
-        __builtin_amdgcn_sched_barrier(0);
-        smfma(ra, xa);
-        __builtin_amdgcn_sched_barrier(0);
-        sload(p + 2 < 64 ? p + 2 : 0, ra, xa);
-        __builtin_amdgcn_sched_barrier(0);
-        smfma(rb, xb);
+        for (int k = 0; k < na; k += 2) {
+          prep(ea, ia, xa);
+          __builtin_amdgcn_sched_barrier(0);
+          sload(pop(), eb, ib, xb);
+          __builtin_amdgcn_sched_barrier(0);
+          smfma();
+          __builtin_amdgcn_sched_barrier(0);
+          prep(eb, ib, xb);
+          __builtin_amdgcn_sched_barrier(0);
+          sload(pop(), ea, ia, xa);
+          __builtin_amdgcn_sched_barrier(0);
+          smfma();
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     if (rn < hi && !async_x) load_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, X, rn, hi, d, DP, tid, nthr, vec);
@@ -1815,7 +1855,7 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
   const int nthr = p.waves * 64;
   const int KS = p.waves * 32;
   const size_t lds = (size_t)(2 * 64 * (32 * DT + 4) + 64 * (KS + 8) + 256) * sizeof(float) +
-                     (size_t)nthr * sizeof(double) + (size_t)p.waves * kRefCap * sizeof(uint32_t);
+                     (size_t)nthr * sizeof(double) + (size_t)(p.waves * kRefCap + 64) * sizeof(uint32_t);
   auto fn = p.stats_split ? estep_stats_kernel<DT, MODE, XT, true> : estep_stats_kernel<DT, MODE, XT, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
