@@ -300,6 +300,10 @@ def main(argv=None):
         "hbm_algorithmic_bytes_per_launch": xbytes,
         "hbm_achieved_GBps": round(xbytes / (k_avg * 1e-3) / 1e9, 1),
         "hbm_frac": round(xbytes / (k_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "credit": ("dense 8NKd flops; the fp32 statistics loop skips points whose responsibilities for a "
+                   "wave's 32 components are all exactly zero (exact, data-dependent), so executed "
+                   "matrix-core work can be below the credited flops" if not small and sp == "false"
+                   else "dense 8NKd flops, all executed"),
     }
     out = {
         "metric": METRIC, "value": N * K / (ms_step * 1e-3), "unit": UNIT, "n_gpus": 1,

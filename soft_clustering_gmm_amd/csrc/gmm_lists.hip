@@ -409,14 +409,18 @@ __global__ void kmeans_segcount_kernel(const int64_t* __restrict__ offsets, int 
 }
 
 // Block b sums segment b: rows members[start, end) of list k, where k is the
-// last list whose first segment is <= b. Wave w takes rows start + w + 4i in
-// groups of 8 (their loads in flight together); lanes hold features lane and
-// lane + 64 in fp64; the four waves are combined in order.
+// last list whose first segment is <= b. Fixed orders throughout.
+//  - fp32 rows with d % 4 == 0 (16-byte aligned): a row takes LPR lanes (the
+//    power of two >= d/4) with four features each, so a wave reads 64 / LPR
+//    rows per load and eight loads per lane are in flight; the row groups are
+//    combined by an xor butterfly, then the four waves in order.
+//  - otherwise: lanes hold features lane and lane + 64, wave w takes rows
+//    start + w + 4i in groups of 8.
 template <typename XT>
 __global__ void __launch_bounds__(256)
 kmeans_segsum_kernel(const XT* __restrict__ X, int d, const int64_t* __restrict__ offsets,
                      const int32_t* __restrict__ members, const int64_t* __restrict__ segoff, int K,
-                     double* __restrict__ part) {
+                     double* __restrict__ part, int vec) {
   __shared__ double s[4][128];
   const int64_t b = blockIdx.x;
   if (b >= segoff[K]) return;
@@ -432,44 +436,102 @@ kmeans_segsum_kernel(const XT* __restrict__ X, int d, const int64_t* __restrict_
   const int64_t start = offsets[k] + (b - segoff[k]) * kSegRows;
   const int64_t end = min(start + kSegRows, offsets[k + 1]);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int f0 = lane, f1 = lane + 64;
-  double a0 = 0.0, a1 = 0.0;
   constexpr int G = 8;
-  for (int64_t i0 = start + wave; i0 < end; i0 += 4 * G) {
-    float v0[G], v1[G];
+  if (sizeof(XT) == 4 && vec) {
+    int LPR = 1;
+    while (4 * LPR < d) LPR <<= 1;
+    const int RPW = 64 / LPR, rsub = lane / LPR, q = lane - rsub * LPR;
+    const bool fin = 4 * q < d;
+    const float* Xf = reinterpret_cast<const float*>(X);
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    for (int64_t i0 = start + wave * RPW + rsub; i0 < end; i0 += 4 * RPW * G) {
+      float4 v[G];
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const int64_t i = i0 + 4 * j;
-      const bool in = i < end;
-      const XT* row = X + (int64_t)(in ? members[i] : 0) * d;
-      v0[j] = in && f0 < d ? (float)row[f0] : 0.f;
-      v1[j] = in && f1 < d ? (float)row[f1] : 0.f;
-    }
+      for (int j = 0; j < G; ++j) {
+        const int64_t i = i0 + 4 * RPW * j;
+        v[j] = (i < end && fin) ? *reinterpret_cast<const float4*>(Xf + (int64_t)members[i] * d + 4 * q)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      a0 += (double)v0[j];
-      a1 += (double)v1[j];
+      for (int j = 0; j < G; ++j) {
+        a0 += (double)v[j].x;
+        a1 += (double)v[j].y;
+        a2 += (double)v[j].z;
+        a3 += (double)v[j].w;
+      }
     }
+    for (int o = LPR; o < 64; o <<= 1) {
+      a0 += __shfl_xor(a0, o, 64);
+      a1 += __shfl_xor(a1, o, 64);
+      a2 += __shfl_xor(a2, o, 64);
+      a3 += __shfl_xor(a3, o, 64);
+    }
+    if (rsub == 0 && fin) {
+      s[wave][4 * q] = a0;
+      s[wave][4 * q + 1] = a1;
+      s[wave][4 * q + 2] = a2;
+      s[wave][4 * q + 3] = a3;
+    }
+  } else {
+    const int f0 = lane, f1 = lane + 64;
+    double a0 = 0.0, a1 = 0.0;
+    for (int64_t i0 = start + wave; i0 < end; i0 += 4 * G) {
+      float v0[G], v1[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int64_t i = i0 + 4 * j;
+        const bool in = i < end;
+        const XT* row = X + (int64_t)(in ? members[i] : 0) * d;
+        v0[j] = in && f0 < d ? (float)row[f0] : 0.f;
+        v1[j] = in && f1 < d ? (float)row[f1] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        a0 += (double)v0[j];
+        a1 += (double)v1[j];
+      }
+    }
+    s[wave][f0] = a0;
+    s[wave][f1] = a1;
   }
-  s[wave][f0] = a0;
-  s[wave][f1] = a1;
   __syncthreads();
   if (threadIdx.x < d)
     part[b * d + threadIdx.x] = (s[0][threadIdx.x] + s[1][threadIdx.x]) + (s[2][threadIdx.x] + s[3][threadIdx.x]);
 }
 
-__global__ void kmeans_finalize_kernel(const double* __restrict__ part, const int64_t* __restrict__ segoff,
-                                       const int64_t* __restrict__ offsets, int K, int d, float* __restrict__ C,
-                                       int64_t* __restrict__ counts) {
-  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (t >= (int64_t)K * d) return;
-  const int k = (int)(t / d), j = (int)(t - (int64_t)k * d);
+// One block per list: lanes take features (64 at a time), wave w the
+// segments congruent to w mod 4 with eight independent sums per lane (their
+// loads in flight together); the sums and then the waves combine in a fixed
+// order. The centre becomes sum / count; a list with no members keeps it.
+__global__ void __launch_bounds__(256)
+kmeans_finalize_kernel(const double* __restrict__ part, const int64_t* __restrict__ segoff,
+                       const int64_t* __restrict__ offsets, int K, int d, float* __restrict__ C,
+                       int64_t* __restrict__ counts) {
+  __shared__ double s[4][64];
+  const int k = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t L = offsets[k + 1] - offsets[k];
-  if (j == 0 && counts) counts[k] = L;
-  if (L == 0) return;
-  double a = 0.0;
-  for (int64_t g = segoff[k]; g < segoff[k + 1]; ++g) a += part[g * d + j];
-  C[t] = (float)(a / (double)L);
+  if (threadIdx.x == 0 && counts) counts[k] = L;
+  if (L == 0) return;  // the whole block: the centre keeps its value
+  const int64_t g0 = segoff[k], g1 = segoff[k + 1];
+  for (int j0 = 0; j0 < d; j0 += 64) {
+    const int j = j0 + lane;
+    double a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = 0.0;
+    for (int64_t g = g0 + wave; g < g1; g += 32) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t gg = g + 4 * u;
+        if (gg < g1 && j < d) a[u] += part[gg * d + j];
+      }
+    }
+    s[wave][lane] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    __syncthreads();
+    if (wave == 0 && j < d)
+      C[(int64_t)k * d + j] = (float)(((s[0][lane] + s[1][lane]) + (s[2][lane] + s[3][lane])) / (double)L);
+    __syncthreads();
+  }
 }
 
 int64_t kmeans_max_segments(int64_t N, int K) { return (N + kSegRows - 1) / kSegRows + K; }
@@ -483,12 +545,13 @@ hipError_t launch_kmeans_update(const void* X, int x_dtype, int d, int K, const 
   if (e != hipSuccess) return e;
   e = with_x_type(x_dtype, X, [&](auto x) {
     using XT = std::remove_cv_t<std::remove_pointer_t<decltype(x)>>;
-    kmeans_segsum_kernel<XT><<<(unsigned)max_segments, 256, 0, stream>>>(x, d, offsets, members, segoff, K, part);
+    const int vec = (sizeof(XT) == 4 && d % 4 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0) ? 1 : 0;
+    kmeans_segsum_kernel<XT><<<(unsigned)max_segments, 256, 0, stream>>>(x, d, offsets, members, segoff, K, part,
+                                                                          vec);
     return hipGetLastError();
   });
   if (e != hipSuccess) return e;
-  const int64_t n = (int64_t)K * d;
-  kmeans_finalize_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(part, segoff, offsets, K, d, C, counts);
+  kmeans_finalize_kernel<<<(unsigned)K, 256, 0, stream>>>(part, segoff, offsets, K, d, C, counts);
   return hipGetLastError();
 }
 
