@@ -971,11 +971,13 @@ kmeans_assign_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int wave
           }
           wave_lds_sync();
           const int n = min(total - p0, kRefCap);
-          // eight lanes per candidate, DP / 8 contiguous features each; all
-          // loads are issued before the arithmetic (inactive lanes read entry 0)
-          constexpr int FPL = DP / 8;
-          for (int e0 = 0; e0 < n; e0 += 8) {
-            const int e = e0 + (lane >> 3), sl = lane & 7;
+          // LPE lanes per candidate (16 or 12 contiguous features each), so
+          // that short rows take few passes; all loads are issued before the
+          // arithmetic (inactive lanes read entry 0)
+          constexpr int LPE = DT == 1 ? 2 : DT == 2 ? 4 : 8, FPL = DP / LPE, EPP = 64 / LPE;
+          static_assert(FPL % 4 == 0, "float4 pieces");
+          for (int e0 = 0; e0 < n; e0 += EPP) {
+            const int e = e0 + lane / LPE, sl = lane % LPE;
             const bool act = e < n;
             const uint32_t ent = act ? wl[e] : 0u;
             const int er = (int)(ent >> 16), kg = k0 + (int)(ent & 0xffffu);
@@ -1002,8 +1004,8 @@ kmeans_assign_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int wave
             }
             double acc = a0 + a1;
             acc += dpp_d<kDppXor1>(acc);
-            acc += dpp_d<kDppXor2>(acc);
-            acc += dpp_d<kDppHalfMirror>(acc);
+            if (LPE >= 4) acc += dpp_d<kDppXor2>(acc);
+            if (LPE >= 8) acc += dpp_d<kDppHalfMirror>(acc);
             if (act && sl == 0) wd[e] = acc;
           }
           wave_lds_sync();
