@@ -5,8 +5,11 @@ relative, responsibilities 1e-5 absolute, Nk/Sx/Sxx 1e-4 relative. Where a
 pure relative error is ill-posed the reading is:
   l_n : |dl| <= 1e-4 * max(|l|, 1)
   Nk  : |dNk| <= 1e-4 * max(Nk, 1)
-  Sx  : per component, max_j |dSx_kj| <= 1e-4 * max_j sum_n r_nk |x_nj|   (Sx sums signed values)
-  Sxx : per component, max_j |dSxx_kj| <= 1e-4 * max_j Sxx_kj
+  Sx  : per component, max_j |dSx_kj| <= 1e-4 * f_k * max_j sum_n r_nk |x_nj|   (Sx sums signed values)
+  Sxx : per component, max_j |dSxx_kj| <= 1e-4 * f_k * max_j Sxx_kj
+        with f_k = max(Nk, 1) / Nk: as for Nk, a component holding less than one
+        point's worth of responsibility is measured against one point's worth
+        (its responsibilities are each exact to an absolute, not relative, bound)
   L   : |dL| <= 1e-4 * sum_n max(|l_n|, 1)
 """
 from __future__ import annotations
@@ -37,11 +40,12 @@ def check_stats(gpu, ref, X, R_absx=None, what=""):
     Nk, Sx, Sxx = (np.asarray(a, np.float64) for a in gpu)
     eN = np.abs(Nk - ref["Nk"]) / np.maximum(ref["Nk"], 1.0)
     assert eN.max() <= S_TOL, f"{what}: Nk rel err {eN.max():.3e} at k={eN.argmax()}"
-    scale_x = np.maximum(R_absx.max(axis=1), 1e-30)
+    f = np.maximum(ref["Nk"], 1.0) / np.maximum(ref["Nk"], 1e-300)
+    scale_x = np.maximum(R_absx.max(axis=1) * f, 1e-30)
     eX = np.abs(Sx - ref["Sx"]).max(axis=1) / scale_x
     eX = np.where(ref["Nk"] > 0, eX, 0.0)
     assert eX.max() <= S_TOL, f"{what}: Sx normwise err {eX.max():.3e} at k={eX.argmax()}"
-    scale_xx = np.maximum(ref["Sxx"].max(axis=1), 1e-30)
+    scale_xx = np.maximum(ref["Sxx"].max(axis=1) * f, 1e-30)
     eXX = np.abs(Sxx - ref["Sxx"]).max(axis=1) / scale_xx
     eXX = np.where(ref["Nk"] > 0, eXX, 0.0)
     assert eXX.max() <= S_TOL, f"{what}: Sxx normwise err {eXX.max():.3e} at k={eXX.argmax()}"
