@@ -63,6 +63,11 @@ constexpr float kGateTau = 5e-7f;
 // Per-operation relative error assumed for fp32 arithmetic in the bound below:
 // 2^-23, which also covers an accumulator that truncates rather than rounds.
 constexpr float kUnitRound = 1.1920928955078125e-7f;
+// The error bound's inputs (|x|^2 and |x|_1 of a row, summed in fp32 over at
+// most 2 * 128 nonnegative terms) and its own fp32 evaluation are each off by
+// less than 300 u relative; this factor (> 1 + 2000 u) keeps the computed
+// bound an upper bound.
+constexpr float kBoundSlack = 1.0005f;
 constexpr int kRefCap = 128;       // re-score list entries per wave and pass
 // Word 3 of a raw buffer resource on CDNA (32-bit data format, no swizzle):
 // loads at offsets past the record count return zero.
@@ -419,7 +424,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   // zero, then c is added once, so
   //   |s32 - s| <= (2*DP + 4) u sum_i |F_i W_i| + 2 u |c|,
   //   sum_i |F_i W_i| <= a_max |x|^2 + min(b_max |x|_1, b2_max |x|_2).
-  const float gam = (float)(2 * DP + 4) * kUnitRound;
+  const float gam = (float)(2 * DP + 4) * kUnitRound * kBoundSlack;
 
   // Statistics accumulators, feature block t: Sx and Sxx of component
   // kw + acc_row(h, j), feature DT c + t at element j. The fp32 path keeps
@@ -883,7 +888,7 @@ kmeans_assign_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int wave
   const float a_max = errc[0], b_max = errc[1], c_max = errc[2], b2_max = errc[3];
   // fp32 score error bound in natural units (as in the statistics kernel);
   // the base-2 scores are off by at most log2(e) times that
-  const float gam = (float)(2 * DP + 4) * kUnitRound;
+  const float gam = (float)(2 * DP + 4) * kUnitRound * kBoundSlack;
   double ll_acc = 0.0;
 
   const int64_t lo = chunk * rows_per_chunk;
@@ -1165,7 +1170,7 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
 #pragma unroll
   for (int k = 0; k < 16; ++k) cks[k] = (float)(c64e[k] * kLog2E);
   const float a_max = errc[0], c_max = errc[2], b2_max = errc[3];
-  const float gam = (float)(2 * DP + 4) * kUnitRound;
+  const float gam = (float)(2 * DP + 4) * kUnitRound * kBoundSlack;
 
   v4f SX[DS], SXX[DS];
 #pragma unroll
@@ -1226,10 +1231,15 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
     // MFMAs is preferred while the other wave of the SIMD does VALU work.
     __builtin_amdgcn_s_setprio(1);
     // 2. scores, 16-point block b: lane (g, c) supplies point 16b + c,
-    //    feature g*(DP/4) + s/2; accumulator slot j = point 16b+4g+j
+    //    feature g*(DP/4) + s/2; accumulator slot j = point 16b+4g+j. The
+    //    squares the MFMAs consume are also summed: after the sum over the
+    //    four lanes g of a point, lane (g = b, c) keeps |x|^2 of point
+    //    16b + c, the point it takes in the row phase.
+    float sq = 0.f;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       v4f acc = {0.f, 0.f, 0.f, 0.f};
+      float sqb = 0.f;
       const float* xrow = xs + (16 * b + c) * XS + g * (DP / 4);
 #pragma unroll
       for (int q = 0; q < DP / 16; ++q) {
@@ -1237,10 +1247,15 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
         const float xv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[u] * xv[u], w[8 * q + 2 * u], acc, 0, 0, 0);
+          const float x2 = xv[u] * xv[u];
+          sqb += x2;
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x2, w[8 * q + 2 * u], acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[u], w[8 * q + 2 * u + 1], acc, 0, 0, 0);
         }
       }
+      sqb += __shfl_xor(sqb, 16, 64);
+      sqb += __shfl_xor(sqb, 32, 64);
+      if (g == b) sq = sqb;
 #pragma unroll
       for (int j = 0; j < 4; ++j) sc[(16 * b + 4 * g + j) * SS + c] = acc[j];
     }
@@ -1270,13 +1285,8 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
         e[k] = __builtin_amdgcn_exp2f(e[k] - m);
         z += e[k];
       }
-      float sq = 0.f;
-      const float* xr = xs + p * XS;
-#pragma unroll
-      for (int q = 0; q < DP / 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(xr + 4 * q);
-        sq += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-      }
+      // sq = |x|^2 of point p, from the score loop (its fp32 sum order differs
+      // from a row-wise sum by rounding only, which the bound's factor covers)
       // re-score rule of the single sweep (see the main kernel): refine entries
       // with 2 E r (1 - r) > tau; widen to the e >= kExpWindow window if the unrefined
       // mass could still move the refined ones by more than tau.
