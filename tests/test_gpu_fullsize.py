@@ -10,6 +10,8 @@ is checked by
   * properties that hold at any size: sum_k Nk = N, L = sum_n l_n, and
     additivity of Nk/Sx/Sxx over a split of the rows (to the statistics'
     1e-4 bar: the two runs accumulate different row sets in fp32).
+An X of more than 2^31 elements (17M x 128) checks the 64-bit offsets the
+same way, with the halves below element 2^31.
 """
 import numpy as np
 import pytest
@@ -160,3 +162,46 @@ def test_kmeans_full_size_ref(G):
     err = np.abs(host(C).astype(np.float64) - rC) / np.maximum(np.abs(rC), 1e-3)
     assert err.max() <= 3e-7, err.max()
     print(f"kmeans full size: {diff.size} near-tie rows, {int((rn == 0).sum())} empty clusters", flush=True)
+
+
+def _beyond_2_31():
+    """17,000,000 x 128 fp32 rows (N d = 2.18e9 > 2^31 elements, 8.7 GB) from 64 blobs."""
+    N, d, K = 17_000_000, 128, 64
+    rng = np.random.default_rng(2031)
+    C = rng.normal(0.0, 2.0, (K, d)).astype(np.float32)
+    X = np.empty((N, d), np.float32)
+    for lo in range(0, N, 1 << 20):
+        hi = min(N, lo + (1 << 20))
+        X[lo:hi] = C[rng.integers(0, K, hi - lo)] + rng.standard_normal((hi - lo, d), dtype=np.float32)
+    mu = (C + rng.normal(0.0, 0.3, C.shape)).astype(np.float32)
+    var = rng.uniform(0.8, 1.5, (K, d)).astype(np.float32)
+    logw = np.full(K, -np.log(K), np.float32)
+    return X, mu, var, logw
+
+
+def test_x_beyond_2_31_elements(G):
+    """Every offset into X past element 2^31 must be formed in 64 bits. l_n of
+    rows sampled mostly past that element (and the last row) and their
+    nearest-centre assignment against the oracle; the statistics of all rows
+    against the sum of the two halves' (each half lies below element 2^31, so
+    a row read from a wrong offset would break the additivity), sum Nk = N and
+    L = sum l_n."""
+    X, mu, var, logw = _beyond_2_31()
+    N, d = X.shape
+    assert N * d > 2 ** 31 and (N // 2 + 37) * d < 2 ** 31
+    Xd = dev(X)
+    full = G.estep_stats(Xd, dev(mu), dev(var), dev(logw), want_point_loglik=True)
+    a, d2, _ = G.kmeans_assign(Xd, dev(mu))
+    torch.cuda.synchronize()
+    del Xd
+    first = 2 ** 31 // d + 1  # the first row that lies wholly past element 2^31
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([rng.choice(first, 64, replace=False),
+                                     first + rng.choice(N - first, 448, replace=False), [first - 1, N - 1]]))
+    l_ref, _ = oracle.estep_rows(X, mu, var, logw, rows)
+    parity.check_loglik_point(host(full[4])[rows], l_ref, "beyond 2^31: sampled l_n")
+    ra, rd = oracle.kmeans_assign(X[rows], mu)
+    assert np.array_equal(host(a)[rows], ra), "beyond 2^31: sampled assignment"
+    assert np.all(np.abs(host(d2)[rows] - rd) <= 1e-6 * np.maximum(rd, 1.0)), "beyond 2^31: sampled dist2"
+    _properties(G, "beyond 2^31", X, mu, var, logw, full)
+    print(f"beyond 2^31 (N={N}, d={d}): sampled rows and additivity ok", flush=True)
