@@ -9,9 +9,10 @@
 // Score contraction. With A_kj = -1/(2 var_kj), B_kj = mu_kj/var_kj and
 // c_k = log w_k - 1/2 (d log 2pi + sum_j log var_kj + sum_j mu_kj^2/var_kj),
 //     s_nk = sum_j (A_kj x_nj^2 + B_kj x_nj) + c_k,
-// a dense (N x 2d) . (2d x K) product that runs on MFMA tiles. The inner
-// dimension interleaves x^2 and x feature by feature, so one LDS read of x
-// feeds both halves of an MFMA step.
+// a dense (N x 2d) . (2d x K) product that runs on MFMA tiles. The 32x32
+// fp32 tiles pair two features in an MFMA step (the x^2 steps of a feature
+// block, then its x steps), so each lane squares only the x values it holds;
+// the 16x16 tiles interleave x^2 and x of one feature per step.
 //
 // Precision. FP32 accumulation of the expanded form loses ~1e-4 absolute on
 // scores of magnitude ~10^2, which is too coarse for responsibilities near
@@ -261,10 +262,13 @@ __global__ void pack_kernel(const float* __restrict__ mu, const float* __restric
   mup[t] = m;
   ivp[t] = iv;
   {
-    const int kt = k >> 5, c = k & 31, q = f >> 2, u = f & 3, Q = DP >> 2;
-    const size_t base = (((size_t)kt * Q + q) * 64 + c) * 4 + u;
-    W32p[base] = (float)(A * kLog2E);  // base-2 scaled, like c32
-    W32p[base + 32 * 4] = (float)(B * kLog2E);
+    // fp32 score operands, base-2 scaled like c32: lane (h, c) of feature
+    // block q (features 4q..4q+3) holds A of features 4q + 2h + {0, 1} in
+    // slots 0-1 (the x^2 steps) and their B in slots 2-3 (the x steps)
+    const int kt = k >> 5, c = k & 31, q = f >> 2, h = (f >> 1) & 1, u = f & 1, Q = DP >> 2;
+    const size_t base = (((size_t)kt * Q + q) * 64 + 32 * h + c) * 4 + u;
+    W32p[base] = (float)(A * kLog2E);
+    W32p[base + 2] = (float)(B * kLog2E);
   }
   if (k < Kp16) {
     const int kt = k >> 4, c = k & 15, s = f >> 1, S = DP >> 1, g0 = 2 * (f & 1);
@@ -312,29 +316,34 @@ __device__ __forceinline__ void score_tile(const float* xs, float* sc, float* xq
   // Score operands (L2-resident) are prefetched two steps ahead in two
   // register pairs that swap roles every two steps, so the loop needs no
   // register rotation (which would wait for the loads in flight).
-  float sqab0 = 0.f, sqab1 = 0.f;  // error-bound inputs, summed alongside the MFMAs
-  auto xld = [&](int q, float4& x0, float4& x1) {
-    x0 = *reinterpret_cast<const float4*>(xs + c * XS + 4 * q);
-    x1 = *reinterpret_cast<const float4*>(xs + (c + 32) * XS + 4 * q);
+  // Feature block q takes four MFMAs per row half: the two k slots of the
+  // 32x32x2 MFMA are features 4q + 2h + u of lanes h = 0 and h = 1, first as
+  // x^2 (u = 0, 1), then as x; each lane squares only its own two features.
+  float sq0 = 0.f, sq1 = 0.f, ab0 = 0.f, ab1 = 0.f;  // error-bound inputs over this lane's features
+  auto xld = [&](int q, float2& x0, float2& x1) {
+    x0 = *reinterpret_cast<const float2*>(xs + c * XS + 4 * q + 2 * h);
+    x1 = *reinterpret_cast<const float2*>(xs + (c + 32) * XS + 4 * q + 2 * h);
   };
-  auto step = [&](const float4& x0, const float4& x1, v4f w) {
-    const float xv0[4] = {x0.x, x0.y, x0.z, x0.w};
-    const float xv1[4] = {x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float a0 = h ? xv0[u] : xv0[u] * xv0[u];
-      const float a1 = h ? xv1[u] : xv1[u] * xv1[u];
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, w[u], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, w[u], acc1, 0, 0, 0);
-      sqab0 += fabsf(a0);  // h = 0: |x|^2, h = 1: |x|_1 of rows c and c + 32
-      sqab1 += fabsf(a1);
-    }
+  auto step = [&](const float2& x0, const float2& x1, v4f w) {
+    const float s00 = x0.x * x0.x, s01 = x0.y * x0.y, s10 = x1.x * x1.x, s11 = x1.y * x1.y;
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(s00, w[0], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(s10, w[0], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(s01, w[1], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(s11, w[1], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x0.x, w[2], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x1.x, w[2], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x0.y, w[3], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x1.y, w[3], acc1, 0, 0, 0);
+    sq0 += s00 + s01;  // rows c and c + 32
+    sq1 += s10 + s11;
+    ab0 += fabsf(x0.x) + fabsf(x0.y);
+    ab1 += fabsf(x1.x) + fabsf(x1.y);
   };
   // The X operands of the next step are read from LDS before this step's
   // MFMAs issue; the scheduling barriers keep every load where it is.
   static_assert(Q % 4 == 0, "the score loop takes four steps at a time");
   v4f wa = wload(0), wb = wload(1);
-  float4 pa0, pa1, pb0, pb1;
+  float2 pa0, pa1, pb0, pb1;
   xld(0, pa0, pa1);
 #pragma unroll 1
   for (int q = 0; q < Q; q += 4) {
@@ -363,8 +372,17 @@ __device__ __forceinline__ void score_tile(const float* xs, float* sc, float* xq
   int scb = 4 * h * SCS + wave * 32 + c;
   asm volatile("" : "+v"(scb));
   if (wave == 0) {
-    xq[2 * c + h] = sqab0;
-    xq[2 * (c + 32) + h] = sqab1;
+    // the two halves of the wave hold the two halves of each row's features
+    sq0 += __shfl_xor(sq0, 32, 64);
+    sq1 += __shfl_xor(sq1, 32, 64);
+    ab0 += __shfl_xor(ab0, 32, 64);
+    ab1 += __shfl_xor(ab1, 32, 64);
+    if (h == 0) {
+      xq[2 * c] = sq0;
+      xq[2 * c + 1] = ab0;
+      xq[2 * (c + 32)] = sq1;
+      xq[2 * (c + 32) + 1] = ab1;
+    }
   }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
