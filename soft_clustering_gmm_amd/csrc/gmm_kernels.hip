@@ -874,7 +874,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
 //   2. per row (`waves` threads per row): every centre whose fp32 score is
 //      within twice the score error bound of the slab's best fp32 score may be
 //      the slab's nearest centre. Those candidates get |x - c_k|^2 exactly in
-//      fp64 (difference form, eight lanes per candidate) and the smallest
+//      fp64 (difference form, 2 to 8 lanes per candidate by d) and the smallest
 //      wins, ties to the lower index;
 //   3. the slab's winner replaces the row's best so far only when strictly
 //      nearer, so across slabs ties also go to the lower index.
