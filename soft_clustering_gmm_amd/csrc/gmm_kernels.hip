@@ -271,10 +271,13 @@ __global__ void pack_kernel(const float* __restrict__ mu, const float* __restric
     W32p[base + 2] = (float)(B * kLog2E);
   }
   if (k < Kp16) {
-    const int kt = k >> 4, c = k & 15, s = f >> 1, S = DP >> 1, g0 = 2 * (f & 1);
-    const size_t base = (((size_t)kt * S + s) * 4 + g0) * 16 + c;
+    // 16x16x4 f64 MFMA A operand of 16-component tile kt: lane (g, c) of step
+    // 2j holds A of feature 4j + g of component c (the x^2 step), of step
+    // 2j + 1 its B (the x step)
+    const int kt = k >> 4, c = k & 15, j = f >> 2, g = f & 3, S = DP >> 1;
+    const size_t base = (((size_t)kt * S + 2 * j) * 4 + g) * 16 + c;
     W64p[base] = A;
-    W64p[base + 16] = B;
+    W64p[base + 64] = B;
   }
 }
 
@@ -1172,7 +1175,7 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
   // Score operands in registers. Step s pairs lane (g, c) with feature
   // g*(DP/4) + s/2, as x^2 on even steps and x on odd steps: each lane reads
   // its point's features contiguously and squares each once. W64p holds
-  // feature f, part t of component c at ((f/2)*4 + 2*(f%2) + t)*16 + c.
+  // feature f, part t (A, B) of component c at ((2*(f/4) + t)*4 + f%4)*16 + c.
   // Operands and constants are scaled by log2(e) before rounding to fp32, so
   // the scores come out in base-2 units and e = 2^(s - m) needs no multiply.
   // Every fp32 operand is still the correctly rounded value of an exact one,
@@ -1182,7 +1185,7 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int f = g * (DP / 4) + (s >> 1);
-    w[s] = (float)(W64p[((f >> 1) * 4 + 2 * (f & 1) + (s & 1)) * 16 + c] * kLog2E);
+    w[s] = (float)(W64p[((2 * (f >> 2) + (s & 1)) * 4 + (f & 3)) * 16 + c] * kLog2E);
   }
   float cks[16];
 #pragma unroll
@@ -1589,27 +1592,29 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
     v4d D[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) D[p] = (v4d){0.0, 0.0, 0.0, 0.0};
-    auto step = [&](int s, double a) {
-      const int f = 2 * s + (g >> 1);
+    // Feature block j (features 4j..4j+3; lane group g takes feature 4j + g
+    // of its point): the x^2 step with the operands of step 2j, then the x
+    // step with those of step 2j + 1. Each lane converts and squares only its
+    // own x.
+    auto block = [&](int j, double asq, double alin) {
+      double xv[NP];
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const double x = (double)xs[((pg + p * PS) * 16 + c) * XS + f];
-        const double b = (g & 1) ? x : x * x;
-        D[p] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, D[p], 0, 0, 0);
-      }
+      for (int p = 0; p < NP; ++p) xv[p] = (double)xs[((pg + p * PS) * 16 + c) * XS + 4 * j + g];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) D[p] = __builtin_amdgcn_mfma_f64_16x16x4f64(asq, xv[p] * xv[p], D[p], 0, 0, 0);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) D[p] = __builtin_amdgcn_mfma_f64_16x16x4f64(alin, xv[p], D[p], 0, 0, 0);
     };
 #pragma unroll 1
     for (int s = 0; s < S; s += 4) {
       const double wc = wl(kt, s + 2), wd = wl(kt, s + 3);
       __builtin_amdgcn_sched_barrier(0);
-      step(s, wa);
-      step(s + 1, wb);
+      block(s >> 1, wa, wb);
       __builtin_amdgcn_sched_barrier(0);
       wa = s + 4 < S ? wl(kt, s + 4) : wl(kt + NP, 0);
       wb = s + 4 < S ? wl(kt, s + 5) : wl(kt + NP, 1);
       __builtin_amdgcn_sched_barrier(0);
-      step(s + 2, wc);
-      step(s + 3, wd);
+      block((s >> 1) + 1, wc, wd);
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
