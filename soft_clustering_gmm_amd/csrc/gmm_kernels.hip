@@ -478,6 +478,13 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   // The next tile's X streams straight into the other LDS buffer (16-byte
   // global->LDS loads) while the statistics MFMAs run.
   const bool async_x = vec && sizeof(XT) == 4;
+  // Half-precision rows of at most 96 values (vec == 2: d % 8 == 0, 16-byte
+  // aligned): the next tile is fetched as 16-byte chunks of eight values
+  // (chunk tid + nthr i, at most two per thread) into registers while the
+  // statistics run, and widened into the other buffer at the end of the tile.
+  constexpr bool kHalfPre = sizeof(XT) == 2 && DT <= 3;
+  const bool hpref = kHalfPre && vec == 2 && 8 * DP <= 2 * nthr;
+  uint4 hpre[2];
   load_x_tile<XS>(xsb, X, lo, hi, d, DP, tid, nthr, vec);
   int cur = 0;
   for (int64_t r0 = lo; r0 < hi; r0 += 64) {
@@ -731,6 +738,15 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     const int64_t rn = r0 + 64;
     if (async_x && rn < hi) async_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, reinterpret_cast<const float*>(X),
                                              rn, hi, d, wave, waves, lane);
+    if constexpr (kHalfPre)
+      if (hpref && rn < hi)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ch = tid + nthr * i, row = ch / (DP / 8), q = ch - row * (DP / 8);
+        const int64_t gr = rn + row;
+        hpre[i] = (ch < 8 * DP && gr < hi && 8 * q < d) ? *reinterpret_cast<const uint4*>(X + gr * d + 8 * q)
+                                                        : make_uint4(0u, 0u, 0u, 0u);
+      }
     if constexpr (SPLIT) {
       // Split-bf16 products on the 32x32x16 bf16 MFMA (see the small-K
       // kernel for the error of a product): block pb covers points
@@ -830,7 +846,26 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         }
       }
     }
-    if (rn < hi && !async_x) load_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, X, rn, hi, d, DP, tid, nthr, vec);
+    if constexpr (kHalfPre) {
+      if (rn < hi && hpref) {
+        float* xn = xsb + (cur ^ 1) * 64 * XS;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int ch = tid + nthr * i, row = ch / (DP / 8), q = ch - row * (DP / 8);
+          if (ch < 8 * DP) {
+            const XT* hv = reinterpret_cast<const XT*>(&hpre[i]);
+            *reinterpret_cast<float4*>(xn + row * XS + 8 * q) =
+                make_float4((float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]);
+            *reinterpret_cast<float4*>(xn + row * XS + 8 * q + 4) =
+                make_float4((float)hv[4], (float)hv[5], (float)hv[6], (float)hv[7]);
+          }
+        }
+      } else if (rn < hi) {
+        load_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, X, rn, hi, d, DP, tid, nthr, vec);
+      }
+    } else if (rn < hi && !async_x) {
+      load_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, X, rn, hi, d, DP, tid, nthr, vec);
+    }
     // This thread's async tile loads have landed. The wait is unconditional so
     // that no global->LDS load counts as in flight at the top of the loop:
     // the compiler would otherwise drain every global load before each LDS
@@ -1896,7 +1931,10 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(p.P * p.kslabs);
-  const int vec = (sizeof(XT) == 4 && p.d % 4 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0) ? 1 : 0;
+  // 1: fp32 rows of d % 4 == 0 floats, 2: half-precision rows of d % 8 == 0
+  // values, both 16-byte aligned; 0 otherwise
+  const bool al16 = reinterpret_cast<uintptr_t>(X) % 16 == 0;
+  const int vec = sizeof(XT) == 4 ? (p.d % 4 == 0 && al16 ? 1 : 0) : (p.d % 8 == 0 && al16 ? 2 : 0);
   fn<<<grid, nthr, lds, stream>>>(X, p.N, p.d, p.K, p.Kp, p.waves, p.kslabs, p.rows_per_chunk,
                                   reinterpret_cast<const float4*>(w.W32p), w.c32, w.mup, w.ivp, w.c64d, w.errc,
                                   w.rowref, w.partials, w.llpart, ll_point, R, vec);
