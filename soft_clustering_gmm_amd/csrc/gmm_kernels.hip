@@ -949,11 +949,14 @@ kmeans_assign_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int wave
 
   const int64_t lo = chunk * rows_per_chunk;
   const int64_t hi = min(N, lo + rows_per_chunk);
-  // fp32 rows: the next tile is fetched into registers (16-byte chunks
-  // tid + nthr * i) while the rows of this one are decided, and written to
-  // LDS once the tile is done; other inputs load at the end of the tile.
+  // fp32 rows (vec == 1) and half-precision rows (vec == 2): the next tile
+  // is fetched into registers (16-byte chunks tid + nthr * i) while the rows
+  // of this one are decided, and written to LDS once the tile is done (half
+  // values widened there); other inputs load at the end of the tile.
   const int nch = 16 * DP / nthr;
-  const bool pref = vec && sizeof(XT) == 4 && nch <= 8 && nch * nthr == 16 * DP;
+  const bool pref = vec == 1 && sizeof(XT) == 4 && nch <= 8 && nch * nthr == 16 * DP;
+  const int nhc = 8 * DP, nh = (nhc + nthr - 1) / nthr;  // half rows: chunks of eight values
+  const bool hpref = vec == 2 && sizeof(XT) == 2 && nh <= 8;
   float4 xpre[8];
   auto chunk_at = [&](int i, int& row, int& q) {
     const int ch = tid + nthr * i;
@@ -982,6 +985,17 @@ kmeans_assign_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int wave
             xpre[i] = (gr < hi && 4 * q < d) ? *reinterpret_cast<const float4*>(Xf + gr * d + 4 * q)
                                              : make_float4(0.f, 0.f, 0.f, 0.f);
           }
+      }
+      if (sizeof(XT) == 2 && slab == 0 && hpref && rn < hi) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int ch = tid + nthr * i, row = ch / (DP / 8), q = ch - row * (DP / 8);
+          const int64_t gr = rn + row;
+          if (i < nh)
+            xpre[i] = (ch < nhc && gr < hi && 8 * q < d)
+                          ? __builtin_bit_cast(float4, *reinterpret_cast<const uint4*>(X + gr * d + 8 * q))
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
 
       const int row = prow;
@@ -1122,6 +1136,19 @@ kmeans_assign_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int wave
             chunk_at(i, row, q);
             *reinterpret_cast<float4*>(xs + row * XS + 4 * q) = xpre[i];
           }
+      } else if (sizeof(XT) == 2 && hpref) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int ch = tid + nthr * i, row = ch / (DP / 8), q = ch - row * (DP / 8);
+          if (i < nh && ch < nhc) {
+            const uint4 raw = __builtin_bit_cast(uint4, xpre[i]);
+            const XT* hv = reinterpret_cast<const XT*>(&raw);
+            *reinterpret_cast<float4*>(xs + row * XS + 8 * q) =
+                make_float4((float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]);
+            *reinterpret_cast<float4*>(xs + row * XS + 8 * q + 4) =
+                make_float4((float)hv[4], (float)hv[5], (float)hv[6], (float)hv[7]);
+          }
+        }
       } else {
         load_x_tile<XS>(xs, X, rn, hi, d, DP, tid, nthr, vec);
       }
@@ -2092,7 +2119,8 @@ static hipError_t run_kmeans_assign(const Plan& p, const XT* X, int32_t* assign,
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const int vec = (sizeof(XT) == 4 && p.d % 4 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0) ? 1 : 0;
+  const bool al16 = reinterpret_cast<uintptr_t>(X) % 16 == 0;
+  const int vec = sizeof(XT) == 4 ? (p.d % 4 == 0 && al16 ? 1 : 0) : (p.d % 8 == 0 && al16 ? 2 : 0);
   fn<<<(unsigned)chunks, nthr, lds, stream>>>(X, p.N, p.d, p.K, p.waves, p.kslabs, rows_per_chunk,
                                               reinterpret_cast<const float4*>(w.W32p), w.c32, w.mup, w.errc,
                                               assign, dist2, w.llpart, vec);
