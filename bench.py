@@ -153,6 +153,45 @@ def border_lists_bench(args, w, torch, gmm, dev):
     return 0
 
 
+def top2_bench(args, w, X, mu, var, logw, torch, gmm, dev):
+    """One step = gmm_assign_top2 (each point's two most responsible components
+    and their responsibilities, from the fp64 score pass) on the workload's X
+    and initial parameters, all resident in HBM. Roofline: the pass's 4NKd
+    score flops on the FP64 MFMA peak, timed with events around the call."""
+    N, d, K = X.shape[0], X.shape[1], mu.shape[0]
+    Xd = torch.from_numpy(X).to(dev)
+    mud, vard, lwd = (torch.from_numpy(a.copy()).to(dev) for a in (mu, var, logw))
+    ws = gmm.workspace(N, d, K, dev)
+    for _ in range(args.warmup):
+        gmm.assign_top2(Xd, mud, vard, lwd, ws=ws)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        gmm.assign_top2(Xd, mud, vard, lwd, ws=ws)
+        b.record()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    flops = 4.0 * N * K * d
+    ach = flops / (k_ms * 1e-3) / 1e12
+    out = {
+        "metric": "top-2 assignment, points x components/s", "value": N * K / (ms * 1e-3),
+        "unit": "points×components/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"{w.name} recipe: N={N} d={d} K={K} {w.x_dtype}; initial parameters; "
+                               f"step = gmm_assign_top2", "N": N, "d": d, "K": K},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP64_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_FP64_MFMA_TFLOPS, 4), "traffic": None,
+                     "kernel": "estep_lse_kernel (top-2)", "flops_per_launch": flops,
+                     "avg_call_ms": round(k_ms, 4)},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def kmeans_bench(args, w, torch, gmm, dev):
     """One step = one Lloyd iteration (nearest-centre assignment: fp32 scores on
     the matrix cores, exact fp64 distances for the candidates; then the
@@ -224,6 +263,8 @@ def main(argv=None):
                     help="time the border-vector inverted-list build on the workload's N and K from a "
                          "synthetic top-2 assignment resident in HBM")
     ap.add_argument("--border-threshold", type=float, default=0.05)
+    ap.add_argument("--top2", action="store_true",
+                    help="time gmm_assign_top2 on the workload's X and initial parameters")
     ap.add_argument("--kmeans", action="store_true",
                     help="time Lloyd iterations of k-means on the workload's X with its K initial means as centres")
     ap.add_argument("--stats-precision", default="fp32", choices=["fp32", "split-bf16"],
@@ -248,6 +289,8 @@ def main(argv=None):
     X, mu, var, logw = datagen.make_workload(args.workload)
     if args.x_on_host:
         return host_streamed(args, w, X, mu, var, logw, torch, gmm, dev)
+    if args.top2:
+        return top2_bench(args, w, X, mu, var, logw, torch, gmm, dev)
     N, d, K = X.shape[0], X.shape[1], mu.shape[0]
     Xd = torch.from_numpy(X).to(dev)
     mu0, var0, lw0 = (torch.from_numpy(a.copy()).to(dev) for a in (mu, var, logw))
