@@ -1973,7 +1973,9 @@ static hipError_t run_lse(const Plan& p, const XT* X, float* ll_point, int32_t* 
                           hipStream_t stream) {
   const Workspace& w = p.ws;
   const int Kt = p.Kp16 / 16;
-  if (Kt >= kLseWaves)
+  // Top-2 takes two point groups per wave even with many component tiles:
+  // its extra state would otherwise keep the kernel from four waves per SIMD.
+  if (Kt >= kLseWaves && !TOP2)
     estep_lse_kernel<DT, TOP2, XT, 4><<<(unsigned)p.tiles, 256, 0, stream>>>(
         X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp);
   else if (Kt >= 2)
