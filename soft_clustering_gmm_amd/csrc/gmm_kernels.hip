@@ -1201,8 +1201,9 @@ struct SmallTile {
   static constexpr int LPE = DS == 1 ? 1 : (DS == 2 ? 2 : 4), FPL = DP / LPE;
 };
 
+// Two blocks per CU (two waves per SIMD): at most 256 registers per lane.
 template <int DS, typename XT, bool SPLIT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wave_rows,
                    const double* __restrict__ W64p, const double* __restrict__ c64e,
                    const float* __restrict__ mu, const double* __restrict__ iv64,
