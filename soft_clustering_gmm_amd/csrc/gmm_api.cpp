@@ -455,7 +455,7 @@ static hipError_t kmeans_update_impl(const void* X, int32_t xt, int64_t N, int32
   int32_t* members = reinterpret_cast<int32_t*>(w + L.members);
   hipError_t e = launch_border_lists(assign, nullptr, N, K, 0.f, offsets, members, w + L.lists, s);
   if (e == hipSuccess)
-    e = launch_kmeans_update(X, xt, d, K, offsets, members, reinterpret_cast<int32_t*>(w + L.seg),
+    e = launch_kmeans_update(X, xt, N, d, K, offsets, members, reinterpret_cast<int32_t*>(w + L.seg),
                              reinterpret_cast<int64_t*>(w + L.segoff), reinterpret_cast<int64_t*>(w + L.scan),
                              reinterpret_cast<double*>(w + L.part), L.max_segments, C, counts, s);
   return e;

@@ -97,7 +97,7 @@ hipError_t launch_kmeans_assign(const Plan& p, const void* X, int x_dtype, int32
 hipError_t launch_fill(float* a, int64_t n, float v, hipStream_t stream);
 // k-means update from the lists of a hard assignment (gmm_lists.hip).
 int64_t kmeans_max_segments(int64_t N, int K);
-hipError_t launch_kmeans_update(const void* X, int x_dtype, int d, int K, const int64_t* offsets,
+hipError_t launch_kmeans_update(const void* X, int x_dtype, int64_t N, int d, int K, const int64_t* offsets,
                                 const int32_t* members, int32_t* seg, int64_t* segoff, int64_t* scan_tmp,
                                 double* part, int64_t max_segments, float* C, int64_t* counts,
                                 hipStream_t stream);

@@ -40,6 +40,7 @@
 #include "gmm_device.hpp"
 #include "gmm_internal.hpp"
 
+#include <atomic>
 #include <algorithm>
 #include <limits.h>
 #include <math.h>
@@ -2110,8 +2111,8 @@ hipError_t launch_top2(const Plan& p, const void* X, int x_dtype, int32_t* idx, 
 }
 
 template <int DT, typename XT>
-static hipError_t run_kmeans_assign(const Plan& p, const XT* X, int32_t* assign, float* dist2, int64_t rows_per_chunk,
-                                    int64_t chunks, hipStream_t stream) {
+static hipError_t run_kmeans_assign(const Plan& p, const XT* X, int32_t* assign, float* dist2, double* inertia,
+                                    hipStream_t stream) {
   const Workspace& w = p.ws;
   const int nthr = p.waves * 64;
   const int KS = p.waves * 32;
@@ -2122,37 +2123,46 @@ static hipError_t run_kmeans_assign(const Plan& p, const XT* X, int32_t* assign,
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
+  // One block walks every slab of its rows, so the row chunks are cut for
+  // exactly the blocks that can be resident at once (by LDS, registers and
+  // waves) over 256 CUs: one more chunk than fits would run as a second
+  // round on a nearly idle chip. There are at most `tiles` chunks, which the
+  // workspace's per-chunk sums hold.
+  static std::atomic<int> resident[kSlabWaves + 1];
+  int per_cu = resident[p.waves].load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, nthr, lds);
+    if (e != hipSuccess) return e;
+    per_cu = std::max(per_cu, 1);
+    resident[p.waves].store(per_cu, std::memory_order_relaxed);
+  }
+  const int64_t target = std::max<int64_t>(1, std::min<int64_t>(256 * (int64_t)per_cu, p.tiles));
+  const int64_t rows_per_chunk = (p.tiles + target - 1) / target * 64;
+  const int64_t chunks = (p.N + rows_per_chunk - 1) / rows_per_chunk;
   const bool al16 = reinterpret_cast<uintptr_t>(X) % 16 == 0;
   const int vec = sizeof(XT) == 4 ? (p.d % 4 == 0 && al16 ? 1 : 0) : (p.d % 8 == 0 && al16 ? 2 : 0);
   fn<<<(unsigned)chunks, nthr, lds, stream>>>(X, p.N, p.d, p.K, p.waves, p.kslabs, rows_per_chunk,
                                               reinterpret_cast<const float4*>(w.W32p), w.c32, w.mup, w.errc,
                                               assign, dist2, w.llpart, vec);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess && inertia) {
+    reduce_ll_kernel<false><<<1, 256, 0, stream>>>(w.llpart, chunks, inertia, 0);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 hipError_t launch_kmeans_assign(const Plan& p, const void* X, int x_dtype, int32_t* assign, float* dist2,
                                 double* inertia, hipStream_t stream) {
   if (p.N == 0) return hipSuccess;
-  // One block walks every slab of its rows, so the row chunks are cut for
-  // one resident block per SIMD-set (8 waves per CU) over 256 CUs whatever
-  // the number of slabs. There are at most `tiles` chunks, which the
-  // workspace's per-chunk sums hold.
-  const int64_t target = std::max<int64_t>(1, std::min<int64_t>(256 * std::max(1, 8 / p.waves), p.tiles));
-  const int64_t rows_per_chunk = (p.tiles + target - 1) / target * 64;
-  const int64_t chunks = (p.N + rows_per_chunk - 1) / rows_per_chunk;
-  hipError_t e = with_x_type(x_dtype, X, [&](auto x) {
+  return with_x_type(x_dtype, X, [&](auto x) {
     switch (p.DT) {
-      case 1: return run_kmeans_assign<1>(p, x, assign, dist2, rows_per_chunk, chunks, stream);
-      case 2: return run_kmeans_assign<2>(p, x, assign, dist2, rows_per_chunk, chunks, stream);
-      case 3: return run_kmeans_assign<3>(p, x, assign, dist2, rows_per_chunk, chunks, stream);
-      default: return run_kmeans_assign<4>(p, x, assign, dist2, rows_per_chunk, chunks, stream);
+      case 1: return run_kmeans_assign<1>(p, x, assign, dist2, inertia, stream);
+      case 2: return run_kmeans_assign<2>(p, x, assign, dist2, inertia, stream);
+      case 3: return run_kmeans_assign<3>(p, x, assign, dist2, inertia, stream);
+      default: return run_kmeans_assign<4>(p, x, assign, dist2, inertia, stream);
     }
   });
-  if (e == hipSuccess && inertia) {
-    reduce_ll_kernel<false><<<1, 256, 0, stream>>>(p.ws.llpart, chunks, inertia, 0);
-    e = hipGetLastError();
-  }
-  return e;
 }
 
 __global__ void fill_kernel(float* __restrict__ a, int64_t n, float v) {

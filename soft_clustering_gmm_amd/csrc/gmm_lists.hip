@@ -14,6 +14,7 @@
 // major), then a scatter in which each one-wave block ranks its items
 // stably with ballots into an LDS stage ordered by digit, and writes each
 // digit's run out contiguously. Everything is integer work and deterministic.
+#include <atomic>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -396,16 +397,19 @@ hipError_t launch_border_lists(const int32_t* idx, const float* resp, int64_t N,
 // ---------------------------------------------------------------------------
 // Lloyd's k-means update through the sorted lists (sort-inverse update of
 // the Flash-KMeans articles): each list is summed as contiguous segments of
-// kSegRows members, segment sums are combined per list in segment order, and
+// seg_rows members, segment sums are combined per list in segment order, and
 // the centre becomes sum / count (a list with no members keeps its centre).
-// Fixed orders throughout: deterministic.
+// seg_rows is at least kSegRows and grows with N so that all segments fit in
+// one round of resident blocks (enough to fill the chip, and few partials for
+// the per-list combine). Fixed orders throughout: deterministic.
 // ---------------------------------------------------------------------------
 
-constexpr int kSegRows = 1024;
+constexpr int kSegRows = 512;
 
-__global__ void kmeans_segcount_kernel(const int64_t* __restrict__ offsets, int K, int32_t* __restrict__ seg) {
+__global__ void kmeans_segcount_kernel(const int64_t* __restrict__ offsets, int K, int64_t seg_rows,
+                                       int32_t* __restrict__ seg) {
   const int k = blockIdx.x * blockDim.x + threadIdx.x;
-  if (k < K) seg[k] = (int32_t)((offsets[k + 1] - offsets[k] + kSegRows - 1) / kSegRows);
+  if (k < K) seg[k] = (int32_t)((offsets[k + 1] - offsets[k] + seg_rows - 1) / seg_rows);
 }
 
 // Block b sums segment b: rows members[start, end) of list k, where k is the
@@ -420,7 +424,7 @@ template <typename XT>
 __global__ void __launch_bounds__(256)
 kmeans_segsum_kernel(const XT* __restrict__ X, int d, const int64_t* __restrict__ offsets,
                      const int32_t* __restrict__ members, const int64_t* __restrict__ segoff, int K,
-                     double* __restrict__ part, int vec) {
+                     int64_t seg_rows, double* __restrict__ part, int vec) {
   __shared__ double s[4][128];
   const int64_t b = blockIdx.x;
   if (b >= segoff[K]) return;
@@ -433,8 +437,8 @@ kmeans_segsum_kernel(const XT* __restrict__ X, int d, const int64_t* __restrict_
       hi = mid - 1;
   }
   const int k = lo;
-  const int64_t start = offsets[k] + (b - segoff[k]) * kSegRows;
-  const int64_t end = min(start + kSegRows, offsets[k + 1]);
+  const int64_t start = offsets[k] + (b - segoff[k]) * seg_rows;
+  const int64_t end = min(start + seg_rows, offsets[k + 1]);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int G = 8;
   if (sizeof(XT) == 4 && vec) {
@@ -534,20 +538,36 @@ kmeans_finalize_kernel(const double* __restrict__ part, const int64_t* __restric
   }
 }
 
+// An upper bound for every choice of seg_rows >= kSegRows: the lists'
+// segments number at most ceil(N / kSegRows) + K.
 int64_t kmeans_max_segments(int64_t N, int K) { return (N + kSegRows - 1) / kSegRows + K; }
 
-hipError_t launch_kmeans_update(const void* X, int x_dtype, int d, int K, const int64_t* offsets,
+hipError_t launch_kmeans_update(const void* X, int x_dtype, int64_t N, int d, int K, const int64_t* offsets,
                                 const int32_t* members, int32_t* seg, int64_t* segoff, int64_t* scan_tmp,
                                 double* part, int64_t max_segments, float* C, int64_t* counts,
                                 hipStream_t stream) {
-  kmeans_segcount_kernel<<<(unsigned)((K + 255) / 256), 256, 0, stream>>>(offsets, K, seg);
-  hipError_t e = excl_scan(seg, K, segoff, scan_tmp, segoff + K, stream);
-  if (e != hipSuccess) return e;
-  e = with_x_type(x_dtype, X, [&](auto x) {
+  hipError_t e = with_x_type(x_dtype, X, [&](auto x) {
     using XT = std::remove_cv_t<std::remove_pointer_t<decltype(x)>>;
+    auto fn = kmeans_segsum_kernel<XT>;
+    // Blocks resident at once over 256 CUs; the lists' segments number at
+    // most ceil(N / seg_rows) + K, so seg_rows is chosen to keep that within
+    // one such round (never below kSegRows, which the workspace is sized for).
+    static std::atomic<int> resident{0};
+    int per_cu = resident.load(std::memory_order_relaxed);
+    if (per_cu == 0) {
+      hipError_t q = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0);
+      if (q != hipSuccess) return q;
+      per_cu = std::max(per_cu, 1);
+      resident.store(per_cu, std::memory_order_relaxed);
+    }
+    const int64_t round = 256 * (int64_t)per_cu - K;
+    const int64_t seg_rows = round > 0 ? std::max<int64_t>(kSegRows, (N + round - 1) / round) : kSegRows;
+    kmeans_segcount_kernel<<<(unsigned)((K + 255) / 256), 256, 0, stream>>>(offsets, K, seg_rows, seg);
+    hipError_t e2 = excl_scan(seg, K, segoff, scan_tmp, segoff + K, stream);
+    if (e2 != hipSuccess) return e2;
     const int vec = (sizeof(XT) == 4 && d % 4 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0) ? 1 : 0;
-    kmeans_segsum_kernel<XT><<<(unsigned)max_segments, 256, 0, stream>>>(x, d, offsets, members, segoff, K, part,
-                                                                          vec);
+    const int64_t blocks = std::min<int64_t>(max_segments, (N + seg_rows - 1) / seg_rows + K);
+    fn<<<(unsigned)blocks, 256, 0, stream>>>(x, d, offsets, members, segoff, K, seg_rows, part, vec);
     return hipGetLastError();
   });
   if (e != hipSuccess) return e;

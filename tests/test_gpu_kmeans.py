@@ -7,8 +7,8 @@ oracle's fp64 differences), so it must match exactly except at near-ties,
 whose gap is below the fp64 rounding of the distances; those rows are counted
 and excluded. Centres are fp64 means rounded to
 float, checked to a few float ulps. Cases: each workload recipe at reduced N
-(fp16 X for the IVF recipe, K up to 4096), lists longer than one 1024-row
-segment, an empty cluster, and a device loop against the oracle loop.
+(fp16 X for the IVF recipe, K up to 4096), lists longer than one 512-row
+segment (and, at full size, segments of 8K rows), an empty cluster, and a device loop against the oracle loop.
 """
 import numpy as np
 import pytest
@@ -84,12 +84,22 @@ def test_kmeans_update_workloads(G, name, N):
 
 
 def test_kmeans_update_long_lists_and_empty_cluster(G):
-    """One cluster takes 5000 points (five 1024-row segments), one none."""
+    """One cluster takes 5000 points (ten segments of the 512-row minimum), one none."""
     rng = np.random.default_rng(9)
     X = rng.normal(size=(6000, 37)).astype(np.float32)
     assign = np.where(np.arange(6000) < 5000, 2, rng.integers(0, 2, 6000)).astype(np.int64)
     C = rng.normal(size=(4, 37)).astype(np.float32)
     _check_update(G, X, assign, C, "long lists")
+
+
+def test_kmeans_update_full_size(G):
+    """The small-K recipe at full size (16M rows, 32 features): lists of about
+    1M members, summed in segments longer than the 512-row minimum, with one
+    list left empty. Random labels stand in for an assignment."""
+    X, mu, _, _ = datagen.make_workload("smallk")
+    K = mu.shape[0]
+    assign = np.random.default_rng(43).integers(0, K - 1, X.shape[0])
+    _check_update(G, X, assign, mu, "smallk full-size update")
 
 
 def test_kmeans_device_loop_matches_oracle_loop(G):
