@@ -418,6 +418,9 @@ __global__ void kmeans_segcount_kernel(const int64_t* __restrict__ offsets, int 
 //    power of two >= d/4) with four features each, so a wave reads 64 / LPR
 //    rows per load and eight loads per lane are in flight; the row groups are
 //    combined by an xor butterfly, then the four waves in order.
+//  - half-precision rows with d % 8 == 0 (16-byte aligned): the same with
+//    eight features per lane (LPR the power of two >= d/8), widened in
+//    registers.
 //  - otherwise: lanes hold features lane and lane + 64, wave w takes rows
 //    start + w + 4i in groups of 8.
 template <typename XT>
@@ -441,7 +444,7 @@ kmeans_segsum_kernel(const XT* __restrict__ X, int d, const int64_t* __restrict_
   const int64_t end = min(start + seg_rows, offsets[k + 1]);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int G = 8;
-  if (sizeof(XT) == 4 && vec) {
+  if (sizeof(XT) == 4 && vec == 1) {
     int LPR = 1;
     while (4 * LPR < d) LPR <<= 1;
     const int RPW = 64 / LPR, rsub = lane / LPR, q = lane - rsub * LPR;
@@ -476,6 +479,35 @@ kmeans_segsum_kernel(const XT* __restrict__ X, int d, const int64_t* __restrict_
       s[wave][4 * q + 2] = a2;
       s[wave][4 * q + 3] = a3;
     }
+  } else if (sizeof(XT) == 2 && vec == 2) {
+    int LPR = 1;
+    while (8 * LPR < d) LPR <<= 1;
+    const int RPW = 64 / LPR, rsub = lane / LPR, q = lane - rsub * LPR;
+    const bool fin = 8 * q < d;
+    double a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = 0.0;
+    for (int64_t i0 = start + wave * RPW + rsub; i0 < end; i0 += 4 * RPW * G) {
+      uint4 v[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int64_t i = i0 + 4 * RPW * j;
+        v[j] = (i < end && fin) ? *reinterpret_cast<const uint4*>(X + (int64_t)members[i] * d + 8 * q)
+                                : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const XT* hv = reinterpret_cast<const XT*>(&v[j]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] += (double)(float)hv[u];
+      }
+    }
+    for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] += __shfl_xor(a[u], o, 64);
+    if (rsub == 0 && fin)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s[wave][8 * q + u] = a[u];
   } else {
     const int f0 = lane, f1 = lane + 64;
     double a0 = 0.0, a1 = 0.0;
@@ -565,7 +597,8 @@ hipError_t launch_kmeans_update(const void* X, int x_dtype, int64_t N, int d, in
     kmeans_segcount_kernel<<<(unsigned)((K + 255) / 256), 256, 0, stream>>>(offsets, K, seg_rows, seg);
     hipError_t e2 = excl_scan(seg, K, segoff, scan_tmp, segoff + K, stream);
     if (e2 != hipSuccess) return e2;
-    const int vec = (sizeof(XT) == 4 && d % 4 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0) ? 1 : 0;
+    const bool al16 = reinterpret_cast<uintptr_t>(x) % 16 == 0;
+    const int vec = sizeof(XT) == 4 ? (d % 4 == 0 && al16 ? 1 : 0) : (d % 8 == 0 && al16 ? 2 : 0);
     const int64_t blocks = std::min<int64_t>(max_segments, (N + seg_rows - 1) / seg_rows + K);
     fn<<<(unsigned)blocks, 256, 0, stream>>>(x, d, offsets, members, segoff, K, seg_rows, part, vec);
     return hipGetLastError();

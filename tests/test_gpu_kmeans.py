@@ -92,6 +92,33 @@ def test_kmeans_update_long_lists_and_empty_cluster(G):
     _check_update(G, X, assign, C, "long lists")
 
 
+@pytest.mark.parametrize("dtype,d,offset", [("float16", 96, 0), ("float16", 37, 0), ("bfloat16", 64, 0),
+                                             ("bfloat16", 24, 1)])
+def test_kmeans_update_half_rows(G, dtype, d, offset):
+    """Half-precision rows (rounded by torch; the oracle gets the same values,
+    widened): 16-byte loads of eight values when d % 8 == 0 and the base is
+    16-byte aligned, element loads otherwise (odd d, or a base one element
+    past an aligned address). One list spans several segments."""
+    rng = np.random.default_rng(50 + d)
+    N, K = 7000, 5
+    tdt = getattr(torch, dtype)
+    Xt = torch.from_numpy(rng.normal(2.0, 3.0, (N, d)).astype(np.float32)).to(tdt)
+    Xv = Xt.float().numpy()
+    buf = torch.zeros(N * d + offset, dtype=tdt, device="cuda")
+    buf[offset:] = Xt.reshape(-1).to("cuda")
+    Xd = buf[offset:].view(N, d)
+    assign = rng.integers(0, K, N)
+    assign[:3000] = 1
+    C = rng.normal(size=(K, d)).astype(np.float32)
+    Cg = dev(C.copy())
+    counts = G.kmeans_update(Xd, dev(assign.astype(np.int32)), Cg)
+    torch.cuda.synchronize()
+    rC, rn = oracle.kmeans_update(Xv, assign, C)
+    assert np.array_equal(host(counts), rn)
+    err = np.abs(host(Cg).astype(np.float64) - rC) / np.maximum(np.abs(rC), 1e-3)
+    assert err.max() <= 3e-7, f"{dtype} d={d} offset={offset}: centre rel err {err.max():.2e}"
+
+
 def test_kmeans_update_full_size(G):
     """The small-K recipe at full size (16M rows, 32 features): lists of about
     1M members, summed in segments longer than the 512-row minimum, with one
