@@ -223,9 +223,11 @@ int gmm_kmeans_assign(const void* X, int32_t x_dtype, int64_t N, int32_t d, cons
                       void* workspace, size_t ws_bytes, void* stream);
 
 /* gmm_kmeans_update: C[k] (in/out) becomes the mean of the points with
- * assign[n] == k, summed in fp64 in point order; a centre with no points
- * keeps its value. counts (nullable, K int64) receives the cluster sizes.
- * assign[n] must lie in [0, K). */
+ * assign[n] == k, summed in fp64 (each cluster's points in point order, cut
+ * into fixed segments whose length depends on N and on how many blocks the
+ * device holds at once, so results repeat exactly on one device model); a
+ * centre with no points keeps its value. counts (nullable, K int64)
+ * receives the cluster sizes. assign[n] must lie in [0, K). */
 int gmm_kmeans_update(const void* X, int32_t x_dtype, int64_t N, int32_t d, const int32_t* assign, int32_t K,
                       float* C, int64_t* counts, void* workspace, size_t ws_bytes, void* stream);
 
