@@ -245,6 +245,21 @@ lists_scatter_kernel(const int32_t* __restrict__ idx, const float* __restrict__ 
       if (lo + 64 * r >= hi) break;
       const bool vp = n < hi;
       const int kp = pk[r].x;
+      if (!resp) {  // one label per point (uniform): no second pick to rank
+        const int dg = (kp >> shift) & 255;
+        uint64_t b[8], mv;
+        digit_ballots(vp, dg, b, &mv);
+        const uint64_t m = digit_match(dg, b, mv);
+        const int pos = loc[dg] + __popcll(m & lt);
+        wave_lds_fence();
+        if (vp) {
+          sk[pos] = kp;
+          sv[pos] = (int32_t)n;
+          if ((m & gt) == 0) loc[dg] = pos + 1;
+        }
+        wave_lds_fence();
+        continue;
+      }
       const bool vs = vp && pk[r].y >= 0 && r1[r] >= thr;
       const int ks = vs ? pk[r].y : 0;
       const int dp = (kp >> shift) & 255, ds = (ks >> shift) & 255;
