@@ -69,6 +69,11 @@ int gmm_version(void);
 const char* gmm_error_string(int code);
 
 /* Workspace bytes needed by every entry point below for this (N, d, K).
+ * The fused kernels keep the responsibilities on chip (Flash-GMM abstract:
+ * no N x K matrix in memory), so the scratch holds only the packed
+ * parameters, per-row normalisers of the two-pass regime (Turbo-GMM
+ * abstract: normalisers first, then a second score computation) and per-block
+ * statistics partials: O(N + K d) bytes, never O(N K).
  * Returns 0 for arguments outside the limits. */
 size_t gmm_workspace_bytes(int64_t N, int32_t d, int32_t K);
 
@@ -113,13 +118,26 @@ int gmm_estep_resp(const void* X, int32_t x_dtype, int64_t N, int32_t d,
 int gmm_mstep(const float* Nk, const float* Sx, const float* Sxx, int64_t N, int32_t d, int32_t K,
               float var_floor, float* mu, float* var, float* logw, void* stream);
 
-/* `iters` EM iterations on the device: E-step (AUTO regime) then M-step, all
+/* EM iterations (Turbo-GMM abstract: EM alternates the fused E-step with the
+ * parameter update; its fused kernels are equivalent to standard EM in real
+ * arithmetic). `iters` iterations on the device: E-step (AUTO regime) then M-step, all
  * enqueued on `stream` with nothing read back. loglik_hist (device, `iters`
  * doubles) receives the log-likelihood of the parameters before each M-step.
  * mu, var, logw are in/out. Needs N >= 1, iters >= 0. */
 int gmm_em_iterate(const void* X, int32_t x_dtype, int64_t N, int32_t d, int32_t K, int32_t iters,
                    float var_floor, float* mu, float* var, float* logw, double* loglik_hist,
                    void* workspace, size_t ws_bytes, void* stream);
+
+/* Launch-shape query (host only, touches no device): the plan that
+ * gmm_estep_stats_regime would use for (N, d, K, regime). info (host, 7
+ * int64) receives {regime taken (1 single, 2 two-pass, 3 small-K), waves per
+ * block, component slabs, rows per statistics chunk, number of chunks, 64-row
+ * tiles, scratch bytes this plan uses}. A chunk is the row range whose statistics one block (one slab's
+ * block in the two-pass regime) accumulates on chip across its tiles, so
+ * rows per chunk / 64 is the number of tiles a block walks (Turbo-GMM
+ * abstract: statistics accumulated on chip over the traversal). Returns the
+ * codes of gmm_estep_stats_regime for the same arguments. */
+int gmm_plan_info(int64_t N, int32_t d, int32_t K, int32_t regime, int64_t* info);
 
 /* Measurement aid (one-shot, per host thread): the next E-step enqueued by
  * this thread through gmm_estep_stats, gmm_estep_stats_regime or

@@ -126,7 +126,7 @@ def responsibilities(S, l=None):
 # E-step with sufficient statistics
 # ---------------------------------------------------------------------------
 
-def estep(X, mu, var, logw, *, form="difference", keep_R=False, row_chunk=_ROW_CHUNK):
+def estep(X, mu, var, logw, *, form="difference", keep_R=False, row_chunk=_ROW_CHUNK, abs_x=False):
     """Standard (unfused) E-step and sufficient statistics.
 
     For each row chunk: scores -> row log-sum-exp -> materialised R ->
@@ -134,7 +134,9 @@ def estep(X, mu, var, logw, *, form="difference", keep_R=False, row_chunk=_ROW_C
     (elementwise square). L = sum_n l_n.
 
     Returns a dict with Nk (K,), Sx (K,d), Sxx (K,d), l (N,), L (scalar) and,
-    if ``keep_R``, the full R (N,K).
+    if ``keep_R``, the full R (N,K); if ``abs_x``, also absx (K,d) =
+    sum_n r_nk |x_n| (elementwise), the magnitude against which a sum of
+    signed values such as Sx is judged.
     """
     X = _f64(X)
     mu, var, logw = _f64(mu), _f64(var), _f64(logw)
@@ -145,6 +147,7 @@ def estep(X, mu, var, logw, *, form="difference", keep_R=False, row_chunk=_ROW_C
     Sxx = np.zeros((K, d))
     l_all = np.empty(N)
     R_all = np.empty((N, K)) if keep_R else None
+    absx = np.zeros((K, d)) if abs_x else None
     for lo in range(0, N, row_chunk):
         hi = min(N, lo + row_chunk)
         x = X[lo:hi]
@@ -154,12 +157,16 @@ def estep(X, mu, var, logw, *, form="difference", keep_R=False, row_chunk=_ROW_C
         Nk += R.sum(axis=0)
         Sx += R.T @ x
         Sxx += R.T @ (x * x)
+        if abs_x:
+            absx += R.T @ np.abs(x)
         l_all[lo:hi] = l
         if keep_R:
             R_all[lo:hi] = R
     out = {"Nk": Nk, "Sx": Sx, "Sxx": Sxx, "l": l_all, "L": float(l_all.sum()) if N else 0.0}
     if keep_R:
         out["R"] = R_all
+    if abs_x:
+        out["absx"] = absx
     return out
 
 

@@ -18,6 +18,7 @@ namespace gmm {
 // Statistics contraction of the small-K kernel (gmm_set_stats_precision).
 static std::atomic<int> g_stats_precision{GMM_STATS_FP32};
 
+
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static int pow2_waves(int K) {
@@ -97,7 +98,8 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
   const size_t o_ivp = take((size_t)p.Kp * p.DP * sizeof(double));
   const size_t o_cmax = take((size_t)K * 4 * sizeof(float));
   const size_t o_errc = take(4 * sizeof(float));
-  const size_t o_rowref = take((size_t)std::max<int64_t>(N, 1) * sizeof(float2));
+  // per-row normalisers: only the two-pass regime has a first pass
+  const size_t o_rowref = take(regime == GMM_REGIME_TWOPASS ? (size_t)std::max<int64_t>(N, 1) * sizeof(float2) : 0);
   const size_t o_part = take((size_t)std::max<int64_t>(p.P, 1) * p.Kp * p.E * sizeof(float));
   const size_t o_ll = take((size_t)std::max<int64_t>(std::max(p.P, p.tiles), 1) * sizeof(double));
   const size_t o_stats = take((size_t)K * (1 + 2 * d) * sizeof(float));
@@ -121,7 +123,7 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
     p.ws.ivp = reinterpret_cast<double*>(b + o_ivp);
     p.ws.compmax = reinterpret_cast<float*>(b + o_cmax);
     p.ws.errc = reinterpret_cast<float*>(b + o_errc);
-    p.ws.rowref = reinterpret_cast<float2*>(b + o_rowref);
+    p.ws.rowref = regime == GMM_REGIME_TWOPASS ? reinterpret_cast<float2*>(b + o_rowref) : nullptr;
     p.ws.partials = reinterpret_cast<float*>(b + o_part);
     p.ws.llpart = reinterpret_cast<double*>(b + o_ll);
     p.ws.stats = reinterpret_cast<float*>(b + o_stats);
@@ -329,11 +331,17 @@ int gmm_estep_stats_chunked(const void* X_host, int32_t x_dtype, int64_t N, int3
   const size_t row_bytes = (size_t)d * (x_dtype == GMM_F32 ? 4 : 2);
   const char* xh = static_cast<const char*>(X_host);
 
+  // Both chunk plans (full chunks and the ragged tail) are built before
+  // anything is enqueued, so a rejected plan leaves the stream untouched.
+  Plan p, ptail;
+  const int64_t tail = N % L.chunk;
+  if (make_plan(L.chunk, d, K, GMM_REGIME_AUTO, workspace, &p) != GMM_OK) return GMM_EINVAL;
+  if (make_plan(tail ? tail : L.chunk, d, K, GMM_REGIME_AUTO, workspace, &ptail) != GMM_OK) return GMM_EINVAL;
+  if (p.bytes > L.plan_bytes || ptail.bytes > L.plan_bytes) return GMM_EWORKSPACE;
+
   std::lock_guard<std::mutex> lock(g_chunk_mutex);
   ChunkRes* r = nullptr;
   hipError_t e = chunk_resources(&r);
-  Plan p;
-  if (e == hipSuccess && make_plan(L.chunk, d, K, GMM_REGIME_AUTO, workspace, &p) != GMM_OK) return GMM_EINVAL;
   if (e == hipSuccess) e = launch_precompute(p, mu, var, logw, s);
   // the staging buffers may still be read by earlier work on `stream`
   if (e == hipSuccess) e = hipEventRecord(r->entry, s);
@@ -348,8 +356,7 @@ int gmm_estep_stats_chunked(const void* X_host, int32_t x_dtype, int64_t N, int3
                          r->copy);
     if (e == hipSuccess) e = hipEventRecord(r->copied[b], r->copy);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, r->copied[b], 0);
-    Plan pc;
-    if (e == hipSuccess && make_plan(n, d, K, GMM_REGIME_AUTO, workspace, &pc) != GMM_OK) return GMM_EINVAL;
+    const Plan& pc = n == L.chunk ? p : ptail;
     if (e == hipSuccess)
       e = launch_estep_accum(pc, stage[b], x_dtype, mu, acc, i == 0 ? 1 : 0,
                              loglik_point ? loglik_point + off : nullptr, s);
@@ -498,6 +505,16 @@ int gmm_kmeans_iterate(const void* X, int32_t x_dtype, int64_t N, int32_t d, int
     if (e == hipSuccess) e = kmeans_update_impl(X, x_dtype, N, d, assign, K, C, nullptr, w, L, s);
     if (e != hipSuccess) return GMM_EHIP;
   }
+  return GMM_OK;
+}
+
+int gmm_plan_info(int64_t N, int32_t d, int32_t K, int32_t regime, int64_t* info) {
+  if (!info) return GMM_EINVAL;
+  Plan p;
+  const int st = make_plan(N, d, K, regime, nullptr, &p);
+  if (st) return st;
+  const int64_t v[7] = {p.regime, p.waves, p.kslabs, p.rows_per_chunk, p.P, p.tiles, (int64_t)p.bytes};
+  for (int i = 0; i < 7; ++i) info[i] = v[i];
   return GMM_OK;
 }
 

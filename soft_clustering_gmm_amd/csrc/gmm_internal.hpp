@@ -89,9 +89,10 @@ struct ListsLayout {
 ListsLayout lists_layout(int64_t N, int K);
 hipError_t launch_border_lists(const int32_t* idx, const float* resp, int64_t N, int K, float thr,
                                int64_t* offsets, int32_t* members, void* workspace, hipStream_t stream);
-// Lloyd's k-means: nearest-centre assignment through the fp64 top-score pass
-// (the plan's parameters packed from centres, unit variances, zero
-// log-weights); dist2 and inertia (sum of dist2) are nullable.
+// Lloyd's k-means: nearest-centre assignment on the fp32 score tile with an
+// exact fp64 distance check of the centres the fp32 error bound cannot rule
+// out (the plan's parameters packed from centres, unit variances, zero
+// log-weights); dist2 and inertia (sum of the minima) are nullable.
 hipError_t launch_kmeans_assign(const Plan& p, const void* X, int x_dtype, int32_t* assign, float* dist2,
                                 double* inertia, hipStream_t stream);
 hipError_t launch_fill(float* a, int64_t n, float v, hipStream_t stream);

@@ -580,8 +580,10 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       //   nothing). Refined entries are then off by at most E * U, U = the
       //   unrefined mass; if that could exceed tau the window widens to every
       //   entry within 20 of the row maximum (e >= kExpWindow).
-      //  MODE 1: l_n is exact (first pass), an unrefined entry is off by
-      //   <= E r_k, and entries with r_k > tau / E are refined.
+      //  MODE 1: l_n comes from the first pass's fp64 scores (its sum of
+      //   exponentials takes each term in fp32, so l_n is off by ~1e-7, far
+      //   below tau); an unrefined entry is off by <= E r_k, and entries with
+      //   r_k > tau / E are refined.
       uint32_t mask = 0;
       if (MODE == 0) {
         const float zf = (float)z;

@@ -26,6 +26,7 @@ EXPORTS = (
     "gmm_set_timing_events", "gmm_set_stats_precision", "gmm_estep_stats_chunked", "gmm_workspace_bytes_chunked",
     "gmm_border_lists", "gmm_border_lists_workspace_bytes",
     "gmm_kmeans_assign", "gmm_kmeans_update", "gmm_kmeans_iterate", "gmm_kmeans_workspace_bytes",
+    "gmm_plan_info",
 )
 
 
@@ -79,6 +80,8 @@ def _load() -> ctypes.CDLL:
     L.gmm_kmeans_iterate.argtypes = [P, I32, I64, I32, I32, I32, P, P, P, SZ, P]
     L.gmm_kmeans_workspace_bytes.restype = SZ
     L.gmm_kmeans_workspace_bytes.argtypes = [I64, I32, I32]
+    L.gmm_plan_info.restype = ctypes.c_int
+    L.gmm_plan_info.argtypes = [I64, I32, I32, I32, P]
     return L
 
 
@@ -140,6 +143,14 @@ def _params(X, mu, var, logw):
     _need(var, "var", torch.float32, (K, d), dev)
     _need(logw, "logw", torch.float32, (K,), dev)
     return N, d, K, dev
+
+
+def plan_info(N: int, d: int, K: int, regime: int = REGIME_AUTO) -> dict:
+    """The launch shape gmm_estep_stats_regime takes for (N, d, K, regime) (host only)."""
+    buf = (ctypes.c_int64 * 7)()
+    _check("gmm_plan_info", lib().gmm_plan_info(N, d, K, regime, buf))
+    keys = ("regime", "waves", "kslabs", "rows_per_chunk", "chunks", "tiles", "scratch_bytes")
+    return dict(zip(keys, (int(v) for v in buf)))
 
 
 def workspace_bytes(N: int, d: int, K: int) -> int:

@@ -61,7 +61,27 @@ def test_workspace_bytes(L):
     assert L.gmm_workspace_bytes(1 << 20, 128, 256) % 256 == 0
 
 
+def test_plan_info_launch_shapes(L):
+    """Host-only launch-shape query: regime choice, slabs and tiles per block."""
+    from soft_clustering_gmm_amd import gmm
+    assert L.gmm_plan_info(10, 4, 3, 0, None) == -1
+    buf = (ctypes.c_int64 * 7)()
+    assert L.gmm_plan_info(10, 0, 3, 0, buf) == -1
+    assert L.gmm_plan_info(10, 4, 300, 1, buf) == -2
+    ref = gmm.plan_info(1 << 20, 128, 256)
+    assert ref["regime"] == 1 and ref["waves"] == 8 and ref["kslabs"] == 1 and ref["tiles"] == 16384
+    assert ref["chunks"] * ref["rows_per_chunk"] >= 1 << 20
+    lk = gmm.plan_info(1 << 22, 128, 4096)
+    assert lk["regime"] == 2 and lk["kslabs"] == 16
+    assert gmm.plan_info(1 << 24, 32, 16)["regime"] == 3
+    # the reduced-size cases of the multi-tile parity tests walk several tiles per block
+    assert gmm.plan_info(65536, 128, 4096)["rows_per_chunk"] // 64 >= 32
+    assert gmm.plan_info(131072, 96, 1024)["rows_per_chunk"] // 64 >= 16
+    assert gmm.plan_info(65536, 96, 256)["rows_per_chunk"] // 64 >= 4
+
+
 FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation first
+
 
 
 def _estep(L, X=FAKE, xt=0, N=100, d=4, K=3, ws=FAKE, wsb=1 << 40, regime=0, nk=FAKE):

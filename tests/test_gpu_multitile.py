@@ -1,0 +1,169 @@
+"""GPU parity at sizes where every block walks many 64-row tiles.
+
+The fused kernels keep a block's statistics in registers across all the
+tiles of its row chunk, double-buffer the X tiles (16-byte global->LDS
+copies for fp32 rows, a register prefetch widened into LDS for half-precision
+rows) and, in the two-pass regime, run one block per (chunk, 256-component
+slab). At the small sizes of the element-wise tests every block takes a
+single tile, so none of that machinery is reached there. These cases are
+sized so that each block walks 4 to 64 tiles (asserted through the
+launch-shape query), and compare against the float64 oracle:
+
+  * all of Nk, Sx, Sxx and L (expanded form, BLAS) at the 1e-4 bars;
+  * l_n of every row against the oracle;
+  * the responsibilities of 256 seeded rows, taken from R materialised by a
+    launch of the same shape (same N, d, K, regime: same plan);
+  * with the split-bf16 statistics contraction: statistics against the
+    oracle, l_n bitwise those of the fp32 contraction.
+
+The IVF recipe's EM iterations are teacher-forced: each GPU E-step and
+M-step is compared with the oracle on the GPU's own parameters.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from soft_clustering_gmm_amd import datagen
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture()
+def G():
+    from soft_clustering_gmm_amd import gmm
+    gmm.lib()
+    gmm.set_stats_precision(gmm.STATS_FP32)
+    yield gmm
+    gmm.set_stats_precision(gmm.STATS_FP32)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def _xdev(X, xkind):
+    """X on the device as float32, float16 or bfloat16, and the values the oracle sees."""
+    if xkind == "f32":
+        return dev(X.astype(np.float32)), X.astype(np.float32)
+    if xkind == "f16":
+        Xh = X.astype(np.float16)
+        return dev(Xh), Xh.astype(np.float32)
+    Xb = torch.from_numpy(np.ascontiguousarray(X, dtype=np.float32)).to(torch.bfloat16)
+    return Xb.to("cuda"), Xb.float().numpy()
+
+
+def _check_case(G, Xd, Xv, mu, var, logw, regime, what, min_tiles, split=(False,), sample=256):
+    N, d = Xv.shape
+    K = mu.shape[0]
+    info = G.plan_info(N, d, K, regime)
+    tiles = info["rows_per_chunk"] // 64
+    print(f"{what}: N={N} d={d} K={K} plan {info}, {tiles} tiles per block", flush=True)
+    assert tiles >= min_tiles, f"{what}: only {tiles} tiles per block"
+    ref = oracle.estep(Xv, mu, var, logw, form="expanded", row_chunk=4096, abs_x=True)
+    rows = np.sort(np.random.default_rng(99).choice(N, min(sample, N), replace=False))
+    l_rows, R_rows = oracle.estep_rows(Xv, mu, var, logw, rows)
+    args = (Xd, dev(mu), dev(var), dev(logw))
+    l_fp32 = None
+    for sp in split:
+        G.set_stats_precision(G.STATS_SPLIT_BF16 if sp else G.STATS_FP32)
+        tag = f"{what} {'split-bf16' if sp else 'fp32'}"
+        Nk, Sx, Sxx, L, lp = G.estep_stats(*args, regime=regime, want_point_loglik=True)
+        torch.cuda.synchronize()
+        es = parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, None, ref["absx"], tag)
+        parity.check_total(host(L), ref, tag)
+        el = parity.check_loglik_point(host(lp), ref["l"], tag + " l_n (all rows)")
+        parity.check_loglik_point(host(lp)[rows], l_rows, tag + " l_n (sampled, difference form)")
+        if l_fp32 is None:
+            l_fp32 = host(lp)
+            R, lr = G.estep_resp(*args, regime=regime)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(lr), l_fp32), f"{tag}: l_n of the resp launch differs"
+            er = parity.check_resp(host(R[torch.from_numpy(rows).to("cuda")]), R_rows, tag + " sampled r")
+            del R
+        else:
+            assert np.array_equal(host(lp), l_fp32), f"{tag}: l_n differs from the fp32 contraction"
+            er = float("nan")
+        print(f"{tag}: stats {es[0]:.1e}/{es[1]:.1e}/{es[2]:.1e}  l_n {el:.1e}  sampled |dr| {er:.1e}",
+              flush=True)
+        G.set_stats_precision(G.STATS_FP32)
+    return ref
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.1])
+def test_two_pass_fp32_many_tiles(G, scale):
+    """largek recipe at N = 65536: 16 slabs, 64 tiles per block, fp32 X through the
+    asynchronous global->LDS tile copies (scale 0.1: dense responsibilities)."""
+    X, mu, var, logw = datagen.make_workload("largek", N=65536, centre_scale=scale)
+    Xd, Xv = _xdev(X, "f32")
+    _check_case(G, Xd, Xv, mu, var, logw, 2, f"largek x{scale}", 32, split=(False, True))
+
+
+def test_two_pass_fp16_prefetch_many_tiles(G):
+    """ivf recipe at N = 131072, X in fp16: 4 slabs, 32 tiles per block, the
+    half-precision register prefetch of the next tile."""
+    X, mu, var, logw = datagen.make_workload("ivf", N=131072)
+    Xd, Xv = _xdev(X, "f16")
+    _check_case(G, Xd, Xv, mu, var, logw, 2, "ivf fp16", 16, split=(False, True))
+
+
+@pytest.mark.parametrize("xkind", ["bf16", "f16", "f32"])
+def test_single_sweep_d96_many_tiles(G, xkind):
+    """Single sweep, d = 96 (three feature tiles), K = 256, N = 65536: 4 tiles
+    per block through the half-precision prefetch (bf16, fp16) or the
+    asynchronous fp32 copies."""
+    X, mu, var, logw = datagen.random_problem(4096, 65536, 96, 256)
+    Xd, Xv = _xdev(X, xkind)
+    _check_case(G, Xd, Xv, mu, var, logw, 1, f"single d=96 {xkind}", 4, split=(False, True))
+
+
+@pytest.mark.parametrize("N,d,K", [(262144, 32, 64), (131072, 64, 128), (131072, 99, 200)])
+def test_single_sweep_narrow_many_tiles(G, N, d, K):
+    """Single sweep with one, two or four waves per block and one to four feature
+    tiles (d = 99: ragged rows through the element-wise tile load), 4 tiles per block."""
+    X, mu, var, logw = datagen.random_problem(5000 + d, N, d, K)
+    Xd, Xv = _xdev(X, "f32")
+    _check_case(G, Xd, Xv, mu, var, logw, 1, f"single N={N} d={d} K={K}", 4)
+
+
+def test_ivf_em_teacher_forced_many_tiles(G):
+    """Five EM iterations of the ivf recipe at N = 131072 (fp16 X, two-pass):
+    each GPU E-step against the oracle on the GPU's own parameters, each
+    M-step against the oracle's M-step on the GPU's statistics; then the
+    on-device loop reproduces the step-by-step run bit for bit."""
+    X, mu, var, logw = datagen.make_workload("ivf", N=131072)
+    Xd, Xv = _xdev(X, "f16")
+    N = Xv.shape[0]
+    floor = 1e-6
+    mud, vard, lwd = dev(mu.copy()), dev(var.copy()), dev(logw.copy())
+    hist = []
+    for t in range(5):
+        m0, v0, w0 = host(mud), host(vard), host(lwd)
+        Nk, Sx, Sxx, L, lp = G.estep_stats(Xd, mud, vard, lwd, want_point_loglik=True)
+        torch.cuda.synchronize()
+        ref = oracle.estep(Xv, m0, v0, w0, form="expanded", row_chunk=4096, abs_x=True)
+        what = f"ivf EM iteration {t}"
+        parity.check_loglik_point(host(lp), ref["l"], what)
+        es = parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, None, ref["absx"], what)
+        parity.check_total(host(L), ref, what)
+        hist.append(float(L))
+        G.mstep(Nk, Sx, Sxx, N, floor, mud, vard, lwd)
+        torch.cuda.synchronize()
+        rm, rv, rl = oracle.mstep(host(Nk), host(Sx), host(Sxx), N, floor, m0, v0)
+        np.testing.assert_allclose(host(mud), rm.astype(np.float32), rtol=1e-6, atol=1e-6)
+        np.testing.assert_allclose(host(vard), rv.astype(np.float32), rtol=1e-6, atol=1e-7)
+        np.testing.assert_allclose(host(lwd), rl.astype(np.float32), rtol=1e-6, atol=1e-6)
+        print(f"{what}: L {float(L):.6e}  stats {es[0]:.1e}/{es[1]:.1e}/{es[2]:.1e}", flush=True)
+    hist = np.array(hist)
+    assert (np.diff(hist) >= -1e-6 * np.abs(hist[:-1])).all(), hist
+    mu2, var2, lw2 = dev(mu.copy()), dev(var.copy()), dev(logw.copy())
+    h2 = G.em_iterate(Xd, mu2, var2, lw2, 5, floor)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(h2), hist)
+    assert torch.equal(mu2, mud) and torch.equal(var2, vard) and torch.equal(lw2, lwd)

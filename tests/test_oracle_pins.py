@@ -108,6 +108,30 @@ def test_estep_matches_mpmath_bruteforce(name):
     assert abs(e["L"] - L) <= 1e-12 * max(1.0, abs(L))
 
 
+@pytest.mark.parametrize("name", ["estep_tiny_a.json", "estep_tiny_b.json"])
+def test_estep_rows_matches_mpmath_bruteforce_on_row_subsets(name):
+    """The sampled-row E-step returns, for rows given in any order (repeats
+    allowed), exactly the brute-force l_n and r_n. of those rows."""
+    X, mu, var, logw, R, l, *_ = _load_golden(name)
+    rows = np.array([X.shape[0] - 1, 0, X.shape[0] // 2, 0])
+    for form in ("difference", "expanded"):
+        lr, Rr = oracle.estep_rows(X, mu, var, logw, rows, form=form)
+        np.testing.assert_allclose(lr, l[rows], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(Rr, R[rows], atol=1e-12)
+
+
+def test_estep_rows_matches_sklearn_on_selected_rows():
+    X, mu, var, logw = datagen.random_problem(6, 400, 5, 7)
+    w = np.exp(logw.astype(np.float64))
+    logw = np.log(w / w.sum())
+    g = _sklearn_gmm(mu, var, logw)
+    rows = np.random.default_rng(0).choice(400, 37, replace=False)
+    lr, Rr = oracle.estep_rows(X, mu, var, logw, rows)
+    xs = X[rows].astype(np.float64)
+    np.testing.assert_allclose(lr, g.score_samples(xs), rtol=1e-12, atol=1e-10)
+    np.testing.assert_allclose(Rr, g.predict_proba(xs), atol=1e-12)
+
+
 def test_top2_matches_plain_scan_with_ties():
     rng = np.random.default_rng(5)
     X, mu, var, logw = datagen.random_problem(5, 40, 3, 6)
@@ -244,6 +268,20 @@ def test_point_permutation_and_additivity_of_stats():
         np.testing.assert_allclose(b[key], a[key], rtol=1e-12, atol=1e-11)
         np.testing.assert_allclose(h1[key] + h2[key], a[key], rtol=1e-12, atol=1e-11)
     assert abs(h1["L"] + h2["L"] - a["L"]) < 1e-9
+
+
+@pytest.mark.parametrize("name", ["estep_tiny_a.json", "estep_tiny_b.json"])
+def test_abs_weighted_scale_matches_bruteforce_and_closed_forms(name):
+    """absx = sum_n r_nk |x_n|: against the brute-force R of the golden file,
+    equal to Sx when X >= 0 (elementwise), and to sum_n |x_n| when K = 1."""
+    X, mu, var, logw, R, *_ = _load_golden(name)
+    e = oracle.estep(X, mu, var, logw, abs_x=True)
+    np.testing.assert_allclose(e["absx"], R.T @ np.abs(X), rtol=1e-12, atol=1e-12)
+    Xp = np.abs(X)
+    p = oracle.estep(Xp, mu, var, logw, abs_x=True)
+    np.testing.assert_allclose(p["absx"], p["Sx"], rtol=1e-14, atol=0)
+    one = oracle.estep(X, mu[:1], var[:1], np.zeros(1), abs_x=True)
+    np.testing.assert_allclose(one["absx"][0], np.abs(X).sum(axis=0), rtol=1e-13)
 
 
 def test_expanded_form_agrees_with_difference_form():
