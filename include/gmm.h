@@ -49,7 +49,8 @@ enum gmm_status {
   GMM_EINVAL = -1,        /* null pointer, negative size, bad dtype or regime */
   GMM_EUNSUPPORTED = -2,  /* shape beyond the limits above, or regime not possible */
   GMM_EWORKSPACE = -3,    /* workspace NULL, too small or misaligned */
-  GMM_EHIP = -4           /* a HIP launch failed (see hipGetLastError) */
+  GMM_EHIP = -4,          /* a HIP launch failed (see hipGetLastError) */
+  GMM_ESCRATCH = -5       /* gmm_estep_stats_static: shape needs more than its static scratch */
 };
 
 enum gmm_dtype { GMM_F32 = 0, GMM_F16 = 1, GMM_BF16 = 2 };
@@ -92,6 +93,25 @@ int gmm_estep_stats(const void* X, int32_t x_dtype, int64_t N, int32_t d,
                     float* Nk, float* Sx, float* Sxx,
                     double* loglik_total, float* loglik_point,
                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Allocation-free E-step, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): gmm_estep_stats (AUTO regime, same kernels, same results bit
+ * for bit) without a workspace argument. It calls no hipMalloc, hipFree or
+ * allocating library routine. Its scratch is a static device array of
+ * GMM_STATIC_SCRATCH_MIB MiB that the library holds on every GPU it runs on
+ * until the process ends (its address is looked up once per device, on the
+ * first call there). Shapes whose workspace plan needs more than that
+ * return GMM_ESCRATCH before anything is enqueued; for reference,
+ * N = 1,048,576, d = 128, K = 256 needs about 68 MiB. Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (concurrent streams,
+ * threads) race and give wrong results, so order them on one stream.
+ * Arguments and outputs as in gmm_estep_stats. */
+#define GMM_STATIC_SCRATCH_MIB 128
+int gmm_estep_stats_static(const void* X, int32_t x_dtype, int64_t N, int32_t d,
+                           const float* mu, const float* var, const float* logw, int32_t K,
+                           float* Nk, float* Sx, float* Sxx,
+                           double* loglik_total, float* loglik_point, void* stream);
 
 /* gmm_estep_stats with the regime forced (GMM_REGIME_SINGLE needs K <= 256,
  * GMM_REGIME_SMALLK needs K <= 16 and d <= 64; otherwise GMM_EUNSUPPORTED). */

@@ -18,6 +18,39 @@ namespace gmm {
 // Statistics contraction of the small-K kernel (gmm_set_stats_precision).
 static std::atomic<int> g_stats_precision{GMM_STATS_FP32};
 
+// Scratch of the allocation-free E-step (gmm_estep_stats_static): one array
+// per GPU, allocated with the code object and held until the process ends.
+// In host code `scratch` names a host-side stand-in, never the device
+// memory: kernels and copies get the per-device address that
+// hipGetSymbolAddress returns (static_scratch below).
+constexpr size_t kStaticScratchBytes = (size_t)GMM_STATIC_SCRATCH_MIB << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+#define GMM_STR2(x) #x
+#define GMM_STR(x) GMM_STR2(x)
+
+static std::mutex g_scratch_mutex;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this GPU's scratch array, looked up once per device
+// with that device current.
+static hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256 != 0) return hipErrorInvalidValue;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -228,6 +261,9 @@ const char* gmm_error_string(int code) {
       return "unsupported shape or regime (1<=d<=128, 1<=K<=65536; single sweep needs K<=256, small-K K<=16 and d<=64)";
     case GMM_EWORKSPACE: return "workspace missing, misaligned (256 B) or smaller than gmm_workspace_bytes()";
     case GMM_EHIP: return "HIP launch failed";
+    case GMM_ESCRATCH:
+      return "the allocation-free E-step needs more scratch for this shape than its static array holds "
+             "(" GMM_STR(GMM_STATIC_SCRATCH_MIB) " MiB per GPU); use gmm_estep_stats with a workspace";
     default: return "unknown status";
   }
 }
@@ -259,6 +295,29 @@ int gmm_estep_stats(const void* X, int32_t x_dtype, int64_t N, int32_t d, const 
                     float* loglik_point, void* workspace, size_t ws_bytes, void* stream) {
   return gmm_estep_stats_regime(X, x_dtype, N, d, mu, var, logw, K, Nk, Sx, Sxx, loglik_total, loglik_point,
                                 workspace, ws_bytes, GMM_REGIME_AUTO, stream);
+}
+
+int gmm_estep_stats_static(const void* X, int32_t x_dtype, int64_t N, int32_t d, const float* mu,
+                           const float* var, const float* logw, int32_t K, float* Nk, float* Sx, float* Sxx,
+                           double* loglik_total, float* loglik_point, void* stream) {
+  int st = check_common(X, x_dtype, N, d, K, mu, var, logw);
+  if (st) return st;
+  if (!Nk || !Sx || !Sxx || !loglik_total) return GMM_EINVAL;
+  Plan p;
+  if ((st = make_plan(N, d, K, GMM_REGIME_AUTO, nullptr, &p))) return st;
+  if (p.bytes > kStaticScratchBytes) return GMM_ESCRATCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) return hip_status(launch_zero_outputs(Nk, Sx, Sxx, d, K, loglik_total, s));
+  void* base = nullptr;
+  hipError_t e = static_scratch(&base);
+  if (e != hipSuccess) return GMM_EHIP;
+  make_plan(N, d, K, GMM_REGIME_AUTO, base, &p);
+  // Every kernel of the E-step writes the scratch regions it later reads
+  // (packed parameters, per-block partials, block sums), so nothing left by
+  // an earlier call is read.
+  e = launch_precompute(p, mu, var, logw, s);
+  if (e == hipSuccess) e = launch_estep(p, X, x_dtype, mu, Nk, Sx, Sxx, loglik_total, loglik_point, nullptr, s);
+  return hip_status(e);
 }
 
 int gmm_estep_resp(const void* X, int32_t x_dtype, int64_t N, int32_t d, const float* mu, const float* var,

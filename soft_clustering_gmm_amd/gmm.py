@@ -26,7 +26,7 @@ EXPORTS = (
     "gmm_set_timing_events", "gmm_set_stats_precision", "gmm_estep_stats_chunked", "gmm_workspace_bytes_chunked",
     "gmm_border_lists", "gmm_border_lists_workspace_bytes",
     "gmm_kmeans_assign", "gmm_kmeans_update", "gmm_kmeans_iterate", "gmm_kmeans_workspace_bytes",
-    "gmm_plan_info",
+    "gmm_plan_info", "gmm_estep_stats_static",
 )
 
 
@@ -82,6 +82,8 @@ def _load() -> ctypes.CDLL:
     L.gmm_kmeans_workspace_bytes.argtypes = [I64, I32, I32]
     L.gmm_plan_info.restype = ctypes.c_int
     L.gmm_plan_info.argtypes = [I64, I32, I32, I32, P]
+    L.gmm_estep_stats_static.restype = ctypes.c_int
+    L.gmm_estep_stats_static.argtypes = [P, I32, I64, I32, P, P, P, I32, P, P, P, P, P, P]
     return L
 
 
@@ -183,6 +185,21 @@ def estep_stats(X, mu, var, logw, *, regime: int = REGIME_AUTO, want_point_logli
     _check("gmm_estep_stats_regime", lib().gmm_estep_stats_regime(
         _ptr(X), _xtype(X), N, d, _ptr(mu), _ptr(var), _ptr(logw), K, _ptr(Nk), _ptr(Sx), _ptr(Sxx),
         _ptr(L), _ptr(lp), _ptr(ws), ws.numel(), regime, _stream(dev)))
+    return Nk, Sx, Sxx, L, lp
+
+
+def estep_stats_static(X, mu, var, logw, *, want_point_loglik: bool = False):
+    """Allocation-free fused E-step (the library's static per-GPU scratch, no
+    workspace): returns the estep_stats outputs. Calls on one GPU must not overlap."""
+    N, d, K, dev = _params(X, mu, var, logw)
+    Nk = torch.empty(K, dtype=torch.float32, device=dev)
+    Sx = torch.empty(K, d, dtype=torch.float32, device=dev)
+    Sxx = torch.empty(K, d, dtype=torch.float32, device=dev)
+    L = torch.empty((), dtype=torch.float64, device=dev)
+    lp = torch.empty(N, dtype=torch.float32, device=dev) if want_point_loglik else None
+    _check("gmm_estep_stats_static", lib().gmm_estep_stats_static(
+        _ptr(X), _xtype(X), N, d, _ptr(mu), _ptr(var), _ptr(logw), K, _ptr(Nk), _ptr(Sx), _ptr(Sxx),
+        _ptr(L), _ptr(lp), _stream(dev)))
     return Nk, Sx, Sxx, L, lp
 
 

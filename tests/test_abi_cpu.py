@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_error_strings(L):
     assert L.gmm_version() == 10000
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert len(L.gmm_error_string(code)) >= 2
     assert L.gmm_error_string(-99) == b"unknown status"
 
@@ -82,6 +82,25 @@ def test_plan_info_launch_shapes(L):
 
 FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation first
 
+
+def test_static_entry_point_rejects_on_the_host(L):
+    """The allocation-free E-step validates its arguments and rejects shapes whose
+    plan needs more than the static scratch, before touching any device."""
+    from soft_clustering_gmm_amd import gmm
+
+    def call(X=FAKE, xt=0, N=100, d=4, K=3, nk=FAKE):
+        return L.gmm_estep_stats_static(X, xt, N, d, FAKE, FAKE, FAKE, K, nk, FAKE, FAKE, FAKE, None, None)
+
+    assert call(d=0) == -1 and call(xt=9) == -1 and call(X=None) == -1 and call(nk=None) == -1
+    assert call(d=129) == -2
+    cap = 128 << 20
+    big = gmm.plan_info(1 << 22, 128, 4096)["scratch_bytes"]
+    assert big > cap and call(N=1 << 22, d=128, K=4096) == -5
+    assert b"static" in L.gmm_error_string(-5) and b"128 MiB" in L.gmm_error_string(-5)
+    ref = gmm.plan_info(1 << 20, 128, 256)["scratch_bytes"]
+    assert ref <= cap, ref  # the headline shape fits (the header quotes about 68 MiB)
+    assert abs(ref / 2 ** 20 - 68) < 1.5
+    assert gmm.plan_info(1 << 24, 32, 16)["scratch_bytes"] < 16 << 20  # small-K: no per-row region
 
 
 def _estep(L, X=FAKE, xt=0, N=100, d=4, K=3, ws=FAKE, wsb=1 << 40, regime=0, nk=FAKE):
