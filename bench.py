@@ -15,8 +15,13 @@ Prints one JSON line with, besides the required keys,
                  stream), against the FP32 MFMA peak, plus its algorithmic
                  HBM rate; `traffic` comes from committed rocprofv3 counter
                  readings when they were taken on the current kernel source
-  cpu_baseline - the float64 oracle's E-step on a bounded row sample of the
-                 same workload, on this host, single-threaded
+  cpu_baseline - the float64 oracle's E-step (expanded form: two BLAS
+                 products per row chunk) on the same workload, on every
+                 host core this process may use, at full N where that takes
+                 under ~20 s, else on a leading row sample
+  measured peaks - the FP32 matrix-core issue rate and the HBM read rate
+                 this GPU sustains (the library's peak probes), so that the
+                 roofline fraction is also quoted against measured peaks
 """
 from __future__ import annotations
 
@@ -39,7 +44,11 @@ PEAK_FP64_MFMA_TFLOPS = 78.6
 PEAK_HBM_GBPS = 8000.0
 VAR_FLOOR = 1e-6
 KERNEL_SRC = os.path.join(ROOT, "soft_clustering_gmm_amd", "csrc", "gmm_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ref_estep_stats.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+# Rough fp64 work the oracle's expanded form does per second on one modern
+# host core (two GEMMs of 2d per point x component, plus the exponentials):
+# only used to choose the row sample so that the baseline takes ~20 s.
+CPU_BUDGET_POINT_COMP_D = 2.5e10
 
 
 def kernel_source_hash() -> str:
@@ -47,30 +56,80 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def committed_traffic(workload: str):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, if still current."""
-    if workload != "ref" or not os.path.exists(TRAFFIC_FILE):
-        return None
-    with open(TRAFFIC_FILE) as f:
-        t = json.load(f)
+def committed_counters(workload: str, stats_precision: str):
+    """rocprofv3 counter readings committed for this workload's fused E-step (HBM
+    bytes and executed MFMA flops per launch), if taken on the current kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return {}
+    with open(COUNTERS_FILE) as f:
+        table = json.load(f)
+    t = table.get(f"{workload}/{stats_precision}", {})
     if t.get("kernel_source_sha256_16") != kernel_source_hash():
-        return None
-    return t.get("hbm_bytes_per_launch")
+        return {}
+    return t
 
 
-def cpu_baseline(X, mu, var, logw, rows: int):
-    """The oracle's E-step (as it stands) on the first `rows` rows, one thread."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(X, mu, var, logw, max_rows: int | None = None):
+    """The oracle's E-step (as it stands, expanded form) on every core this process may use:
+    full N when it fits the time budget, else the leading rows, scaled to the metric's unit."""
     import oracle
     from threadpoolctl import threadpool_limits
-    x = np.ascontiguousarray(X[:rows])
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        oracle.estep(x, mu, var, logw)
-        dt = time.perf_counter() - t0
+    N, d = X.shape
     K = mu.shape[0]
-    return {"value": rows * K / dt, "unit": UNIT, "cores": 1, "kind": "oracle",
-            "sample": f"float64 oracle E-step + statistics (difference form, materialised R) on the first "
-                      f"{rows} of {X.shape[0]} rows, same parameters; {dt:.2f} s on 1 host thread"}
+    cores = len(os.sched_getaffinity(0))
+    rows = int(min(N, max(4096, CPU_BUDGET_POINT_COMP_D * cores / (K * d))))
+    if max_rows:
+        rows = min(rows, max_rows)
+    x = np.ascontiguousarray(X[:rows])
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        oracle.estep(x, mu, var, logw, form="expanded", row_chunk=8192)
+        dt = time.perf_counter() - t0
+    what = "all" if rows == N else f"the first {rows} of"
+    return {"value": rows * K / dt, "unit": UNIT, "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"float64 oracle E-step + statistics, expanded form (scores from two BLAS products, "
+                      f"materialised R per 8192-row chunk), on {what} {N} rows, same parameters; {dt:.2f} s "
+                      f"with BLAS on {cores} threads ({cpu_model()})"}
+
+
+def measured_peaks(torch, gmm, dev, reps: int = 5):
+    """FP32 matrix-core issue rate and HBM read rate of this GPU from the library's
+    peak probes (best of `reps` launches each, timed with events on the probes' stream)."""
+    out = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    res = {}
+    for name, launch in (
+            ("mfma_f32_tflops", lambda: gmm.peak_mfma(gmm.PEAK_FP32, 20000, 2048, out)),
+            ("mfma_f64_tflops", lambda: gmm.peak_mfma(gmm.PEAK_FP64, 10000, 2048, out)),
+            ("hbm_read_gbps", lambda: gmm.peak_hbm_read(buf, 2048, out))):
+        launch()  # warm-up
+        best = 0.0
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            work = launch()
+            b.record()
+            b.synchronize()
+            rate = work / (a.elapsed_time(b) * 1e-3)
+            best = max(best, rate)
+        res[name] = round(best / (1e12 if "tflops" in name else 1e9), 1)
+    del buf
+    res["probes"] = ("gmm_peak_mfma: 2048 blocks x 4 waves, 8 independent MFMAs per trip (32x32x2 fp32 / "
+                     "16x16x4 fp64); gmm_peak_hbm_read: 4 GiB read once, 16-byte loads, 2048 blocks x 256")
+    return res
 
 
 def host_streamed(args, w, X, mu, var, logw, torch, gmm, dev):
@@ -254,7 +313,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ref", choices=["tiny", "ref", "smallk", "largek", "ivf"])
-    ap.add_argument("--cpu-rows", type=int, default=131072, help="row sample for the oracle baseline (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=-1,
+                    help="row cap for the oracle baseline (-1: as many as fit ~20 s, full N where possible; 0: skip)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
     ap.add_argument("--x-on-host", action="store_true",
                     help="keep X in pinned host memory and stream it through the row-chunked E-step "
                          "(PCIe-inclusive rate; not the HBM-resident headline)")
@@ -334,9 +395,14 @@ def main(argv=None):
     kernel = (f"estep_small_kernel<{-(-d // 16)},{ctype},{sp}> (small K)" if small
               else f"estep_stats_kernel<{-(-d // 32)},0,{ctype},{sp}> (single sweep)" if single
               else f"estep_lse_kernel + estep_stats_kernel<{-(-d // 32)},1,{ctype},{sp}> (two-pass)")
+    ctr = committed_counters(args.workload, args.stats_precision)
+    executed = ctr.get("executed_flops_per_launch")
     roof = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": committed_traffic(args.workload),
+        "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": ctr.get("hbm_bytes_per_launch"),
+        "executed_frac": (round(executed / (k_avg * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)
+                          if executed else None),
+        "executed_flops_per_launch": executed,
         "kernel": kernel,
         "flops_per_launch": flops, "avg_launch_ms": round(k_avg, 4),
         "p90_launch_ms": round(float(np.percentile(k_ms, 90)), 4),
@@ -361,8 +427,13 @@ def main(argv=None):
                    "stats_precision": args.stats_precision},
         "roofline": roof,
     }
-    if args.cpu_rows > 0:
-        out["cpu_baseline"] = cpu_baseline(X, mu, var, logw, min(args.cpu_rows, N))
+    if not args.no_peaks:
+        pk = measured_peaks(torch, gmm, dev)
+        roof["measured_peak"] = pk
+        roof["frac_of_measured_peak"] = round(achieved / pk["mfma_f32_tflops"], 4)
+        roof["hbm_frac_of_measured_peak"] = round(xbytes / (k_avg * 1e-3) / 1e9 / pk["hbm_read_gbps"], 4)
+    if args.cpu_rows != 0:
+        out["cpu_baseline"] = cpu_baseline(X, mu, var, logw, args.cpu_rows if args.cpu_rows > 0 else None)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -4,6 +4,7 @@
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -12,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgmm_mi355x.so")
-SOURCES = ["gmm_kernels.hip", "gmm_lists.hip", "gmm_api.cpp"]
+SOURCES = ["gmm_kernels.hip", "gmm_lists.hip", "gmm_api.cpp", "gmm_peaks.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are disabled for all device code; the kernels' fp32
@@ -32,12 +33,16 @@ def build(verbose: bool = False) -> str:
     objs = []
     tmpdir = os.path.join(HERE, "_build")
     os.makedirs(tmpdir, exist_ok=True)
+    cmds = []
     for src in SOURCES:
         obj = os.path.join(tmpdir, src + ".o")
-        cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-               "-Wall", "-Wno-unused-result", *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
-        _run(cmd, verbose)
+        cmds.append([hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+                     "-Wall", "-Wno-unused-result", *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    # the translation units are independent: compile them side by side
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as pool:
+        for f in [pool.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     tmp_lib = LIB + ".tmp"
     _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib], verbose)
     os.replace(tmp_lib, LIB)

@@ -27,7 +27,9 @@ EXPORTS = (
     "gmm_border_lists", "gmm_border_lists_workspace_bytes",
     "gmm_kmeans_assign", "gmm_kmeans_update", "gmm_kmeans_iterate", "gmm_kmeans_workspace_bytes",
     "gmm_plan_info", "gmm_estep_stats_static",
+    "gmm_peak_mfma", "gmm_peak_mfma_flops", "gmm_peak_hbm_read",
 )
+PEAK_FP32, PEAK_FP64 = 0, 1
 
 
 class GmmError(RuntimeError):
@@ -82,6 +84,12 @@ def _load() -> ctypes.CDLL:
     L.gmm_kmeans_workspace_bytes.argtypes = [I64, I32, I32]
     L.gmm_plan_info.restype = ctypes.c_int
     L.gmm_plan_info.argtypes = [I64, I32, I32, I32, P]
+    L.gmm_peak_mfma.restype = ctypes.c_int
+    L.gmm_peak_mfma.argtypes = [I32, I64, I32, P, P]
+    L.gmm_peak_mfma_flops.restype = ctypes.c_double
+    L.gmm_peak_mfma_flops.argtypes = [I32, I64, I32]
+    L.gmm_peak_hbm_read.restype = ctypes.c_int
+    L.gmm_peak_hbm_read.argtypes = [P, SZ, I32, P, P]
     L.gmm_estep_stats_static.restype = ctypes.c_int
     L.gmm_estep_stats_static.argtypes = [P, I32, I64, I32, P, P, P, I32, P, P, P, P, P, P]
     return L
@@ -368,3 +376,16 @@ def kmeans_iterate(X, C, iters: int, *, ws=None):
     _check("gmm_kmeans_iterate", lib().gmm_kmeans_iterate(
         _ptr(X), _xtype(X), N, d, K, iters, _ptr(C), _ptr(hist), _ptr(ws), ws.numel(), _stream(dev)))
     return hist[:iters]
+
+
+def peak_mfma(precision: int, trips: int, blocks: int, out: torch.Tensor) -> float:
+    """Enqueues the matrix-core issue loop on the current stream; returns the flops it executes."""
+    _check("gmm_peak_mfma", lib().gmm_peak_mfma(precision, trips, blocks, _ptr(out), _stream(out.device)))
+    return float(lib().gmm_peak_mfma_flops(precision, trips, blocks))
+
+
+def peak_hbm_read(buf: torch.Tensor, blocks: int, out: torch.Tensor) -> int:
+    """Enqueues the HBM read stream over buf on the current stream; returns the bytes it reads."""
+    nbytes = buf.numel() * buf.element_size() // 16 * 16
+    _check("gmm_peak_hbm_read", lib().gmm_peak_hbm_read(_ptr(buf), nbytes, blocks, _ptr(out), _stream(buf.device)))
+    return nbytes

@@ -7,14 +7,15 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gmm.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gmm.h", "gmm_peaks.h")]
 LIB = os.path.join(ROOT, "soft_clustering_gmm_amd", "libgmm_mi355x.so")
 
 P = ctypes.c_void_p
 
 
 def declared():
-    src = open(HEADER).read()
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == sorted(os.path.basename(h) for h in HEADERS)
+    src = "\n".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(gmm_[a-z0-9_]+)\s*\(", src)))
 
@@ -34,6 +35,17 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, n), n
     from soft_clustering_gmm_amd import gmm
     assert set(gmm.EXPORTS) == set(names)
+
+
+def test_peak_probes_validate_on_the_host(L):
+    assert L.gmm_peak_mfma(2, 10, 4, FAKE, None) == -1
+    assert L.gmm_peak_mfma(0, 0, 4, FAKE, None) == -1
+    assert L.gmm_peak_mfma(0, 10, 4, None, None) == -1
+    assert L.gmm_peak_mfma_flops(0, 10, 4) == 8 * 4096 * 4 * 4 * 10
+    assert L.gmm_peak_mfma_flops(1, 10, 4) == 8 * 2048 * 4 * 4 * 10
+    assert L.gmm_peak_hbm_read(None, 1 << 20, 4, FAKE, None) == -1
+    assert L.gmm_peak_hbm_read(ctypes.c_void_p(0x100004), 1 << 20, 4, FAKE, None) == -1  # misaligned
+    assert L.gmm_peak_hbm_read(FAKE, 8, 4, FAKE, None) == -1
 
 
 def test_version_and_error_strings(L):
