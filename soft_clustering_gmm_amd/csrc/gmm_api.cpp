@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <atomic>
 #include <climits>
+#include <cmath>
 #include <map>
 #include <mutex>
 
@@ -60,7 +61,7 @@ static int pow2_waves(int K) {
   return w;
 }
 
-int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
+static int make_plan_impl(int64_t N, int d, int K, int regime, void* base, Plan* plan, bool records) {
   if (N < 0 || d < 1 || K < 1) return GMM_EINVAL;
   if (d > kMaxD || K > kMaxK || N >= ((int64_t)1 << 40)) return GMM_EUNSUPPORTED;
   if (regime < GMM_REGIME_AUTO || regime > GMM_REGIME_SMALLK) return GMM_EINVAL;
@@ -113,6 +114,8 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
   p.Kp16 = (int)ceil_div(K, 16) * 16;
   p.E = 1 + 2 * p.DP;
   p.stats_split = g_stats_precision.load(std::memory_order_relaxed) == GMM_STATS_SPLIT_BF16;
+  p.pass1 = regime == GMM_REGIME_TWOPASS && records;
+  p.drop_rho = (float)(std::ldexp(1.0, -20) / (double)std::max<int64_t>(N, 1));
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -129,10 +132,22 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
   const size_t o_c64d = take((size_t)K * sizeof(double));
   const size_t o_mup = take((size_t)p.Kp * p.DP * sizeof(float));
   const size_t o_ivp = take((size_t)p.Kp * p.DP * sizeof(double));
+  // (the parameter regions above do not depend on N: the row-chunked E-step
+  // packs them once for plans of several chunk sizes)
+  const size_t o_muvar = take(p.pass1 ? (size_t)p.Kp * p.DP * 2 * sizeof(float) : 0);
   const size_t o_cmax = take((size_t)K * 4 * sizeof(float));
   const size_t o_errc = take(4 * sizeof(float));
-  // per-row normalisers: only the two-pass regime has a first pass
-  const size_t o_rowref = take(regime == GMM_REGIME_TWOPASS ? (size_t)std::max<int64_t>(N, 1) * sizeof(float2) : 0);
+  // per-row normalisers and first-pass records: only the two-pass regime has a first pass
+  const size_t n1 = (size_t)std::max<int64_t>(N, 1);
+  const size_t o_rowref = take(regime == GMM_REGIME_TWOPASS ? n1 * sizeof(float4) : 0);
+  const size_t nrec = p.pass1 ? (size_t)p.kslabs * n1 : 0;
+  const size_t o_p1h = take(nrec * sizeof(float4));
+  const size_t o_p1v = take(nrec * kCandT * sizeof(float));
+  const size_t o_p1k = take(nrec * kCandT);
+  const size_t o_rowE = take(p.pass1 ? n1 * sizeof(float) : 0);
+  const size_t o_lrow = take(p.pass1 ? n1 * sizeof(double) : 0);
+  const size_t o_fbl = take(p.pass1 ? n1 * sizeof(int32_t) : 0);
+  const size_t o_fbc = take(p.pass1 ? sizeof(int32_t) : 0);
   const size_t o_part = take((size_t)std::max<int64_t>(p.P, 1) * p.Kp * p.E * sizeof(float));
   const size_t o_ll = take((size_t)std::max<int64_t>(std::max(p.P, p.tiles), 1) * sizeof(double));
   const size_t o_stats = take((size_t)K * (1 + 2 * d) * sizeof(float));
@@ -156,7 +171,15 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
     p.ws.ivp = reinterpret_cast<double*>(b + o_ivp);
     p.ws.compmax = reinterpret_cast<float*>(b + o_cmax);
     p.ws.errc = reinterpret_cast<float*>(b + o_errc);
-    p.ws.rowref = regime == GMM_REGIME_TWOPASS ? reinterpret_cast<float2*>(b + o_rowref) : nullptr;
+    p.ws.rowref = regime == GMM_REGIME_TWOPASS ? reinterpret_cast<float4*>(b + o_rowref) : nullptr;
+    p.ws.p1h = p.pass1 ? reinterpret_cast<float4*>(b + o_p1h) : nullptr;
+    p.ws.p1v = p.pass1 ? reinterpret_cast<float*>(b + o_p1v) : nullptr;
+    p.ws.p1k = p.pass1 ? reinterpret_cast<uint8_t*>(b + o_p1k) : nullptr;
+    p.ws.rowE = p.pass1 ? reinterpret_cast<float*>(b + o_rowE) : nullptr;
+    p.ws.muvar = p.pass1 ? reinterpret_cast<float*>(b + o_muvar) : nullptr;
+    p.ws.lrow = p.pass1 ? reinterpret_cast<double*>(b + o_lrow) : nullptr;
+    p.ws.fblist = p.pass1 ? reinterpret_cast<int32_t*>(b + o_fbl) : nullptr;
+    p.ws.fbcount = p.pass1 ? reinterpret_cast<int32_t*>(b + o_fbc) : nullptr;
     p.ws.partials = reinterpret_cast<float*>(b + o_part);
     p.ws.llpart = reinterpret_cast<double*>(b + o_ll);
     p.ws.stats = reinterpret_cast<float*>(b + o_stats);
@@ -164,6 +187,14 @@ int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
   }
   *plan = p;
   return GMM_OK;
+}
+
+int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
+  return make_plan_impl(N, d, K, regime, base, plan, true);
+}
+
+int make_plan_params(int64_t N, int d, int K, int regime, void* base, Plan* plan) {
+  return make_plan_impl(N, d, K, regime, base, plan, false);
 }
 
 static size_t workspace_bytes(int64_t N, int d, int K) {
@@ -397,6 +428,8 @@ int gmm_estep_stats_chunked(const void* X_host, int32_t x_dtype, int64_t N, int3
   if (make_plan(L.chunk, d, K, GMM_REGIME_AUTO, workspace, &p) != GMM_OK) return GMM_EINVAL;
   if (make_plan(tail ? tail : L.chunk, d, K, GMM_REGIME_AUTO, workspace, &ptail) != GMM_OK) return GMM_EINVAL;
   if (p.bytes > L.plan_bytes || ptail.bytes > L.plan_bytes) return GMM_EWORKSPACE;
+  // the statistics skip threshold is set by the rows of the whole call
+  p.drop_rho = ptail.drop_rho = (float)(std::ldexp(1.0, -20) / (double)N);
 
   std::lock_guard<std::mutex> lock(g_chunk_mutex);
   ChunkRes* r = nullptr;
@@ -462,7 +495,7 @@ static bool kmeans_args_ok(int64_t N, int d, int K) {
 static KmLayout kmeans_layout(int64_t N, int d, int K) {
   KmLayout L{};
   Plan p;
-  make_plan(N, d, K, GMM_REGIME_TWOPASS, nullptr, &p);
+  make_plan_params(N, d, K, GMM_REGIME_TWOPASS, nullptr, &p);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -506,7 +539,7 @@ static hipError_t kmeans_assign_impl(const void* X, int32_t xt, int64_t N, int32
   float* ones = reinterpret_cast<float*>(w + L.ones);
   float* zeros = reinterpret_cast<float*>(w + L.zeros);
   Plan p;
-  make_plan(N, d, K, GMM_REGIME_TWOPASS, w + L.plan, &p);
+  make_plan_params(N, d, K, GMM_REGIME_TWOPASS, w + L.plan, &p);
   hipError_t e = launch_fill(ones, (int64_t)K * d, 1.f, s);
   if (e == hipSuccess) e = launch_fill(zeros, K, 0.f, s);
   if (e == hipSuccess) e = launch_precompute(p, C, ones, zeros, s);
@@ -596,7 +629,7 @@ int gmm_assign_top2(const void* X, int32_t x_dtype, int64_t N, int32_t d, const 
   if (N > 0 && (!idx || !resp)) return GMM_EINVAL;
   if ((st = check_ws(workspace, ws_bytes, N, d, K))) return st;
   Plan p;
-  if ((st = make_plan(N, d, K, GMM_REGIME_TWOPASS, workspace, &p))) return st;
+  if ((st = make_plan_params(N, d, K, GMM_REGIME_TWOPASS, workspace, &p))) return st;
   if (N == 0) return GMM_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_precompute(p, mu, var, logw, s);

@@ -19,6 +19,7 @@ constexpr int kSmallMaxD = 64;
 constexpr int kLseWaves = 4;         // waves per block in the fp64 normaliser pass
 constexpr int kSmallWaves = 4;       // waves per block in the small-K kernel
 constexpr int64_t kMaxChunkRows = 32768;  // rows per statistics partial, at most
+constexpr int kCandT = 8;            // candidates kept per (row, slab) by the fp32 first pass
 
 // Device pointers into the caller's workspace, filled by gmm::plan().
 struct Workspace {
@@ -32,7 +33,16 @@ struct Workspace {
   double* ivp;      // [Kp][DP] 1/var in fp64, zero padded
   float* compmax;   // [K][4] per-component max|A|, max|B|, |c|, ||B||_2 (error bound inputs)
   float* errc;      // [4] a_max, b_max, c_max, b2_max
-  float2* rowref;   // [N] per-row (m_ref, lZ) from the fp64 pass
+  float4* rowref;   // [N] per-row (m, lZ, theta, E) for the second pass (base 2)
+  // fp32 first pass of the two-pass regime (Plan::pass1):
+  float4* p1h;      // [kslabs][N] per (row, slab): z, slab max, capture threshold, candidate count
+  float* p1v;       // [kslabs][N][kCandT] candidate scores (base 2, fp32)
+  uint8_t* p1k;     // [kslabs][N][kCandT] their components within the slab
+  float* rowE;      // [N] per-row fp32 score error bound E (natural units)
+  float* muvar;     // [Kp][DP] (mean, variance) pairs, variance +inf past d (exact re-score of the merge)
+  double* lrow;     // [N] per-row l_n (natural), before the block sums
+  int32_t* fblist;  // [N] rows whose normaliser needs the fp64 pass
+  int32_t* fbcount; // [1] number of such rows
   float* partials;  // [P][Kp][E] per-chunk statistics
   double* llpart;   // [max(P, tiles)] per-block log-likelihood sums
   float* stats;     // [K][1 + 2d] Nk | Sx | Sxx scratch for the EM loop
@@ -54,6 +64,8 @@ struct Plan {
   int64_t tiles;    // ceil(N / 64)
   int E;            // 1 + 2*DP floats per component in a partial
   int stats_split;  // statistics contraction as split-bf16 products on the bf16 MFMA
+  int pass1;        // two-pass regime with the fp32 first pass (its record regions are laid out)
+  float drop_rho;   // statistics skip threshold rho = 2^-20 / (rows of the whole E-step)
   size_t bytes;     // workspace bytes this plan uses
   Workspace ws;
 };
@@ -61,6 +73,9 @@ struct Plan {
 // Fills `plan` (and the workspace pointers when base != nullptr). Returns a
 // gmm_status code; does not touch the GPU.
 int make_plan(int64_t N, int d, int K, int regime, void* base, Plan* plan);
+// The same without the first-pass record regions of the two-pass regime
+// (for the passes that only use the packed parameters: top-2, k-means).
+int make_plan_params(int64_t N, int d, int K, int regime, void* base, Plan* plan);
 
 // Kernel launchers (gmm_kernels.hip). All enqueue on `stream` and return a
 // hipError_t from hipGetLastError().

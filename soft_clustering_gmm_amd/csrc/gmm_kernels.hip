@@ -21,17 +21,22 @@
 // than a small tau are re-scored exactly (fp64, difference form) before the
 // normalisation: with l_n from the same fp32 scores (single sweep, small K)
 // those with 2 E_n r (1 - r) > tau, widened to every component within 20 of
-// the row maximum when the unrefined mass could still matter; with an
-// exact l_n (second pass of the two-pass regime) those with E_n r > tau. The
+// the row maximum when the unrefined mass could still matter; with the
+// first pass's l_n (two-pass regime) those its merge step chose. The
 // fp32 operands are scaled by log2(e), so scores come out in base 2 and every
 // exponential is one hardware exp2.
 //
 // Regimes (Turbo-GMM abstract): the single sweep keeps the whole component
 // axis of a 64-point tile on chip (K <= 256) and does max, log-sum-exp and
-// statistics in one traversal. The two-pass fallback computes l_n first in a
-// fp64-MFMA pass, then recomputes the fp32 scores per 256-component slab and
-// accumulates the statistics. A small-K kernel (K <= 16, d <= 64) gives each
-// wave its own rows and keeps the whole mixture in registers.
+// statistics in one traversal. The two-pass fallback computes l_n first: an
+// fp32 pass per 256-component slab records each slab's maximum, sum of
+// exponentials and a few candidate entries per row; a merge per row decides
+// which entries must be exact for l_n (and for the second pass) and
+// re-scores them in fp64; rows it cannot settle from the records get an
+// fp64-MFMA normaliser pass. The second pass recomputes the same fp32 scores
+// per slab, re-scores the same entries, and accumulates the statistics. A
+// small-K kernel (K <= 16, d <= 64) gives each wave its own rows and keeps
+// the whole mixture in registers.
 //
 // Lloyd's k-means assignment (Flash-KMeans articles) reuses the fp32 score
 // tile: with unit variances the highest score is the nearest centre, and the
@@ -71,6 +76,15 @@ constexpr float kUnitRound = 1.1920928955078125e-7f;
 // bound an upper bound.
 constexpr float kBoundSlack = 1.0005f;
 constexpr int kRefCap = 128;       // re-score list entries per wave and pass
+// Widest candidate window of the fp32 first pass (base-2 units below the
+// slab maximum): wider than the 20-nat window (28.9 base-2 units) beyond
+// which an entry's weight is below e^-20 of the row maximum's.
+constexpr float kCapWin = 32.f;
+// Candidate windows of the first pass, loosest first (base-2 units below the
+// slab maximum); the last, 0, admits only the entries equal to the maximum.
+constexpr int kCapLevels = 13;
+__constant__ float kCapLadder[kCapLevels] = {kCapWin, 26.f, 22.f, 19.f, 17.f, 15.f, 13.f, 11.f, 9.f,
+                                             7.f, 5.f, 3.f, 0.f};
 // Word 3 of a raw buffer resource on CDNA (32-bit data format, no swizzle):
 // loads at offsets past the record count return zero.
 constexpr int kBufferRsrcWord3 = 0x00020000;
@@ -83,6 +97,13 @@ __device__ __forceinline__ void split_bf16(const float (&v)[8], v8bf& hi, v8bf& 
     hi[t] = (__bf16)v[t];
     lo[t] = (__bf16)(v[t] - (float)hi[t]);
   }
+}
+
+// The smallest float above a finite x.
+__device__ __forceinline__ float next_up(float x) {
+  if (x == 0.f) return __int_as_float(1);
+  const int b = __float_as_int(x);
+  return __int_as_float(x > 0.f ? b + 1 : b - 1);
 }
 
 // Row of the 32x32 MFMA accumulator held in slot j by lanes of half h:
@@ -247,14 +268,15 @@ __global__ void comp_consts_kernel(const float* __restrict__ mu, const float* __
 __global__ void pack_kernel(const float* __restrict__ mu, const float* __restrict__ var, int K, int d,
                             int Kp, int Kp16, int DP, float* __restrict__ W32p,
                             double* __restrict__ W64p, double* __restrict__ iv64,
-                            float* __restrict__ mup, double* __restrict__ ivp) {
+                            float* __restrict__ mup, double* __restrict__ ivp, float2* __restrict__ muvar) {
   const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (t >= (int64_t)Kp * DP) return;
   const int k = (int)(t / DP), f = (int)(t - (int64_t)k * DP);
   double A = 0.0, B = 0.0, iv = 0.0;
-  float m = 0.f;
+  float m = 0.f, v = INFINITY;
   if (k < K && f < d) {
-    iv = 1.0 / (double)var[(size_t)k * d + f];
+    v = var[(size_t)k * d + f];
+    iv = 1.0 / (double)v;
     m = mu[(size_t)k * d + f];
     A = -0.5 * iv;
     B = (double)m * iv;
@@ -262,6 +284,7 @@ __global__ void pack_kernel(const float* __restrict__ mu, const float* __restric
   }
   mup[t] = m;
   ivp[t] = iv;
+  if (muvar) muvar[t] = make_float2(m, v);
   {
     // fp32 score operands, base-2 scaled like c32: lane (h, c) of feature
     // block q (features 4q..4q+3) holds A of features 4q + 2h + {0, 1} in
@@ -413,15 +436,23 @@ __device__ __forceinline__ void score_tile(const float* xs, float* sc, float* xq
 //      32 responsibilities are all exactly zero is skipped.
 // At the end each block writes its statistics partial; a separate kernel
 // sums the partials in a fixed order (no atomics anywhere).
+// Outputs of the fp32 first pass (MODE 2), per (row, slab): see Pass1Out.
+struct Pass1Out {
+  float4* h;      // [kslabs][N] (z, slab max m, capture threshold th, candidate count)
+  float* v;       // [kslabs][N][kCandT] candidate scores
+  uint8_t* k;     // [kslabs][N][kCandT] candidate components within the slab
+  float* rowE;    // [N] the row's fp32 score error bound (written by slab 0)
+};
+
 template <int DT, int MODE, typename XT, bool SPLIT>
 __global__ void __launch_bounds__(512)
 estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, int waves, int kslabs,
                    int64_t rows_per_chunk, const float4* __restrict__ W32p, const float* __restrict__ c32,
                    const float* __restrict__ mup, const double* __restrict__ ivp,
                    const double* __restrict__ c64d, const float* __restrict__ errc,
-                   const float2* __restrict__ rowref, float* __restrict__ partials,
+                   const float4* __restrict__ rowref, float* __restrict__ partials,
                    double* __restrict__ llpart, float* __restrict__ ll_point, float* __restrict__ R,
-                   int vec) {
+                   Pass1Out p1, float rho, int vec) {
   constexpr int DP = 32 * DT, Q = DP / 4, XS = DP + 4, E = 1 + 2 * DP;
   extern __shared__ __align__(16) float smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
@@ -433,8 +464,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   const int kw = k0 + wave * 32;
   float* xsb = smem;             // [2][64][XS]: current and next X tile
   float* sc = xsb + 2 * 64 * XS; // [64][SCS]
-  float* rv = sc + 64 * SCS;     // [64][2]
-  float* xq = rv + 128;          // [64][2] |x|^2 and |x|_1 of the tile's rows
+  float* rv = sc + 64 * SCS;     // [64][4] per-row references (m, lZ or 1/z, theta)
+  float* xq = rv + 256;          // [64][2] |x|^2 and |x|_1 of the tile's rows
   double* lls = reinterpret_cast<double*>(xq + 128);  // [nthr]
   uint32_t* reflist = reinterpret_cast<uint32_t*>(lls + nthr);  // [waves][kRefCap]
   uint32_t* nzrow = reflist + waves * kRefCap;  // [64]: bit w = row has a nonzero r for wave w
@@ -493,9 +524,10 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     __syncthreads();
     if (MODE == 1 && tid < 64) {
       const int64_t gr = r0 + tid;
-      const float2 mr = gr < hi ? rowref[gr] : make_float2(0.f, 0.f);
-      rv[2 * tid] = mr.x;
-      rv[2 * tid + 1] = mr.y;
+      const float4 mr = gr < hi ? rowref[gr] : make_float4(0.f, 0.f, INFINITY, 0.f);
+      rv[4 * tid] = mr.x;
+      rv[4 * tid + 1] = mr.y;
+      rv[4 * tid + 2] = mr.z;
     }
 
     // 2. scores
@@ -508,7 +540,101 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     //    directly to r (MODE 1). m, lZ and the LDS row references are in base 2;
     //    the error bound E stays in natural units (scaling by log2(e) and
     //    back cancels in the bound).
-    {
+    if constexpr (MODE == 2) {
+      // First pass (fp32 normalisers), per (row, slab): the slab maximum m,
+      // z = sum 2^(s - m) over the slab, and the candidates: every entry with
+      // s >= th, th the loosest of m - W (W on the ladder kCapLadder, ending
+      // with m itself) that admits at most kCandT entries; if even m admits
+      // more, th is the next float above m and nothing is recorded. So every
+      // entry of the slab at or above th is recorded and none below it is;
+      // the merge step relies on exactly that.
+      const int row = prow;
+      const int64_t grow = r0 + row;
+      const bool valid = grow < hi;
+      const float4* srow4 = reinterpret_cast<const float4*>(sc + row * SCS);
+      float4 ev[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ev[i] = srow4[psub + tpr * i];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fmaxf(fmaxf(ev[i].x, ev[i].y), fmaxf(ev[i].z, ev[i].w)));
+      const float m = group_max(mx, tpr);
+      const float ms = m == -INFINITY ? 0.f : m;  // a slab whose entries are all -inf has z = 0
+      double z = 0.0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 v = ev[i];
+        // fp32 sums of four e <= 1, gathered in fp64: |dz| <= 2 u z
+        z += (double)((__builtin_amdgcn_exp2f(v.x - ms) + __builtin_amdgcn_exp2f(v.y - ms)) +
+                      (__builtin_amdgcn_exp2f(v.z - ms) + __builtin_amdgcn_exp2f(v.w - ms)));
+      }
+      z = group_sum_d(z, tpr);
+      auto count_ge = [&](float th) {
+        int c = 0;
+        if (mx >= th)
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            c += (int)(ev[i].x >= th) + (int)(ev[i].y >= th) + (int)(ev[i].z >= th) + (int)(ev[i].w >= th);
+        return c;
+      };
+      float th = -INFINITY;
+      int mine = 0, cnt = 0;
+      if (m != -INFINITY) {
+        th = m - kCapLadder[0];
+        mine = count_ge(th);
+        cnt = (int)group_sum((float)mine, tpr);
+        if (cnt > kCandT) {
+          // the loosest level that admits at most kCandT: counts only fall
+          // along the ladder, so bisect levels [1, kCapLevels); kCapLevels
+          // stands for none
+          int lo = 1, hi = kCapLevels;
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((int)group_sum((float)count_ge(m - kCapLadder[mid]), tpr) <= kCandT)
+              hi = mid;
+            else
+              lo = mid + 1;
+          }
+          if (lo < kCapLevels) {
+            th = m - kCapLadder[lo];
+            mine = count_ge(th);
+            cnt = (int)group_sum((float)mine, tpr);
+          } else {
+            th = next_up(m);
+            mine = 0;
+            cnt = 0;
+          }
+        }
+      }
+      // this thread's first slot: exclusive prefix of the counts over the row's lanes
+      int incl = mine;
+      for (int o = 1; o < tpr; o <<= 1) {
+        const int t = __shfl_up(incl, o, tpr);
+        if (psub >= o) incl += t;
+      }
+      if (valid) {
+        const size_t rec = (size_t)slab * N + grow;
+        if (psub == 0) p1.h[rec] = make_float4((float)z, m, th, (float)cnt);
+        if (slab == 0 && psub == 0) {
+          const float sq = xq[2 * row], ab = xq[2 * row + 1];
+          p1.rowE[grow] = gam * (a_max * sq + fminf(b_max * ab, b2_max * sqrtf(sq))) + 2.f * kUnitRound * c_max;
+        }
+        if (mine) {
+          size_t slot = rec * kCandT + (size_t)(incl - mine);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float vv[4] = {ev[i].x, ev[i].y, ev[i].z, ev[i].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (vv[u] >= th) {
+                p1.v[slot] = vv[u];
+                p1.k[slot] = (uint8_t)(4 * (psub + tpr * i) + u);
+                ++slot;
+              }
+          }
+        }
+      }
+    } else {
       const int row = prow;
       const int64_t grow = r0 + row;
       const bool valid = grow < hi;
@@ -521,6 +647,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       float4* srow4 = reinterpret_cast<float4*>(srow);
       float m, lZ = 0.f;
       double z = 0.0;
+      uint32_t mask1 = 0;  // MODE 1: the entries the first pass re-scored
       // The thread's 32 entries stay in registers from one LDS read (all
       // eight loads in flight) through the max, exp and flag passes.
       float4 ev[8];
@@ -544,30 +671,44 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         }
         z = group_sum_d(z, tpr);
       } else {
-        m = rv[2 * row];
-        lZ = rv[2 * row + 1];
+        // the first pass's row reference: the row's maximal fp32 score m, lZ =
+        // l - m, and theta: the entries with s - m >= theta are the ones the
+        // first pass re-scored exactly (the same fp32 scores, bit for bit)
+        m = rv[4 * row];
+        lZ = rv[4 * row + 1];
+        const float theta = valid ? rv[4 * row + 2] : INFINITY;
 #pragma unroll
         for (int i = 0; i < 8; ++i) ev[i] = srow4[psub + tpr * i];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           float4& v = ev[i];
-          v.x = __builtin_amdgcn_exp2f((v.x - m) - lZ);
-          v.y = __builtin_amdgcn_exp2f((v.y - m) - lZ);
-          v.z = __builtin_amdgcn_exp2f((v.z - m) - lZ);
-          v.w = __builtin_amdgcn_exp2f((v.w - m) - lZ);
+          const float dx = v.x - m, dy = v.y - m, dz = v.z - m, dw = v.w - m;
+          mask1 |= ((dx >= theta ? 1u : 0u) | (dy >= theta ? 2u : 0u) | (dz >= theta ? 4u : 0u) |
+                    (dw >= theta ? 8u : 0u)) << (4 * i);
+          v.x = __builtin_amdgcn_exp2f(dx - lZ);
+          v.y = __builtin_amdgcn_exp2f(dy - lZ);
+          v.z = __builtin_amdgcn_exp2f(dz - lZ);
+          v.w = __builtin_amdgcn_exp2f(dw - lZ);
           srow4[psub + tpr * i] = v;
         }
       }
-      // Which waves' component slices hold a nonzero e (or r) in this row.
-      // Entry chunk psub + tpr i belongs to wave (i * waves) / 8. An exact
-      // zero is never re-scored (every flag rule needs e > 0), so the bits
-      // are final; rows past the end take none (their r is zero).
+      // Which waves' component slices hold a responsibility above
+      // rho / max(1, |x|^2) in this row (r = e / z in MODE 0); a point whose
+      // 32 responsibilities for a wave are all at or below that threshold is
+      // left out of that wave's statistics. Over all N points this drops at
+      // most N rho (1 + 2E) from any Nk, and, as |x_j| <= |x|^2 for |x|^2 >= 1,
+      // at most as much from any Sx or Sxx element: rho = 2^-20 / N keeps every
+      // statistic within about 1e-6 of its value. Entry chunk psub + tpr i
+      // belongs to wave (i * waves) / 8. The bits are taken from the fp32
+      // responsibilities, before the re-score (which moves an entry by a
+      // factor within 1 +- 2E); rows past the end take none (their r is zero).
       if constexpr (!SPLIT) {
         uint32_t nzb = 0;
+        const float wthr = rho / fmaxf(1.f, sq) * (MODE == 0 ? (float)z : 1.f);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float4 v = ev[i];
-          const bool nz = (v.x != 0.f) | (v.y != 0.f) | (v.z != 0.f) | (v.w != 0.f);
+          const bool nz = (v.x > wthr) | (v.y > wthr) | (v.z > wthr) | (v.w > wthr);
           nzb |= (nz ? 1u : 0u) << ((i * waves) >> 3);
         }
         for (int o = 1; o < tpr; o <<= 1) nzb |= (uint32_t)__shfl_xor((int)nzb, o, 64);
@@ -580,10 +721,10 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       //   nothing). Refined entries are then off by at most E * U, U = the
       //   unrefined mass; if that could exceed tau the window widens to every
       //   entry within 20 of the row maximum (e >= kExpWindow).
-      //  MODE 1: l_n comes from the first pass's fp64 scores (its sum of
-      //   exponentials takes each term in fp32, so l_n is off by ~1e-7, far
-      //   below tau); an unrefined entry is off by <= E r_k, and entries with
-      //   r_k > tau / E are refined.
+      //  MODE 1: the first pass decided, per row, which entries to re-score
+      //   (those with s - m >= theta) and took l_n from exactly those exact
+      //   scores and the other fp32 ones, so that every entry meets tau; this
+      //   pass re-scores the same entries.
       uint32_t mask = 0;
       if (MODE == 0) {
         const float zf = (float)z;
@@ -619,21 +760,12 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           }
         }
       } else {
-        const float thr = kGateTau / Ebound;
-        if (valid && __builtin_amdgcn_exp2f(-lZ) > thr)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float4 v = ev[i];
-            mask |= (v.x >= thr ? 1u : 0u) << (4 * i);
-            mask |= (v.y >= thr ? 1u : 0u) << (4 * i + 1);
-            mask |= (v.z >= thr ? 1u : 0u) << (4 * i + 2);
-            mask |= (v.w >= thr ? 1u : 0u) << (4 * i + 3);
-          }
+        mask = mask1;
       }
       // Exact re-score of the window entries. Each wave pools the entries of
       // its rows into an LDS list and re-scores eight at a time, eight lanes
       // per entry splitting the features (fp64, difference form).
-      if (MODE == 0 && psub == 0) rv[2 * row] = m;
+      if (MODE == 0 && psub == 0) rv[4 * row] = m;
       {
         const int cnt = __popc(mask);
         const int incl = wave_incl_scan(cnt);
@@ -689,8 +821,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
             acc += dpp_d<kDppHalfMirror>(acc);
             if (act && sl == 0) {
               // exact (s - m) / ln 2: acc = sum_j (x_j - mu_j)^2 / var_j - 2 c_k
-              const double dl = (-0.5 * acc) * kLog2E - (double)rv[2 * er];
-              sc[er * SCS + ek] = __builtin_amdgcn_exp2f(MODE == 0 ? (float)dl : (float)(dl - (double)rv[2 * er + 1]));
+              const double dl = (-0.5 * acc) * kLog2E - (double)rv[4 * er];
+              sc[er * SCS + ek] = __builtin_amdgcn_exp2f(MODE == 0 ? (float)dl : (float)(dl - (double)rv[4 * er + 1]));
             }
           }
           wave_lds_sync();
@@ -717,7 +849,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           if (ll_point) ll_point[grow] = (float)l;
         }
         // the tile keeps e; the statistics loop applies r = e / z as it reads it
-        if (psub == 0) rv[2 * row + 1] = invz;
+        if (psub == 0) rv[4 * row + 1] = invz;
         if (R && valid)
 #pragma unroll 1
           for (int i = 0; i < 32; ++i) {
@@ -750,7 +882,9 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         hpre[i] = (ch < 8 * DP && gr < hi && 8 * q < d) ? *reinterpret_cast<const uint4*>(X + gr * d + 8 * q)
                                                         : make_uint4(0u, 0u, 0u, 0u);
       }
-    if constexpr (SPLIT) {
+    if constexpr (MODE == 2) {
+      // the first pass accumulates no statistics
+    } else if constexpr (SPLIT) {
       // Split-bf16 products on the 32x32x16 bf16 MFMA (see the small-K
       // kernel for the error of a product): block pb covers points
       // 16 pb + 8 h + t (t < 8) of lane (h, c), r of component c as the A
@@ -763,7 +897,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         for (int t = 0; t < 8; ++t) {
           const int row = 16 * pb + 8 * h + t;
           rr[t] = sc[row * SCS + wave * 32 + c];
-          if (MODE == 0) rr[t] *= rv[2 * row + 1];  // e -> r = e / z (0 past the last row)
+          if (MODE == 0) rr[t] *= rv[4 * row + 1];  // e -> r = e / z (0 past the last row)
           nk += rr[t];
           const float* xr = xs + row * XS + DT * c;
 #pragma unroll
@@ -802,7 +936,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       // point's LDS reads issue, so the wait for them never covers those.
       auto sload = [&](int p, float& e, float& iz, float(&xv)[DT]) {
         e = sc[p * SCS + wave * 32 + c];
-        iz = MODE == 0 ? rv[2 * p + 1] : 1.f;
+        iz = MODE == 0 ? rv[4 * p + 1] : 1.f;
         const float* xr = xs + p * XS + DT * c;
 #pragma unroll
         for (int t = 0; t < DT; ++t) xv[t] = xr[t];
@@ -877,6 +1011,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     cur ^= 1;
   }
 
+  if constexpr (MODE == 2) return;
   // statistics partial of this (chunk, slab)
   float* part = partials + (size_t)chunk * Kp * E;
 #pragma unroll
@@ -901,6 +1036,252 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       llpart[chunk] = s;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Per-row normalisers from the fp32 first pass (two-pass regime)
+// ---------------------------------------------------------------------------
+//
+// One wave per 64 consecutive rows, one lane per row, all in base-2 units.
+// From the row's per-slab records: m = the largest fp32 score, z = sum_s z_s
+// 2^(m_s - m), so that m + log2 z is the log-sum-exp of the fp32 scores.
+// With E the row's bound on |s32 - s| (E2 = E log2 e in base 2), the second
+// pass gets (m, lZ, theta) and re-scores exactly the entries with
+// s32 - m >= theta, with r = 2^(s' - m - lZ) where s' is the exact score of
+// those entries and the fp32 score of the others. With F the re-scored set
+// and U the responsibility mass outside it, an entry is then off by at most
+//   r E U (k in F),   r E (1 + U - 2 r) (k outside F).
+//  (a) No re-score (theta = +inf, U = 1): every entry is off by at most
+//      2 E r (1 - r), and over a row max_k r (1 - r) is the largest entry's
+//      r_1 (1 - r_1) (the others sum to 1 - r_1), with r_1 = 1/z. Taken
+//      when 2 E r_1 (1 - r_1) <= tau: one-hot rows and dense rows of small r.
+//  (b) Otherwise a window theta = -W: outside it s32 - m < -W, so
+//      r < 2^(-W + 2 E2) (the exact l is at least m - E2), and W >= Wb =
+//      log2(2E / tau) + 2 E2 keeps every outside entry within tau. The
+//      smallest W of a ladder from Wb up to what the records hold completely
+//      (every slab recorded all its entries at or above its threshold th, so
+//      the window must stay above the largest th) with E U <= tau, U bounded
+//      by 2^(2 E2) (z - sum of the window's 2^(s32 - m)) / z, is taken; its
+//      entries are re-scored here (fp64, difference form) and l is
+//      m + log2(z + sum over the window of 2^(s - m) - 2^(s32 - m)).
+//  (c) Neither (no window satisfies E U <= tau, or a slab had more than
+//      kCandT entries near its maximum): the row goes on the fallback list
+//      for the fp64 normaliser pass.
+// l_n (natural log) goes to lrow; the fallback pass writes its rows' entries.
+template <int DT, typename XT>
+__global__ void __launch_bounds__(64)
+lse_merge_kernel(const XT* __restrict__ X, int64_t N, int d, int kslabs, int KS,
+                 const float4* __restrict__ p1h, const float* __restrict__ p1v, const uint8_t* __restrict__ p1k,
+                 const float* __restrict__ rowE, const float* __restrict__ muvar,
+                 const double* __restrict__ c64d, float4* __restrict__ rowref, double* __restrict__ lrow,
+                 int32_t* __restrict__ fblist, int32_t* __restrict__ fbcount) {
+  constexpr int DP = 32 * DT, FPL = DP / 8, kLevels = 8, kCap = 512, kHdr = 16;
+  static_assert(kCandT == 8, "a record's candidates are read as two float4");
+  __shared__ uint32_t elist[kCap];  // (lane << 16) | component
+  __shared__ float ev32[kCap];      // its fp32 score
+  __shared__ double ex[kCap];       // its exact score
+  __shared__ float4 hs[kHdr][64];   // the block's slab headers (kslabs <= kHdr)
+  const int lane = threadIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.x * 64, n = n0 + lane;
+  const bool valid = n < N;
+  // slab sl's header of this lane's row: from LDS when the block staged them
+  const bool staged = kslabs <= kHdr;
+  if (staged)
+    for (int sl = 0; sl < kslabs; ++sl) hs[sl][lane] = valid ? p1h[(size_t)sl * N + n] : make_float4(0, 0, 0, 0);
+  auto hdr = [&](int sl) { return staged ? hs[sl][lane] : p1h[(size_t)sl * N + n]; };
+  auto cands = [&](int sl, float (&v)[kCandT]) {
+    const float4* q = reinterpret_cast<const float4*>(p1v + ((size_t)sl * N + n) * kCandT);
+    const float4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  };
+
+  // the row's largest fp32 score, and the largest capture threshold
+  float m = -INFINITY, tc = -INFINITY;
+  if (valid)
+    for (int sl = 0; sl < kslabs; ++sl) {
+      const float4 h = hdr(sl);
+      m = fmaxf(m, h.y);
+      tc = fmaxf(tc, h.z);
+    }
+  const float E = valid ? rowE[n] : 0.f;
+  const double E2 = (double)E * kLog2E;
+  // the window ladder of (b): from Wb to what the records hold completely,
+  // each as the fp32 threshold the second pass compares s32 - m with (the
+  // 1/64 keeps the rounding of s32 - m inside)
+  const double Wb = log2(2.0 * (double)E / (double)kGateTau) + 2.0 * E2 + 1.0 / 64;
+  const double Wmax = fmin((double)kCapWin, (double)m - (double)tc) - 1.0 / 64;
+  // z (hardware exp2 of exact fp32 differences, each term within 2 ulp;
+  // fp64 sums)
+  double z = 0.0;
+  if (valid)
+    for (int sl = 0; sl < kslabs; ++sl) {
+      const float4 h = hdr(sl);
+      if (h.y != -INFINITY) z += (double)h.x * (double)__builtin_amdgcn_exp2f(h.y - m);
+    }
+  // the fp32 mass of the windows lev[0..kLevels) (thresholds on s32 - m,
+  // loosest last)
+  float lev[kLevels];
+  double S[kLevels];
+  auto window_mass = [&]() {
+#pragma unroll
+    for (int i = 0; i < kLevels; ++i) S[i] = 0.0;
+    for (int sl = 0; sl < kslabs; ++sl) {
+      const float4 h = hdr(sl);
+      if (h.w > 0.f && h.y - m >= lev[kLevels - 1]) {
+        float v[kCandT];
+        cands(sl, v);
+#pragma unroll
+        for (int j = 0; j < kCandT; ++j) {
+          const float dd = v[j] - m;
+          if (j < (int)h.w && dd >= lev[kLevels - 1]) {
+            const double e = (double)__builtin_amdgcn_exp2f(dd);
+#pragma unroll
+            for (int i = 0; i < kLevels; ++i)
+              if (dd >= lev[i]) S[i] += e;
+          }
+        }
+      }
+    }
+  };
+  const double grow = exp2(2.0 * E2);
+  // E U <= tau for the window lev[i]; 16 u covers the rounding of z and of
+  // the window sums
+  auto holds = [&](int i) {
+    return (double)E * grow * ((z - S[i]) / z + 16.0 * (double)kUnitRound) <= (double)kGateTau;
+  };
+  const double r1 = 1.0 / z;
+  float theta = INFINITY;
+  bool fallback = false;
+  if (valid && !(2.0 * (double)E * r1 * (1.0 - r1) <= (double)kGateTau)) {
+    fallback = true;
+    if (Wmax >= Wb) {
+      // the smallest window in two rounds of kLevels levels: a coarse ladder
+      // over [Wb, Wmax], then a fine one inside the bracket it found
+      double wlo = Wb, whi = Wmax;
+      for (int round = 0; round < 2 && fallback; ++round) {
+#pragma unroll
+        for (int i = 0; i < kLevels; ++i) lev[i] = (float)-(wlo + (whi - wlo) * i / (kLevels - 1));
+        window_mass();
+        int first = kLevels;
+#pragma unroll
+        for (int i = kLevels - 1; i >= 0; --i)
+          if (holds(i)) first = i;
+        if (first == kLevels) break;  // not even the widest window: fallback
+        theta = lev[first];
+        if (first == 0) fallback = false;
+        else {
+          whi = -(double)lev[first];
+          wlo = -(double)lev[first - 1];
+          if (round == 1) fallback = false;
+        }
+      }
+      if (theta != INFINITY) fallback = false;
+    }
+  }
+  // exact re-score of every window entry, pooled over the wave: lane l's
+  // entries take list positions [base, base + cnt), eight lanes per entry
+  int cnt = 0;
+  if (valid && !fallback && theta != INFINITY)
+    for (int sl = 0; sl < kslabs; ++sl) {
+      const float4 h = hdr(sl);
+      if (h.w <= 0.f || h.y - m < theta) continue;
+      float v[kCandT];
+      cands(sl, v);
+#pragma unroll
+      for (int j = 0; j < kCandT; ++j) cnt += (j < (int)h.w && v[j] - m >= theta) ? 1 : 0;
+    }
+  const int incl = wave_incl_scan(cnt);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  const int base = incl - cnt;
+  double corr = 0.0;
+  for (int p0 = 0; p0 < total; p0 += kCap) {
+    if (cnt) {
+      int pos = base;
+      for (int sl = 0; sl < kslabs; ++sl) {
+        const float4 h = hdr(sl);
+        if (h.w <= 0.f || h.y - m < theta) continue;
+        float v[kCandT];
+        cands(sl, v);
+        const size_t rec = ((size_t)sl * N + n) * kCandT;
+#pragma unroll
+        for (int j = 0; j < kCandT; ++j)
+          if (j < (int)h.w && v[j] - m >= theta) {
+            if (pos >= p0 && pos < p0 + kCap) {
+              elist[pos - p0] = ((uint32_t)lane << 16) | (uint32_t)(sl * KS + p1k[rec + j]);
+              ev32[pos - p0] = v[j];
+            }
+            ++pos;
+          }
+      }
+    }
+    wave_lds_sync();
+    const int nn = min(total - p0, kCap);
+    for (int e0 = 0; e0 < nn; e0 += 8) {
+      const int e = e0 + (lane >> 3), sl8 = lane & 7;
+      const bool act = e < nn;
+      const uint32_t ent = act ? elist[e] : 0u;
+      const int er = (int)(ent >> 16), kg = (int)(ent & 0xffffu);
+      const int64_t xr = (n0 + er) * (int64_t)d;
+      const float4* mvr = reinterpret_cast<const float4*>(muvar + ((size_t)kg * DP + sl8 * FPL) * 2);
+      // every load before the arithmetic; features past d carry var = +inf
+      float xv[FPL];
+      float4 mv[FPL / 2];  // (mu, var) of two features
+#pragma unroll
+      for (int i = 0; i < FPL; ++i) {
+        const int f = sl8 * FPL + i;
+        xv[i] = act && f < d ? load_x(X, xr + f) : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < FPL / 2; ++i) mv[i] = mvr[i];
+      const double cst = sl8 == 0 ? -2.0 * c64d[kg] : 0.0;
+      __builtin_amdgcn_sched_barrier(0);
+      double a0 = cst, a1 = 0.0;
+#pragma unroll
+      for (int i = 0; i < FPL; i += 2) {
+        const double t0 = (double)xv[i] - (double)mv[i / 2].x, t1 = (double)xv[i + 1] - (double)mv[i / 2].z;
+        a0 += t0 * t0 / (double)mv[i / 2].y;
+        a1 += t1 * t1 / (double)mv[i / 2].w;
+      }
+      double acc = a0 + a1;
+      acc += dpp_d<kDppXor1>(acc);
+      acc += dpp_d<kDppXor2>(acc);
+      acc += dpp_d<kDppHalfMirror>(acc);
+      if (act && sl8 == 0) ex[e] = (-0.5 * acc) * kLog2E;  // exact s, base 2
+    }
+    wave_lds_sync();
+    for (int pos = max(base, p0); pos < min(base + cnt, p0 + kCap); ++pos)
+      corr += exp2(ex[pos - p0] - (double)m) - exp2((double)ev32[pos - p0] - (double)m);
+    wave_lds_sync();
+  }
+  if (valid && !fallback) {
+    const double l2 = (double)m + log2(z + corr);
+    rowref[n] = make_float4(m, (float)(l2 - (double)m), theta, E);
+    lrow[n] = l2 * kLn2;
+  }
+  if (valid && fallback) fblist[atomicAdd(fbcount, 1)] = (int32_t)n;
+}
+
+// Per 64-row tile: l_n (natural) to ll_point (nullable) and the tile's sum,
+// in row order, to llpart.
+__global__ void __launch_bounds__(64) row_ll_sum_kernel(const double* __restrict__ lrow, int64_t N,
+                                                        float* __restrict__ ll_point, double* __restrict__ llpart) {
+  __shared__ double s[64];
+  const int64_t n = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  const double l = n < N ? lrow[n] : 0.0;
+  if (ll_point && n < N) ll_point[n] = (float)l;
+  s[threadIdx.x] = l;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double a = 0.0;
+    for (int i = 0; i < 64; ++i) a += s[i];
+    llpart[blockIdx.x] = a;
+  }
+}
+
+__global__ void fill_int_kernel(int32_t* __restrict__ a, int64_t n, int32_t v) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t < n) a[t] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -1566,7 +1947,8 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
 }
 
 // ---------------------------------------------------------------------------
-// First pass of the two-pass regime (also the top-2 kernel): fp64 MFMA scores
+// fp64 MFMA score pass: top-2 assignment, and the normaliser of the rows the
+// fp32 first pass's merge could not settle
 // ---------------------------------------------------------------------------
 //
 // Block = 4 waves, one 64-point tile. With NP = 4, wave w takes the
@@ -1601,24 +1983,32 @@ __device__ __forceinline__ void top2_insert(double v, int i, double& v1, int& i1
 
 // Four waves per SIMD (at most 128 registers): the fp64 MFMA chains of four
 // blocks per CU hide each other's LDS and L2 latency.
+// Rows: the 64 consecutive rows of the block (rows == nullptr), or, as the
+// fallback of the fp32 first pass, slots blockIdx.x * 64 + t of the row list
+// `rows` (its length in *nrows; blocks past it return at once).
 template <int DT, bool TOP2, typename XT, int NP>
 __global__ void __launch_bounds__(256, 4)
 estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
                  const double* __restrict__ W64p, const double* __restrict__ c64e,
-                 float2* __restrict__ rowref, float* __restrict__ ll_point, double* __restrict__ llpart,
+                 const int32_t* __restrict__ rows, const int32_t* __restrict__ nrows,
+                 const float* __restrict__ rowE, float4* __restrict__ rowref, double* __restrict__ lrow,
                  int32_t* __restrict__ tidx, float* __restrict__ tresp) {
   constexpr int DP = 32 * DT, S = DP / 2, XS = DP + 1;
   __shared__ float xs[64 * XS];
   __shared__ double sm[kLseWaves][64], sz[kLseWaves][64], sv1[kLseWaves][64], sv2[kLseWaves][64];
   __shared__ int si1[kLseWaves][64], si2[kLseWaves][64];
-  __shared__ double sl[64];
+  __shared__ int64_t srow[64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int64_t nr = rows ? (int64_t)*nrows : N;
+  if (r0 >= nr) return;
+  if (tid < 64) srow[tid] = r0 + tid < nr ? (rows ? (int64_t)rows[r0 + tid] : r0 + tid) : -1;
+  __syncthreads();
 
   for (int e = tid; e < 64 * DP; e += blockDim.x) {
     const int row = e / DP, f = e - row * DP;
-    const int64_t gr = r0 + row;
-    xs[row * XS + f] = (gr < N && f < d) ? load_x(X, gr * d + f) : 0.f;
+    const int64_t gr = srow[row];
+    xs[row * XS + f] = (gr >= 0 && f < d) ? load_x(X, gr * d + f) : 0.f;
   }
   __syncthreads();
 
@@ -1756,13 +2146,18 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
       }
     }
     const double l = mm + log(zz);
-    const int64_t gr = r0 + tid;
-    sl[tid] = gr < N ? l : 0.0;
-    if (gr < N) {
-      // (m, lZ) in base 2 for the fp32 second pass
-      const float mref = (float)(mm * kLog2E);
-      if (rowref) rowref[gr] = make_float2(mref, (float)(l * kLog2E - (double)mref));
-      if (ll_point) ll_point[gr] = (float)l;
+    const int64_t gr = srow[tid];
+    if (gr >= 0) {
+      if (rowref) {
+        // (m, lZ, theta) in base 2 for the fp32 second pass: with this l (fp64
+        // scores) an entry left unrefined is off by <= E r, so the entries
+        // with r >= tau / E, i.e. s32 - m >= lZ + log2(tau / E), are re-scored
+        const float mref = (float)(mm * kLog2E);
+        const float lZ = (float)(l * kLog2E - (double)mref);
+        const float E = fmaxf(rowE[gr], 1e-30f);
+        rowref[gr] = make_float4(mref, lZ, lZ + log2f(kGateTau / E) - 1.f / 64, E);
+        lrow[gr] = l;
+      }
       if (TOP2) {
         tidx[2 * gr] = b1;
         tresp[2 * gr] = (float)exp(a1 - l);
@@ -1771,12 +2166,6 @@ estep_lse_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp16,
         tresp[2 * gr + 1] = has2 ? (float)exp(a2 - l) : 0.f;
       }
     }
-  }
-  __syncthreads();
-  if (tid == 0 && llpart) {
-    double s = 0.0;
-    for (int i = 0; i < 64; ++i) s += sl[i];
-    llpart[blockIdx.x] = s;
   }
 }
 
@@ -1944,7 +2333,8 @@ hipError_t launch_precompute(const Plan& p, const float* mu, const float* var, c
   comp_consts_kernel<<<nblocks(p.Kp, 4), 256, 0, stream>>>(mu, var, logw, p.K, p.d, p.Kp, p.Kp16, w.c32,
                                                                w.c64e, w.c64d, w.compmax);
   pack_kernel<<<nblocks((int64_t)p.Kp * p.DP, 256), 256, 0, stream>>>(mu, var, p.K, p.d, p.Kp, p.Kp16, p.DP,
-                                                                        w.W32p, w.W64p, w.iv64, w.mup, w.ivp);
+                                                                        w.W32p, w.W64p, w.iv64, w.mup, w.ivp,
+                                                                        reinterpret_cast<float2*>(w.muvar));
   errc_kernel<<<1, 256, 0, stream>>>(w.compmax, p.K, w.errc);
   return hipGetLastError();
 }
@@ -1955,9 +2345,10 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
   const Workspace& w = p.ws;
   const int nthr = p.waves * 64;
   const int KS = p.waves * 32;
-  const size_t lds = (size_t)(2 * 64 * (32 * DT + 4) + 64 * (KS + 8) + 256) * sizeof(float) +
+  const size_t lds = (size_t)(2 * 64 * (32 * DT + 4) + 64 * (KS + 8) + 384) * sizeof(float) +
                      (size_t)nthr * sizeof(double) + (size_t)(p.waves * kRefCap + 64) * sizeof(uint32_t);
-  auto fn = p.stats_split ? estep_stats_kernel<DT, MODE, XT, true> : estep_stats_kernel<DT, MODE, XT, false>;
+  auto fn = (p.stats_split && MODE != 2) ? estep_stats_kernel<DT, MODE, XT, true>
+                                         : estep_stats_kernel<DT, MODE, XT, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -1966,28 +2357,52 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
   // values, both 16-byte aligned; 0 otherwise
   const bool al16 = reinterpret_cast<uintptr_t>(X) % 16 == 0;
   const int vec = sizeof(XT) == 4 ? (p.d % 4 == 0 && al16 ? 1 : 0) : (p.d % 8 == 0 && al16 ? 2 : 0);
+  const Pass1Out p1{w.p1h, w.p1v, w.p1k, w.rowE};
   fn<<<grid, nthr, lds, stream>>>(X, p.N, p.d, p.K, p.Kp, p.waves, p.kslabs, p.rows_per_chunk,
                                   reinterpret_cast<const float4*>(w.W32p), w.c32, w.mup, w.ivp, w.c64d, w.errc,
-                                  w.rowref, w.partials, w.llpart, ll_point, R, vec);
+                                  w.rowref, w.partials, w.llpart, ll_point, R, p1, p.drop_rho, vec);
   return hipGetLastError();
 }
 
+// The fp64 score pass: top-2 (TOP2) over all rows, or the normaliser
+// fallback over the rows the first pass's merge listed.
 template <int DT, bool TOP2, typename XT>
-static hipError_t run_lse(const Plan& p, const XT* X, float* ll_point, int32_t* idx, float* resp,
-                          hipStream_t stream) {
+static hipError_t run_lse(const Plan& p, const XT* X, int32_t* idx, float* resp, hipStream_t stream) {
   const Workspace& w = p.ws;
   const int Kt = p.Kp16 / 16;
+  const int32_t* rows = TOP2 ? nullptr : w.fblist;
+  const int32_t* nrows = TOP2 ? nullptr : w.fbcount;
+  float4* rowref = TOP2 ? nullptr : w.rowref;
   // Top-2 takes two point groups per wave even with many component tiles:
   // its extra state would otherwise keep the kernel from four waves per SIMD.
   if (Kt >= kLseWaves && !TOP2)
     estep_lse_kernel<DT, TOP2, XT, 4><<<(unsigned)p.tiles, 256, 0, stream>>>(
-        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp);
+        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, rows, nrows, w.rowE, rowref, w.lrow, idx, resp);
   else if (Kt >= 2)
     estep_lse_kernel<DT, TOP2, XT, 2><<<(unsigned)p.tiles, 256, 0, stream>>>(
-        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp);
+        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, rows, nrows, w.rowE, rowref, w.lrow, idx, resp);
   else
     estep_lse_kernel<DT, TOP2, XT, 1><<<(unsigned)p.tiles, 256, 0, stream>>>(
-        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, w.rowref, ll_point, w.llpart, idx, resp);
+        X, p.N, p.d, p.K, p.Kp16, w.W64p, w.c64e, rows, nrows, w.rowE, rowref, w.lrow, idx, resp);
+  return hipGetLastError();
+}
+
+// Normalisers of the two-pass regime: the fp32 first pass, the merge of its
+// records per row, the fp64 fallback for the rows the merge lists, and the
+// per-tile log-likelihood sums.
+template <int DT, typename XT>
+static hipError_t run_normalisers(const Plan& p, const XT* X, const float* mu, float* ll_point,
+                                  hipStream_t stream) {
+  const Workspace& w = p.ws;
+  fill_int_kernel<<<1, 64, 0, stream>>>(w.fbcount, 1, 0);
+  hipError_t e = run_stats<DT, 2>(p, X, mu, nullptr, nullptr, stream);
+  if (e != hipSuccess) return e;
+  lse_merge_kernel<DT, XT><<<(unsigned)p.tiles, 64, 0, stream>>>(
+      X, p.N, p.d, p.kslabs, 32 * p.waves, w.p1h, w.p1v, w.p1k, w.rowE, w.muvar, w.c64d, w.rowref, w.lrow,
+      w.fblist, w.fbcount);
+  e = run_lse<DT, false>(p, X, nullptr, nullptr, stream);
+  if (e != hipSuccess) return e;
+  row_ll_sum_kernel<<<(unsigned)p.tiles, 64, 0, stream>>>(w.lrow, p.N, ll_point, w.llpart);
   return hipGetLastError();
 }
 
@@ -2026,10 +2441,10 @@ static hipError_t estep_typed(const Plan& p, const XT* X, const float* mu, float
     return e;
   }
   switch (p.DT) {
-    case 1: e = run_lse<1, false>(p, X, ll_point, nullptr, nullptr, stream); break;
-    case 2: e = run_lse<2, false>(p, X, ll_point, nullptr, nullptr, stream); break;
-    case 3: e = run_lse<3, false>(p, X, ll_point, nullptr, nullptr, stream); break;
-    default: e = run_lse<4, false>(p, X, ll_point, nullptr, nullptr, stream); break;
+    case 1: e = run_normalisers<1>(p, X, mu, ll_point, stream); break;
+    case 2: e = run_normalisers<2>(p, X, mu, ll_point, stream); break;
+    case 3: e = run_normalisers<3>(p, X, mu, ll_point, stream); break;
+    default: e = run_normalisers<4>(p, X, mu, ll_point, stream); break;
   }
   if (e != hipSuccess) return e;
   switch (p.DT) {
@@ -2104,10 +2519,10 @@ hipError_t launch_top2(const Plan& p, const void* X, int x_dtype, int32_t* idx, 
   if (p.N == 0) return hipSuccess;
   return with_x_type(x_dtype, X, [&](auto x) {
     switch (p.DT) {
-      case 1: return run_lse<1, true>(p, x, nullptr, idx, resp, stream);
-      case 2: return run_lse<2, true>(p, x, nullptr, idx, resp, stream);
-      case 3: return run_lse<3, true>(p, x, nullptr, idx, resp, stream);
-      default: return run_lse<4, true>(p, x, nullptr, idx, resp, stream);
+      case 1: return run_lse<1, true>(p, x, idx, resp, stream);
+      case 2: return run_lse<2, true>(p, x, idx, resp, stream);
+      case 3: return run_lse<3, true>(p, x, idx, resp, stream);
+      default: return run_lse<4, true>(p, x, idx, resp, stream);
     }
   });
 }
