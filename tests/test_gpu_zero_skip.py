@@ -1,8 +1,9 @@
-"""GPU parity where most responsibilities are exactly zero.
+"""GPU parity where most responsibilities are zero or negligible.
 
 The fp32 statistics loop of the fused kernels visits, per wave, only the
-points with a nonzero responsibility among the wave's 32 components (a zero
-adds exactly zero). These cases make that skip extreme: components come in
+points with a responsibility above rho / max(1, |x|^2) (rho = 2^-20 / N)
+among the wave's 32 components; the points it leaves out move any statistic
+by at most about rho N = 2^-20. These cases make that skip extreme: components come in
 groups of 32 (one wave's slice each) whose centres are so far apart that a
 point's responsibilities outside its own group underflow to exactly zero.
 With rows sorted by group whole tiles belong to one group, so seven of eight
@@ -72,3 +73,81 @@ def test_stats_with_mostly_zero_responsibilities(G, regime, N, d, K, sort_rows):
     es = parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, X64, ref["R"].T @ np.abs(X64), what)
     parity.check_total(host(L), ref, what)
     print(f"{what}: stats {es[0]:.1e}/{es[1]:.1e}/{es[2]:.1e}", flush=True)
+
+
+@pytest.mark.parametrize("regime", [1, 2])
+def test_statistics_skip_bound_on_negligible_responsibilities(G, regime):
+    """Two blobs (std 0.5) 9.6 apart (components 0 and 1), thirty components far
+    from everything (2..31, responsibilities exactly zero), and two components
+    10 and 10.5 away from both blobs (32 and 33, the second wave's
+    32-component slice): every point's responsibilities for 32 and 33 are
+    tiny but mostly far above the fp32 underflow, so the statistics skip
+    leaves the second slice out for every point. Each statistic of the GPU must then be within
+    the skip's bound, 2^-20 (1 + 2E) summed over all points, plus the fp32
+    accumulation of the kept mass, of the oracle's."""
+    rng = np.random.default_rng(77)
+    N, d, K = 50_000, 8, 34
+    mu = np.zeros((K, d))
+    mu[0, 0], mu[1, 0] = -4.8, 4.8
+    mu[2:32] = 60.0 * np.eye(d)[2] + rng.normal(0.0, 1.0, (30, d))
+    mu[32, 1], mu[33, 1] = 8.77, 9.34
+    lab = rng.integers(0, 2, N)
+    X = (mu[lab] + rng.normal(0.0, 0.5, (N, d))).astype(np.float32)
+    mu = mu.astype(np.float32)
+    var = np.ones((K, d), np.float32)
+    logw = np.full(K, -np.log(K), np.float32)
+    ref = oracle.estep(X, mu, var, logw, keep_R=True)
+    far = ref["R"][:, 32:34]
+    assert far.max() < 1e-12 and (far > 1e-40).mean() > 0.5, "premise: negligible, mostly representable"
+    Nk, Sx, Sxx, L, lp = G.estep_stats(dev(X), dev(mu), dev(var), dev(logw), regime=regime,
+                                        want_point_loglik=True)
+    torch.cuda.synchronize()
+    X64 = X.astype(np.float64)
+    what = f"negligible responsibilities regime={regime}"
+    parity.check_loglik_point(host(lp), ref["l"], what)
+    parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, X64, ref["R"].T @ np.abs(X64), what)
+    bound = 1.1 * 2.0 ** -20
+    absx = ref["R"].T @ np.abs(X64)  # the fp32 accumulation of Sx scales with sum r |x|
+    for key, gpu, scale in (("Nk", host(Nk), ref["Nk"]), ("Sx", host(Sx), absx), ("Sxx", host(Sxx), ref["Sxx"])):
+        err = np.abs(gpu.astype(np.float64) - ref[key])
+        kept = 1e-6 * np.abs(scale if scale.ndim == err.ndim else scale[:, None])
+        assert (err <= bound + kept).all(), f"{what}: {key} off by {err.max():.3e}"
+    # the negligible components: everything the oracle gives them is below the bound
+    assert np.all(np.abs(host(Nk)[32:34] - ref["Nk"][32:34]) <= bound)
+    print(f"{what}: Nk of the negligible components {host(Nk)[32:34]} (oracle {ref['Nk'][32:34]})", flush=True)
+
+
+def test_normaliser_fallback_on_tied_slab_maximum(G):
+    """K = 300 (two 256-component slabs in the two-pass regime) with twelve exact
+    copies of one component near the data in the first slab: every row's
+    largest fp32 score is shared by twelve entries, more than the first
+    pass records per slab, so the merge cannot settle those rows from its
+    records and the fp64 normaliser pass takes them; twelve copies in the
+    second slab, below the row maxima, must not disturb anything. Against
+    the oracle, element by element; the copies' responsibilities must be
+    bitwise equal."""
+    rng = np.random.default_rng(5)
+    N, d, K = 3000, 24, 300
+    mu = rng.normal(0.0, 3.0, (K, d))
+    centre = rng.normal(0.0, 1.0, d)
+    mu[10:22] = centre              # ties at the row maximum, first slab
+    mu[270:282] = centre + 6.0      # ties below the row maximum, second slab
+    var = rng.uniform(0.8, 1.5, (K, d))
+    var[10:22] = 1.0
+    var[270:282] = 1.0
+    mu, var = mu.astype(np.float32), var.astype(np.float32)
+    logw = np.full(K, -np.log(K), np.float32)
+    X = (centre + rng.normal(0.0, 1.0, (N, d))).astype(np.float32)
+    ref = oracle.estep(X, mu, var, logw, keep_R=True)
+    args = (dev(X), dev(mu), dev(var), dev(logw))
+    Nk, Sx, Sxx, L, lp = G.estep_stats(*args, regime=2, want_point_loglik=True)
+    R, lr = G.estep_resp(*args, regime=2)
+    torch.cuda.synchronize()
+    X64 = X.astype(np.float64)
+    what = "tied slab maximum, two-pass"
+    parity.check_loglik_point(host(lp), ref["l"], what)
+    parity.check_resp(host(R), ref["R"], what)
+    parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, X64, ref["R"].T @ np.abs(X64), what)
+    parity.check_total(host(L), ref, what)
+    tie = host(R)[:, 10:22]
+    assert np.all(tie == tie[:, :1]), "exact copies must get bitwise equal responsibilities"
