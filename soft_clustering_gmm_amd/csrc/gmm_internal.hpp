@@ -43,6 +43,12 @@ struct Workspace {
   double* lrow;     // [N] per-row l_n (natural), before the block sums
   int32_t* fblist;  // [N] rows whose normaliser needs the fp64 pass
   int32_t* fbcount; // [1] number of such rows
+  // row lists of the second pass (two-pass regime, Plan::pass1):
+  float* rowSq;     // [N] |x|^2 of each row (fp32, from the first pass)
+  int32_t* slist;   // [kslabs][N] per slab, in increasing order, the rows it keeps
+  uint64_t* smask;  // [kslabs][tiles] per 64-row tile, the kept rows as a bit mask
+  int32_t* soff;    // [kslabs][tiles] kept rows per tile, then their exclusive prefix
+  int32_t* slen;    // [kslabs] length of each slab's list
   float* partials;  // [P][Kp][E] per-chunk statistics
   double* llpart;   // [max(P, tiles)] per-block log-likelihood sums
   float* stats;     // [K][1 + 2d] Nk | Sx | Sxx scratch for the EM loop

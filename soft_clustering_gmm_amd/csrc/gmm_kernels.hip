@@ -168,14 +168,17 @@ __device__ __forceinline__ double group_sum_d(double v, int tpr) {
 // XS/4 instructions spread over the waves. Chunks outside the data (the row
 // padding, features d..DP-1, rows past `hi`) receive finite filler copied
 // from a valid row: they only ever meet zero weights or r = 0.
+// With `rows` (a row list), tile positions [r0, r0 + 64) name rows
+// rows[r0 .. r0 + 63] instead (positions past `hi` take the last listed row).
 template <int XS>
 __device__ __forceinline__ void async_x_tile(float* xn, const float* X, int64_t r0, int64_t hi, int d,
-                                             int wave, int waves, int lane) {
+                                             int wave, int waves, int lane, const int32_t* rows) {
   constexpr int CPR = XS / 4;  // 16-byte chunks per LDS row
   for (int j = wave; j < CPR; j += waves) {
     const int ch = 64 * j + lane;
     const int row = ch / CPR, slot = ch - row * CPR;
-    const int64_t gr = r0 + row < hi ? r0 + row : hi - 1;
+    const int64_t pos = r0 + row < hi ? r0 + row : hi - 1;
+    const int64_t gr = rows ? (int64_t)rows[pos] : pos;
     const int q = 4 * slot < d ? slot : 0;
     __builtin_amdgcn_global_load_lds(X + gr * d + 4 * q,
                                      reinterpret_cast<__attribute__((address_space(3))) void*>(
@@ -186,23 +189,26 @@ __device__ __forceinline__ void async_x_tile(float* xn, const float* X, int64_t 
 
 // Rows [r0, r0 + 64) of X -> LDS tile [64][XS], zero padded to DP features
 // and past `hi`. `vec`: X rows are 16-byte aligned float rows (d % 4 == 0).
+// With `rows`, positions name listed rows as in async_x_tile.
 template <int XS, typename XT>
 __device__ __forceinline__ void load_x_tile(float* xs, const XT* X, int64_t r0, int64_t hi, int d, int DP,
-                                            int tid, int nthr, int vec) {
+                                            int tid, int nthr, int vec, const int32_t* rows = nullptr) {
   if (vec && sizeof(XT) == 4) {
     const float* Xf = reinterpret_cast<const float*>(X);
     for (int ch = tid; ch < 16 * DP; ch += nthr) {
       const int row = ch / (DP / 4), q = ch - row * (DP / 4);
-      const int64_t gr = r0 + row;
+      const int64_t pos = r0 + row;
+      const int64_t gr = pos < hi && rows ? (int64_t)rows[pos] : pos;
       *reinterpret_cast<float4*>(xs + row * XS + 4 * q) =
-          (gr < hi && 4 * q < d) ? *reinterpret_cast<const float4*>(Xf + gr * d + 4 * q)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+          (pos < hi && 4 * q < d) ? *reinterpret_cast<const float4*>(Xf + gr * d + 4 * q)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   } else {
     for (int e = tid; e < 64 * DP; e += nthr) {
       const int row = e / DP, f = e - row * DP;
-      const int64_t gr = r0 + row;
-      xs[row * XS + f] = (gr < hi && f < d) ? load_x(X, gr * d + f) : 0.f;
+      const int64_t pos = r0 + row;
+      const int64_t gr = pos < hi && rows ? (int64_t)rows[pos] : pos;
+      xs[row * XS + f] = (pos < hi && f < d) ? load_x(X, gr * d + f) : 0.f;
     }
   }
 }
@@ -442,6 +448,7 @@ struct Pass1Out {
   float* v;       // [kslabs][N][kCandT] candidate scores
   uint8_t* k;     // [kslabs][N][kCandT] candidate components within the slab
   float* rowE;    // [N] the row's fp32 score error bound (written by slab 0)
+  float* rowSq;   // [N] the row's |x|^2 in fp32 (written by slab 0)
 };
 
 template <int DT, int MODE, typename XT, bool SPLIT>
@@ -452,7 +459,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
                    const double* __restrict__ c64d, const float* __restrict__ errc,
                    const float4* __restrict__ rowref, float* __restrict__ partials,
                    double* __restrict__ llpart, float* __restrict__ ll_point, float* __restrict__ R,
-                   Pass1Out p1, float rho, int vec) {
+                   Pass1Out p1, float rho, const int32_t* __restrict__ slab_rows,
+                   const int32_t* __restrict__ slab_len, int vec) {
   constexpr int DP = 32 * DT, Q = DP / 4, XS = DP + 4, E = 1 + 2 * DP;
   extern __shared__ __align__(16) float smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
@@ -497,8 +505,22 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   float nk = 0.f;
   double ll_acc = 0.0;
 
-  const int64_t lo = chunk * rows_per_chunk;
-  const int64_t hi = min(N, lo + rows_per_chunk);
+  // Row positions [lo, hi) of this block: rows lo..hi-1, or (second pass
+  // with row lists) positions in the slab's list of the rows that hold a
+  // responsibility above the statistics threshold, the list cut into as many
+  // equal chunks (multiples of 64) as the grid has per slab.
+  const int32_t* rows = MODE == 1 && slab_rows ? slab_rows + (size_t)slab * N : nullptr;
+  int64_t lo, hi;
+  if (rows) {
+    const int64_t len = slab_len[slab], nch = gridDim.x / kslabs;
+    const int64_t rpc = ((len + nch - 1) / nch + 63) / 64 * 64;
+    lo = min(len, chunk * rpc);
+    hi = min(len, lo + rpc);
+  } else {
+    lo = chunk * rows_per_chunk;
+    hi = min(N, lo + rows_per_chunk);
+  }
+  auto row_at = [&](int64_t pos) { return rows ? (int64_t)rows[pos] : pos; };
   // The score operands are read through a buffer resource over this wave's
   // slab: the loads are then opaque to the IR optimiser, which would otherwise
   // fold the rotating prefetch registers below into one load per use.
@@ -517,14 +539,14 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   constexpr bool kHalfPre = sizeof(XT) == 2 && DT <= 3;
   const bool hpref = kHalfPre && vec == 2 && 8 * DP <= 2 * nthr;
   uint4 hpre[2];
-  load_x_tile<XS>(xsb, X, lo, hi, d, DP, tid, nthr, vec);
+  if (lo < hi) load_x_tile<XS>(xsb, X, lo, hi, d, DP, tid, nthr, vec, rows);
   int cur = 0;
   for (int64_t r0 = lo; r0 < hi; r0 += 64) {
     float* xs = xsb + cur * 64 * XS;
     __syncthreads();
     if (MODE == 1 && tid < 64) {
-      const int64_t gr = r0 + tid;
-      const float4 mr = gr < hi ? rowref[gr] : make_float4(0.f, 0.f, INFINITY, 0.f);
+      const int64_t pos = r0 + tid;
+      const float4 mr = pos < hi ? rowref[row_at(pos)] : make_float4(0.f, 0.f, INFINITY, 0.f);
       rv[4 * tid] = mr.x;
       rv[4 * tid + 1] = mr.y;
       rv[4 * tid + 2] = mr.z;
@@ -618,6 +640,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         if (slab == 0 && psub == 0) {
           const float sq = xq[2 * row], ab = xq[2 * row + 1];
           p1.rowE[grow] = gam * (a_max * sq + fminf(b_max * ab, b2_max * sqrtf(sq))) + 2.f * kUnitRound * c_max;
+          p1.rowSq[grow] = sq;
         }
         if (mine) {
           size_t slot = rec * kCandT + (size_t)(incl - mine);
@@ -872,15 +895,15 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     // 4. statistics, with the next X tile streaming into the other buffer
     const int64_t rn = r0 + 64;
     if (async_x && rn < hi) async_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, reinterpret_cast<const float*>(X),
-                                             rn, hi, d, wave, waves, lane);
+                                             rn, hi, d, wave, waves, lane, rows);
     if constexpr (kHalfPre)
       if (hpref && rn < hi)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int ch = tid + nthr * i, row = ch / (DP / 8), q = ch - row * (DP / 8);
-        const int64_t gr = rn + row;
-        hpre[i] = (ch < 8 * DP && gr < hi && 8 * q < d) ? *reinterpret_cast<const uint4*>(X + gr * d + 8 * q)
-                                                        : make_uint4(0u, 0u, 0u, 0u);
+        const int64_t pos = rn + row;
+        const bool in = ch < 8 * DP && pos < hi && 8 * q < d;
+        hpre[i] = in ? *reinterpret_cast<const uint4*>(X + row_at(pos) * d + 8 * q) : make_uint4(0u, 0u, 0u, 0u);
       }
     if constexpr (MODE == 2) {
       // the first pass accumulates no statistics
@@ -998,10 +1021,10 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           }
         }
       } else if (rn < hi) {
-        load_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, X, rn, hi, d, DP, tid, nthr, vec);
+        load_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, X, rn, hi, d, DP, tid, nthr, vec, rows);
       }
     } else if (rn < hi && !async_x) {
-      load_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, X, rn, hi, d, DP, tid, nthr, vec);
+      load_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, X, rn, hi, d, DP, tid, nthr, vec, rows);
     }
     // This thread's async tile loads have landed. The wait is unconditional so
     // that no global->LDS load counts as in flight at the top of the loop:
@@ -1276,6 +1299,87 @@ __global__ void __launch_bounds__(64) row_ll_sum_kernel(const double* __restrict
     double a = 0.0;
     for (int i = 0; i < 64; ++i) a += s[i];
     llpart[blockIdx.x] = a;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row lists of the second pass (two-pass regime)
+// ---------------------------------------------------------------------------
+//
+// The statistics leave out a point's contribution to a slice of components
+// when every responsibility it holds there is at most rho / max(1, |x|^2)
+// (the threshold of the in-kernel skip). Whole slabs can be ruled out per row
+// from the first pass alone: with the slab's largest fp32 score m_s and the
+// row's (m, lZ, E) in base 2, every entry of the slab has
+//   r <= 2^(m_s + E2 - m - lZ)
+// (its exact score is within E2 of its fp32 one, and the second pass uses
+// either), so a slab with m_s + E2 - m - lZ < log2(rho / max(1, |x|^2)) holds
+// no responsibility the statistics would take. The check runs in fp64 with
+// 1/64 of slack against the rounding of the fp32 inputs; rows it cannot decide
+// (NaN) are kept. Each slab's list then holds, in increasing order, the rows
+// it keeps, and the second pass walks only those.
+
+// Per (64-row tile, slab): the kept rows as a bit mask and their count.
+__global__ void __launch_bounds__(64) slab_keep_kernel(const float4* __restrict__ p1h,
+                                                       const float4* __restrict__ rowref,
+                                                       const float* __restrict__ rowSq, int64_t N, int64_t tiles,
+                                                       float rho, uint64_t* __restrict__ smask,
+                                                       int32_t* __restrict__ scnt) {
+  const int slab = blockIdx.y;
+  const int64_t t = blockIdx.x, n = t * 64 + threadIdx.x;
+  bool keep = false;
+  if (n < N) {
+    const float ms = p1h[(size_t)slab * N + n].y;
+    const float4 rr = rowref[n];
+    const double lhs = (double)ms - (double)rr.x - (double)rr.y + (double)rr.w * kLog2E + 1.0 / 64;
+    const double rhs = log2((double)rho) - log2(fmax(1.0, (double)rowSq[n]));
+    keep = !(lhs < rhs);
+  }
+  const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+  if (threadIdx.x == 0) {
+    smask[(size_t)slab * tiles + t] = m;
+    scnt[(size_t)slab * tiles + t] = __builtin_popcountll(m);
+  }
+}
+
+// One block of 256 per slab: the tile counts become their exclusive prefix
+// (in place), the total the slab's list length.
+__global__ void __launch_bounds__(256) slab_scan_kernel(int32_t* __restrict__ soff, int64_t tiles,
+                                                        int32_t* __restrict__ slen) {
+  __shared__ int32_t part[256];
+  int32_t* c = soff + (size_t)blockIdx.x * tiles;
+  const int64_t per = (tiles + 255) / 256;
+  const int64_t lo = min(tiles, threadIdx.x * per), hi = min(tiles, lo + per);
+  int32_t a = 0;
+  for (int64_t i = lo; i < hi; ++i) a += c[i];
+  part[threadIdx.x] = a;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {  // inclusive scan of the 256 segment sums
+    const int32_t v = (int)threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int32_t run = part[threadIdx.x] - a;
+  for (int64_t i = lo; i < hi; ++i) {
+    const int32_t v = c[i];
+    c[i] = run;
+    run += v;
+  }
+  if (threadIdx.x == 255) slen[blockIdx.x] = part[255];
+}
+
+// Per (64-row tile, slab): the kept rows to their places in the slab's list.
+__global__ void __launch_bounds__(64) slab_scatter_kernel(const uint64_t* __restrict__ smask,
+                                                          const int32_t* __restrict__ soff, int64_t N,
+                                                          int64_t tiles, int32_t* __restrict__ slist) {
+  const int slab = blockIdx.y;
+  const int64_t t = blockIdx.x;
+  const uint64_t m = smask[(size_t)slab * tiles + t];
+  const int lane = threadIdx.x;
+  if ((m >> lane) & 1u) {
+    const int rank = __builtin_popcountll(m & ((1ull << lane) - 1ull));
+    slist[(size_t)slab * N + soff[(size_t)slab * tiles + t] + rank] = (int32_t)(t * 64 + lane);
   }
 }
 
@@ -2357,10 +2461,13 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
   // values, both 16-byte aligned; 0 otherwise
   const bool al16 = reinterpret_cast<uintptr_t>(X) % 16 == 0;
   const int vec = sizeof(XT) == 4 ? (p.d % 4 == 0 && al16 ? 1 : 0) : (p.d % 8 == 0 && al16 ? 2 : 0);
-  const Pass1Out p1{w.p1h, w.p1v, w.p1k, w.rowE};
+  const Pass1Out p1{w.p1h, w.p1v, w.p1k, w.rowE, w.rowSq};
+  // the second pass walks the slabs' row lists, except when it also writes R
+  const bool lists = MODE == 1 && p.pass1 && !R;
   fn<<<grid, nthr, lds, stream>>>(X, p.N, p.d, p.K, p.Kp, p.waves, p.kslabs, p.rows_per_chunk,
                                   reinterpret_cast<const float4*>(w.W32p), w.c32, w.mup, w.ivp, w.c64d, w.errc,
-                                  w.rowref, w.partials, w.llpart, ll_point, R, p1, p.drop_rho, vec);
+                                  w.rowref, w.partials, w.llpart, ll_point, R, p1, p.drop_rho,
+                                  lists ? w.slist : nullptr, lists ? w.slen : nullptr, vec);
   return hipGetLastError();
 }
 
@@ -2403,6 +2510,11 @@ static hipError_t run_normalisers(const Plan& p, const XT* X, const float* mu, f
   e = run_lse<DT, false>(p, X, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
   row_ll_sum_kernel<<<(unsigned)p.tiles, 64, 0, stream>>>(w.lrow, p.N, ll_point, w.llpart);
+  // the second pass's row lists
+  const dim3 tg((unsigned)p.tiles, (unsigned)p.kslabs);
+  slab_keep_kernel<<<tg, 64, 0, stream>>>(w.p1h, w.rowref, w.rowSq, p.N, p.tiles, p.drop_rho, w.smask, w.soff);
+  slab_scan_kernel<<<(unsigned)p.kslabs, 256, 0, stream>>>(w.soff, p.tiles, w.slen);
+  slab_scatter_kernel<<<tg, 64, 0, stream>>>(w.smask, w.soff, p.N, p.tiles, w.slist);
   return hipGetLastError();
 }
 
