@@ -134,7 +134,6 @@ static int make_plan_impl(int64_t N, int d, int K, int regime, void* base, Plan*
   const size_t o_ivp = take((size_t)p.Kp * p.DP * sizeof(double));
   // (the parameter regions above do not depend on N: the row-chunked E-step
   // packs them once for plans of several chunk sizes)
-  const size_t o_muvar = take(p.pass1 ? (size_t)p.Kp * p.DP * 2 * sizeof(float) : 0);
   const size_t o_cmax = take((size_t)K * 4 * sizeof(float));
   const size_t o_errc = take(4 * sizeof(float));
   // per-row normalisers and first-pass records: only the two-pass regime has a first pass
@@ -182,7 +181,6 @@ static int make_plan_impl(int64_t N, int d, int K, int regime, void* base, Plan*
     p.ws.p1v = p.pass1 ? reinterpret_cast<float*>(b + o_p1v) : nullptr;
     p.ws.p1k = p.pass1 ? reinterpret_cast<uint8_t*>(b + o_p1k) : nullptr;
     p.ws.rowE = p.pass1 ? reinterpret_cast<float*>(b + o_rowE) : nullptr;
-    p.ws.muvar = p.pass1 ? reinterpret_cast<float*>(b + o_muvar) : nullptr;
     p.ws.lrow = p.pass1 ? reinterpret_cast<double*>(b + o_lrow) : nullptr;
     p.ws.fblist = p.pass1 ? reinterpret_cast<int32_t*>(b + o_fbl) : nullptr;
     p.ws.fbcount = p.pass1 ? reinterpret_cast<int32_t*>(b + o_fbc) : nullptr;

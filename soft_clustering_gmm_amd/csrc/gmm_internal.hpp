@@ -39,7 +39,6 @@ struct Workspace {
   float* p1v;       // [kslabs][N][kCandT] candidate scores (base 2, fp32)
   uint8_t* p1k;     // [kslabs][N][kCandT] their components within the slab
   float* rowE;      // [N] per-row fp32 score error bound E (natural units)
-  float* muvar;     // [Kp][DP] (mean, variance) pairs, variance +inf past d (exact re-score of the merge)
   double* lrow;     // [N] per-row l_n (natural), before the block sums
   int32_t* fblist;  // [N] rows whose normaliser needs the fp64 pass
   int32_t* fbcount; // [1] number of such rows

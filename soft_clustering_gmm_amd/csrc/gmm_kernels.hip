@@ -130,14 +130,16 @@ __device__ __forceinline__ double dpp_d(double v) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
-// DPP lane permutations within a row of 16 lanes: quad xor 1, quad xor 2 and
-// the mirror within each half row (i <-> 7 - i). Applied in this order as add
-// steps they leave every lane of an aligned group of 8 with the group's sum
-// (the quad sums, then the half-row sums), bitwise identical on all 8 lanes.
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141;
+// DPP lane permutations within a row of 16 lanes: quad xor 1, quad xor 2, the
+// mirror within each half row (i <-> 7 - i) and the mirror of the whole row
+// (i <-> 15 - i). Applied in this order as add steps they leave every lane of
+// an aligned group of 8 (16) with the group's sum (the quad sums, the half-row
+// sums, then the two halves joined), bitwise identical on all of its lanes
+// (the last step adds the same two values in either order).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 
 // All-reduce over aligned groups of tpr consecutive lanes (tpr a power of two
-// <= 8) with the DPP steps above; every lane of a group ends with the same
+// <= 16) with the DPP steps above; every lane of a group ends with the same
 // value.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -147,18 +149,21 @@ __device__ __forceinline__ float group_max(float v, int tpr) {
   if (tpr > 1) v = fmaxf(v, dpp_f<kDppXor1>(v));
   if (tpr > 2) v = fmaxf(v, dpp_f<kDppXor2>(v));
   if (tpr > 4) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  if (tpr > 8) v = fmaxf(v, dpp_f<kDppMirror>(v));
   return v;
 }
 __device__ __forceinline__ float group_sum(float v, int tpr) {
   if (tpr > 1) v += dpp_f<kDppXor1>(v);
   if (tpr > 2) v += dpp_f<kDppXor2>(v);
   if (tpr > 4) v += dpp_f<kDppHalfMirror>(v);
+  if (tpr > 8) v += dpp_f<kDppMirror>(v);
   return v;
 }
 __device__ __forceinline__ double group_sum_d(double v, int tpr) {
   if (tpr > 1) v += dpp_d<kDppXor1>(v);
   if (tpr > 2) v += dpp_d<kDppXor2>(v);
   if (tpr > 4) v += dpp_d<kDppHalfMirror>(v);
+  if (tpr > 8) v += dpp_d<kDppMirror>(v);
   return v;
 }
 
@@ -274,14 +279,14 @@ __global__ void comp_consts_kernel(const float* __restrict__ mu, const float* __
 __global__ void pack_kernel(const float* __restrict__ mu, const float* __restrict__ var, int K, int d,
                             int Kp, int Kp16, int DP, float* __restrict__ W32p,
                             double* __restrict__ W64p, double* __restrict__ iv64,
-                            float* __restrict__ mup, double* __restrict__ ivp, float2* __restrict__ muvar) {
+                            float* __restrict__ mup, double* __restrict__ ivp) {
   const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (t >= (int64_t)Kp * DP) return;
   const int k = (int)(t / DP), f = (int)(t - (int64_t)k * DP);
   double A = 0.0, B = 0.0, iv = 0.0;
-  float m = 0.f, v = INFINITY;
+  float m = 0.f;
   if (k < K && f < d) {
-    v = var[(size_t)k * d + f];
+    const float v = var[(size_t)k * d + f];
     iv = 1.0 / (double)v;
     m = mu[(size_t)k * d + f];
     A = -0.5 * iv;
@@ -290,7 +295,6 @@ __global__ void pack_kernel(const float* __restrict__ mu, const float* __restric
   }
   mup[t] = m;
   ivp[t] = iv;
-  if (muvar) muvar[t] = make_float2(m, v);
   {
     // fp32 score operands, base-2 scaled like c32: lane (h, c) of feature
     // block q (features 4q..4q+3) holds A of features 4q + 2h + {0, 1} in
@@ -328,19 +332,18 @@ __global__ void errc_kernel(const float* __restrict__ compmax, int K, float* __r
   if (threadIdx.x < 4) errc[threadIdx.x] = s[threadIdx.x][0];
 }
 
-// Score tile of one wave: s_k(x) = sum_j (A_kj x_j^2 + B_kj x_j) + c_k for the
+// Score tile of one wave: s_k(x) - c_k = sum_j (A_kj x_j^2 + B_kj x_j) for the
 // 64 rows of the LDS tile `xs` and the wave's 32 components (operands W from
-// the buffer resource `wrs`, constant `ck` of component c of this lane), on
-// two 32x32x2 fp32 MFMA accumulators (rows 0-31 and 32-63). The scores go to
-// the wave's 32 columns of the LDS score tile `sc` (row stride SCS); wave 0
-// also writes |x|^2 and |x|_1 of each row to `xq` (inputs of the error bound).
+// the buffer resource `wrs`), on two 32x32x2 fp32 MFMA accumulators (rows
+// 0-31 in acc0, 32-63 in acc1; score_store adds c_k and writes them to the
+// wave's 32 columns of an LDS score tile); wave 0 also writes |x|^2 and |x|_1
+// of each row to `xq` (inputs of the error bound).
 template <int DT>
-__device__ __forceinline__ void score_tile(const float* xs, float* sc, float* xq, __amdgpu_buffer_rsrc_t wrs,
-                                           float ck, int wave, int lane, int SCS) {
+__device__ __forceinline__ void score_acc(const float* xs, float* xq, __amdgpu_buffer_rsrc_t wrs, int wave,
+                                          int lane, v16f& acc0, v16f& acc1) {
   constexpr int DP = 32 * DT, Q = DP / 4, XS = DP + 4;
   const int h = lane >> 5, c = lane & 31;
   auto wload = [&](int q) { return __builtin_amdgcn_raw_buffer_load_b128(wrs, (q * 64 + lane) * 16, 0, 0); };
-  v16f acc0, acc1;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     acc0[j] = 0.f;
@@ -399,11 +402,6 @@ __device__ __forceinline__ void score_tile(const float* xs, float* sc, float* xq
     __builtin_amdgcn_sched_barrier(0);
     step(pb0, pb1, wd);
   }
-  // The store base goes through an empty asm so that the 32 store
-  // addresses are formed here, per tile, instead of being hoisted out of
-  // the tile loop and held (or spilled) across it.
-  int scb = 4 * h * SCS + wave * 32 + c;
-  asm volatile("" : "+v"(scb));
   if (wave == 0) {
     // the two halves of the wave hold the two halves of each row's features
     sq0 += __shfl_xor(sq0, 32, 64);
@@ -417,12 +415,34 @@ __device__ __forceinline__ void score_tile(const float* xs, float* sc, float* xq
       xq[2 * (c + 32) + 1] = ab1;
     }
   }
+}
+
+// One 32-row accumulator of score_acc, plus the component constants, to
+// rows row0 .. row0 + 31 of the LDS score tile (row stride SCS).
+__device__ __forceinline__ void score_store(float* sc, const v16f& acc, int row0, float ck, int wave, int lane,
+                                            int SCS) {
+  const int h = lane >> 5, c = lane & 31;
+  // The store base goes through an empty asm so that the 16 store
+  // addresses are formed here, per tile, instead of being hoisted out of
+  // the tile loop and held (or spilled) across it.
+  int scb = (4 * h + row0) * SCS + wave * 32 + c;
+  asm volatile("" : "+v"(scb));
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int r = ((j >> 2) << 3) + (j & 3);  // acc_row(h, j) - 4 h
-    sc[scb + r * SCS] = acc0[j] + ck;
-    sc[scb + (r + 32) * SCS] = acc1[j] + ck;
+    sc[scb + r * SCS] = acc[j] + ck;
   }
+}
+
+// Scores of a 64-row X tile against the wave's 32 components into the LDS
+// score tile [64][SCS] (see score_acc), |x|^2 and |x|_1 of the rows into xq.
+template <int DT>
+__device__ __forceinline__ void score_tile(const float* xs, float* sc, float* xq, __amdgpu_buffer_rsrc_t wrs,
+                                           float ck, int wave, int lane, int SCS) {
+  v16f acc0, acc1;
+  score_acc<DT>(xs, xq, wrs, wave, lane, acc0, acc1);
+  score_store(sc, acc0, 0, ck, wave, lane, SCS);
+  score_store(sc, acc1, 32, ck, wave, lane, SCS);
 }
 
 // ---------------------------------------------------------------------------
@@ -451,8 +471,11 @@ struct Pass1Out {
   float* rowSq;   // [N] the row's |x|^2 in fp32 (written by slab 0)
 };
 
+// The first pass (MODE 2) keeps one X tile and half a score tile in LDS and
+// fits in 128 registers, so that two blocks share a CU and one block's row
+// phase overlaps the other's score MFMAs.
 template <int DT, int MODE, typename XT, bool SPLIT>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 4 : 1)))
 estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, int waves, int kslabs,
                    int64_t rows_per_chunk, const float4* __restrict__ W32p, const float* __restrict__ c32,
                    const float* __restrict__ mup, const double* __restrict__ ivp,
@@ -466,14 +489,28 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
   const int nthr = blockDim.x;
   const int KS = waves * 32, SCS = KS + 8;
-  const int64_t chunk = blockIdx.x / kslabs;
-  const int slab = blockIdx.x - (int)(chunk * kslabs);
+  // (chunk, slab) of this block. The first pass's grid is a multiple of
+  // 8 * kslabs: block b runs on XCD b % 8, and the slabs of a chunk are given
+  // to blocks of one XCD, which then read the chunk's X tiles from one L2.
+  int64_t chunk;
+  int slab;
+  if (MODE == 2 && gridDim.x % (8u * (unsigned)kslabs) == 0) {
+    const int j = (int)(blockIdx.x >> 3);
+    chunk = (int64_t)(blockIdx.x & 7) + 8 * (int64_t)(j / kslabs);
+    slab = j % kslabs;
+  } else {
+    chunk = blockIdx.x / kslabs;
+    slab = blockIdx.x - (int)(chunk * kslabs);
+  }
   const int k0 = slab * KS;
   const int kw = k0 + wave * 32;
-  float* xsb = smem;             // [2][64][XS]: current and next X tile
-  float* sc = xsb + 2 * 64 * XS; // [64][SCS]
-  float* rv = sc + 64 * SCS;     // [64][4] per-row references (m, lZ or 1/z, theta)
-  float* xq = rv + 256;          // [64][2] |x|^2 and |x|_1 of the tile's rows
+  // The first pass has no rv, lls, reflist or nzrow, one X tile and a score
+  // tile of 32 rows.
+  constexpr int kXT = MODE == 2 ? 1 : 2, kSR = MODE == 2 ? 32 : 64;
+  float* xsb = smem;               // [kXT][64][XS]: current (and next) X tile
+  float* sc = xsb + kXT * 64 * XS; // [kSR][SCS]
+  float* rv = sc + kSR * SCS;      // [64][4] per-row references (m, lZ or 1/z, theta)
+  float* xq = rv + (MODE == 2 ? 0 : 256);  // [64][2] |x|^2 and |x|_1 of the tile's rows
   double* lls = reinterpret_cast<double*>(xq + 128);  // [nthr]
   uint32_t* reflist = reinterpret_cast<uint32_t*>(lls + nthr);  // [waves][kRefCap]
   uint32_t* nzrow = reflist + waves * kRefCap;  // [64]: bit w = row has a nonzero r for wave w
@@ -539,7 +576,118 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   constexpr bool kHalfPre = sizeof(XT) == 2 && DT <= 3;
   const bool hpref = kHalfPre && vec == 2 && 8 * DP <= 2 * nthr;
   uint4 hpre[2];
+  // The first pass has no statistics phase to hide the next tile's load
+  // under: there the next tile is fetched into registers (16-byte chunks,
+  // fp32 rows with d % 4 == 0 or half-precision rows with d % 8 == 0) when the
+  // row phase starts, and written over the (single) X tile when it ends.
+  // (Not at DT = 4, where those registers would spill at the first pass's
+  // 128-register budget; the other block on the CU covers that load.)
+  constexpr int kP1Chunks = sizeof(XT) == 4 ? DT : (DT + 1) / 2;  // per thread, at 512 threads
+  const bool p1pre = MODE == 2 && DT <= 3 && vec != 0 && nthr * kP1Chunks * (sizeof(XT) == 4 ? 4 : 8) >= 64 * DP;
+  uint4 p1x[kP1Chunks];
   if (lo < hi) load_x_tile<XS>(xsb, X, lo, hi, d, DP, tid, nthr, vec, rows);
+  // First-pass row phase over 32 rows of the tile (rows rb .. rb + 31, their
+  // |x|^2 and |x|_1 at xq rows xrow0 ..): T2 = 2 * waves threads per row, four
+  // 16-byte chunks of the 32 * waves-entry score row each (entries
+  // 4 (psub + T2 i) + u).
+  auto p1_rows = [&](int64_t rb, int xrow0) {
+    constexpr int NC = 4;
+    const int T2 = 2 * waves;
+    // First pass (fp32 normalisers), per (row, slab): the slab maximum m,
+    // z = sum 2^(s - m) over the slab, and the candidates: every entry with
+    // s >= th, th the loosest of m - W (W on the ladder kCapLadder, ending
+    // with m itself) that admits at most kCandT entries; if even m admits
+    // more, th is the next float above m and nothing is recorded. So every
+    // entry of the slab at or above th is recorded and none below it is;
+    // the merge step relies on exactly that.
+    const int row = tid / T2, psub = tid - row * T2;
+    const int64_t grow = rb + row;
+    const bool valid = grow < hi;
+    const float4* srow4 = reinterpret_cast<const float4*>(sc + row * SCS);
+    float4 ev[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) ev[i] = srow4[psub + T2 * i];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) mx = fmaxf(mx, fmaxf(fmaxf(ev[i].x, ev[i].y), fmaxf(ev[i].z, ev[i].w)));
+    const float m = group_max(mx, T2);
+    const float ms = m == -INFINITY ? 0.f : m;  // a slab whose entries are all -inf has z = 0
+    double z = 0.0;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const float4 v = ev[i];
+      // fp32 sums of four e <= 1, gathered in fp64: |dz| <= 2 u z
+      z += (double)((__builtin_amdgcn_exp2f(v.x - ms) + __builtin_amdgcn_exp2f(v.y - ms)) +
+                    (__builtin_amdgcn_exp2f(v.z - ms) + __builtin_amdgcn_exp2f(v.w - ms)));
+    }
+    z = group_sum_d(z, T2);
+    auto count_ge = [&](float th) {
+      int c = 0;
+      if (mx >= th)
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+          c += (int)(ev[i].x >= th) + (int)(ev[i].y >= th) + (int)(ev[i].z >= th) + (int)(ev[i].w >= th);
+      return c;
+    };
+    float th = -INFINITY;
+    int mine = 0, cnt = 0;
+    if (m != -INFINITY) {
+      th = m - kCapLadder[0];
+      mine = count_ge(th);
+      cnt = (int)group_sum((float)mine, T2);
+      if (cnt > kCandT) {
+        // the loosest level that admits at most kCandT: counts only fall
+        // along the ladder, so bisect levels [1, kCapLevels); kCapLevels
+        // stands for none
+        int lo = 1, hi = kCapLevels;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if ((int)group_sum((float)count_ge(m - kCapLadder[mid]), T2) <= kCandT)
+            hi = mid;
+          else
+            lo = mid + 1;
+        }
+        if (lo < kCapLevels) {
+          th = m - kCapLadder[lo];
+          mine = count_ge(th);
+          cnt = (int)group_sum((float)mine, T2);
+        } else {
+          th = next_up(m);
+          mine = 0;
+          cnt = 0;
+        }
+      }
+    }
+    // this thread's first slot: exclusive prefix of the counts over the row's lanes
+    int incl = mine;
+    for (int o = 1; o < T2; o <<= 1) {
+      const int t = __shfl_up(incl, o, T2);
+      if (psub >= o) incl += t;
+    }
+    if (valid) {
+      const size_t rec = (size_t)slab * N + grow;
+      if (psub == 0) p1.h[rec] = make_float4((float)z, m, th, (float)cnt);
+      if (slab == 0 && psub == 0) {
+        const float sq = xq[2 * (xrow0 + row)], ab = xq[2 * (xrow0 + row) + 1];
+        p1.rowE[grow] = gam * (a_max * sq + fminf(b_max * ab, b2_max * sqrtf(sq))) + 2.f * kUnitRound * c_max;
+        p1.rowSq[grow] = sq;
+      }
+      if (mine) {
+        size_t slot = rec * kCandT + (size_t)(incl - mine);
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const float vv[4] = {ev[i].x, ev[i].y, ev[i].z, ev[i].w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (vv[u] >= th) {
+              p1.v[slot] = vv[u];
+              p1.k[slot] = (uint8_t)(4 * (psub + T2 * i) + u);
+              ++slot;
+            }
+        }
+      }
+    }
+  };
   int cur = 0;
   for (int64_t r0 = lo; r0 < hi; r0 += 64) {
     float* xs = xsb + cur * 64 * XS;
@@ -552,8 +700,15 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       rv[4 * tid + 2] = mr.z;
     }
 
-    // 2. scores
-    score_tile<DT>(xs, sc, xq, wrs, ck, wave, lane, SCS);
+    // 2. scores (the first pass stores them a half tile at a time)
+    v16f acc1;
+    if constexpr (MODE == 2) {
+      v16f acc0;
+      score_acc<DT>(xs, xq, wrs, wave, lane, acc0, acc1);
+      score_store(sc, acc0, 0, ck, wave, lane, SCS);
+    } else {
+      score_tile<DT>(xs, sc, xq, wrs, ck, wave, lane, SCS);
+    }
     __syncthreads();
 
     // 3. row phase. The score tile holds s / ln 2 (operands and constants are
@@ -563,100 +718,22 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     //    the error bound E stays in natural units (scaling by log2(e) and
     //    back cancels in the bound).
     if constexpr (MODE == 2) {
-      // First pass (fp32 normalisers), per (row, slab): the slab maximum m,
-      // z = sum 2^(s - m) over the slab, and the candidates: every entry with
-      // s >= th, th the loosest of m - W (W on the ladder kCapLadder, ending
-      // with m itself) that admits at most kCandT entries; if even m admits
-      // more, th is the next float above m and nothing is recorded. So every
-      // entry of the slab at or above th is recorded and none below it is;
-      // the merge step relies on exactly that.
-      const int row = prow;
-      const int64_t grow = r0 + row;
-      const bool valid = grow < hi;
-      const float4* srow4 = reinterpret_cast<const float4*>(sc + row * SCS);
-      float4 ev[8];
+      if (p1pre && r0 + 64 < hi) {
+        constexpr int VPC = sizeof(XT) == 4 ? 4 : 8;  // values per 16-byte chunk
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ev[i] = srow4[psub + tpr * i];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fmaxf(fmaxf(ev[i].x, ev[i].y), fmaxf(ev[i].z, ev[i].w)));
-      const float m = group_max(mx, tpr);
-      const float ms = m == -INFINITY ? 0.f : m;  // a slab whose entries are all -inf has z = 0
-      double z = 0.0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float4 v = ev[i];
-        // fp32 sums of four e <= 1, gathered in fp64: |dz| <= 2 u z
-        z += (double)((__builtin_amdgcn_exp2f(v.x - ms) + __builtin_amdgcn_exp2f(v.y - ms)) +
-                      (__builtin_amdgcn_exp2f(v.z - ms) + __builtin_amdgcn_exp2f(v.w - ms)));
-      }
-      z = group_sum_d(z, tpr);
-      auto count_ge = [&](float th) {
-        int c = 0;
-        if (mx >= th)
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            c += (int)(ev[i].x >= th) + (int)(ev[i].y >= th) + (int)(ev[i].z >= th) + (int)(ev[i].w >= th);
-        return c;
-      };
-      float th = -INFINITY;
-      int mine = 0, cnt = 0;
-      if (m != -INFINITY) {
-        th = m - kCapLadder[0];
-        mine = count_ge(th);
-        cnt = (int)group_sum((float)mine, tpr);
-        if (cnt > kCandT) {
-          // the loosest level that admits at most kCandT: counts only fall
-          // along the ladder, so bisect levels [1, kCapLevels); kCapLevels
-          // stands for none
-          int lo = 1, hi = kCapLevels;
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if ((int)group_sum((float)count_ge(m - kCapLadder[mid]), tpr) <= kCandT)
-              hi = mid;
-            else
-              lo = mid + 1;
-          }
-          if (lo < kCapLevels) {
-            th = m - kCapLadder[lo];
-            mine = count_ge(th);
-            cnt = (int)group_sum((float)mine, tpr);
-          } else {
-            th = next_up(m);
-            mine = 0;
-            cnt = 0;
-          }
+        for (int i = 0; i < kP1Chunks; ++i) {
+          const int ch = tid + nthr * i, row = ch / (DP / VPC), q = ch - row * (DP / VPC);
+          const int64_t gr = r0 + 64 + row;
+          p1x[i] = (ch < 64 * DP / VPC && gr < hi && VPC * q < d)
+                       ? *reinterpret_cast<const uint4*>(X + gr * d + VPC * q)
+                       : make_uint4(0u, 0u, 0u, 0u);
         }
       }
-      // this thread's first slot: exclusive prefix of the counts over the row's lanes
-      int incl = mine;
-      for (int o = 1; o < tpr; o <<= 1) {
-        const int t = __shfl_up(incl, o, tpr);
-        if (psub >= o) incl += t;
-      }
-      if (valid) {
-        const size_t rec = (size_t)slab * N + grow;
-        if (psub == 0) p1.h[rec] = make_float4((float)z, m, th, (float)cnt);
-        if (slab == 0 && psub == 0) {
-          const float sq = xq[2 * row], ab = xq[2 * row + 1];
-          p1.rowE[grow] = gam * (a_max * sq + fminf(b_max * ab, b2_max * sqrtf(sq))) + 2.f * kUnitRound * c_max;
-          p1.rowSq[grow] = sq;
-        }
-        if (mine) {
-          size_t slot = rec * kCandT + (size_t)(incl - mine);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float vv[4] = {ev[i].x, ev[i].y, ev[i].z, ev[i].w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (vv[u] >= th) {
-                p1.v[slot] = vv[u];
-                p1.k[slot] = (uint8_t)(4 * (psub + tpr * i) + u);
-                ++slot;
-              }
-          }
-        }
-      }
+      p1_rows(r0, 0);
+      __syncthreads();
+      score_store(sc, acc1, 0, ck, wave, lane, SCS);
+      __syncthreads();
+      p1_rows(r0 + 32, 32);
     } else {
       const int row = prow;
       const int64_t grow = r0 + row;
@@ -894,9 +971,9 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
 
     // 4. statistics, with the next X tile streaming into the other buffer
     const int64_t rn = r0 + 64;
-    if (async_x && rn < hi) async_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, reinterpret_cast<const float*>(X),
+    if (MODE != 2 && async_x && rn < hi) async_x_tile<XS>(xsb + (cur ^ 1) * 64 * XS, reinterpret_cast<const float*>(X),
                                              rn, hi, d, wave, waves, lane, rows);
-    if constexpr (kHalfPre)
+    if constexpr (kHalfPre && MODE != 2)
       if (hpref && rn < hi)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -1006,7 +1083,30 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         }
       }
     }
-    if constexpr (kHalfPre) {
+    if (MODE == 2) {
+      // one X buffer: the scores of this tile are done with it
+      if (rn < hi && p1pre) {
+        float* xn = xsb;
+        constexpr int VPC = sizeof(XT) == 4 ? 4 : 8;
+#pragma unroll
+        for (int i = 0; i < kP1Chunks; ++i) {
+          const int ch = tid + nthr * i, row = ch / (DP / VPC), q = ch - row * (DP / VPC);
+          if (ch < 64 * DP / VPC) {
+            if constexpr (sizeof(XT) == 4) {
+              *reinterpret_cast<uint4*>(xn + row * XS + 4 * q) = p1x[i];
+            } else {
+              const XT* hv = reinterpret_cast<const XT*>(&p1x[i]);
+              *reinterpret_cast<float4*>(xn + row * XS + 8 * q) =
+                  make_float4((float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]);
+              *reinterpret_cast<float4*>(xn + row * XS + 8 * q + 4) =
+                  make_float4((float)hv[4], (float)hv[5], (float)hv[6], (float)hv[7]);
+            }
+          }
+        }
+      } else if (rn < hi) {
+        load_x_tile<XS>(xsb, X, rn, hi, d, DP, tid, nthr, vec, rows);
+      }
+    } else if constexpr (kHalfPre) {
       if (rn < hi && hpref) {
         float* xn = xsb + (cur ^ 1) * 64 * XS;
 #pragma unroll
@@ -1031,7 +1131,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     // the compiler would otherwise drain every global load before each LDS
     // read of the score loop.
     __builtin_amdgcn_s_waitcnt(0);
-    cur ^= 1;
+    if (MODE != 2) cur ^= 1;
   }
 
   if constexpr (MODE == 2) return;
@@ -1095,23 +1195,19 @@ template <int DT, typename XT>
 __global__ void __launch_bounds__(64)
 lse_merge_kernel(const XT* __restrict__ X, int64_t N, int d, int kslabs, int KS,
                  const float4* __restrict__ p1h, const float* __restrict__ p1v, const uint8_t* __restrict__ p1k,
-                 const float* __restrict__ rowE, const float* __restrict__ muvar,
-                 const double* __restrict__ c64d, float4* __restrict__ rowref, double* __restrict__ lrow,
-                 int32_t* __restrict__ fblist, int32_t* __restrict__ fbcount) {
-  constexpr int DP = 32 * DT, FPL = DP / 8, kLevels = 8, kCap = 512, kHdr = 16;
+                 const float* __restrict__ rowE, const float* __restrict__ mup,
+                 const double* __restrict__ ivp, const double* __restrict__ c64d, float4* __restrict__ rowref,
+                 double* __restrict__ lrow, int32_t* __restrict__ fblist, int32_t* __restrict__ fbcount, int vec) {
+  constexpr int DP = 32 * DT, FPL = DP / 8, kLevels = 8, kCap = 512;
   static_assert(kCandT == 8, "a record's candidates are read as two float4");
   __shared__ uint32_t elist[kCap];  // (lane << 16) | component
   __shared__ float ev32[kCap];      // its fp32 score
   __shared__ double ex[kCap];       // its exact score
-  __shared__ float4 hs[kHdr][64];   // the block's slab headers (kslabs <= kHdr)
   const int lane = threadIdx.x;
   const int64_t n0 = (int64_t)blockIdx.x * 64, n = n0 + lane;
   const bool valid = n < N;
-  // slab sl's header of this lane's row: from LDS when the block staged them
-  const bool staged = kslabs <= kHdr;
-  if (staged)
-    for (int sl = 0; sl < kslabs; ++sl) hs[sl][lane] = valid ? p1h[(size_t)sl * N + n] : make_float4(0, 0, 0, 0);
-  auto hdr = [&](int sl) { return staged ? hs[sl][lane] : p1h[(size_t)sl * N + n]; };
+  // slab sl's header of this lane's row (read where needed: L2-resident)
+  auto hdr = [&](int sl) { return p1h[(size_t)sl * N + n]; };
   auto cands = [&](int sl, float (&v)[kCandT]) {
     const float4* q = reinterpret_cast<const float4*>(p1v + ((size_t)sl * N + n) * kCandT);
     const float4 a = q[0], b = q[1];
@@ -1246,25 +1342,52 @@ lse_merge_kernel(const XT* __restrict__ X, int64_t N, int d, int kslabs, int KS,
       const uint32_t ent = act ? elist[e] : 0u;
       const int er = (int)(ent >> 16), kg = (int)(ent & 0xffffu);
       const int64_t xr = (n0 + er) * (int64_t)d;
-      const float4* mvr = reinterpret_cast<const float4*>(muvar + ((size_t)kg * DP + sl8 * FPL) * 2);
-      // every load before the arithmetic; features past d carry var = +inf
+      const float4* mr = reinterpret_cast<const float4*>(mup + (size_t)kg * DP + sl8 * FPL);
+      const double2* ir = reinterpret_cast<const double2*>(ivp + (size_t)kg * DP + sl8 * FPL);
+      // every load before the arithmetic; features past d carry 1/var = 0.
+      // vec: rows of d % 4 == 0 values, 16-byte (fp32) or 8-byte (half)
+      // aligned, read four values per load.
       float xv[FPL];
-      float4 mv[FPL / 2];  // (mu, var) of two features
+      float4 mv[FPL / 4];
+      double2 iv[FPL / 2];
 #pragma unroll
-      for (int i = 0; i < FPL; ++i) {
-        const int f = sl8 * FPL + i;
-        xv[i] = act && f < d ? load_x(X, xr + f) : 0.f;
+      for (int j = 0; j < FPL / 4; ++j) {
+        const int f = sl8 * FPL + 4 * j;
+        if (vec) {
+          float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (f < d) {
+            if constexpr (sizeof(XT) == 4) {
+              q = *reinterpret_cast<const float4*>(X + xr + f);
+            } else {
+              const uint2 raw = *reinterpret_cast<const uint2*>(X + xr + f);
+              const XT* hv = reinterpret_cast<const XT*>(&raw);
+              q = make_float4((float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]);
+            }
+          }
+          xv[4 * j] = q.x;
+          xv[4 * j + 1] = q.y;
+          xv[4 * j + 2] = q.z;
+          xv[4 * j + 3] = q.w;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) xv[4 * j + u] = f + u < d ? load_x(X, xr + f + u) : 0.f;
+        }
       }
 #pragma unroll
-      for (int i = 0; i < FPL / 2; ++i) mv[i] = mvr[i];
+      for (int i = 0; i < FPL / 4; ++i) mv[i] = mr[i];
+#pragma unroll
+      for (int i = 0; i < FPL / 2; ++i) iv[i] = ir[i];
       const double cst = sl8 == 0 ? -2.0 * c64d[kg] : 0.0;
       __builtin_amdgcn_sched_barrier(0);
       double a0 = cst, a1 = 0.0;
 #pragma unroll
-      for (int i = 0; i < FPL; i += 2) {
-        const double t0 = (double)xv[i] - (double)mv[i / 2].x, t1 = (double)xv[i + 1] - (double)mv[i / 2].z;
-        a0 += t0 * t0 / (double)mv[i / 2].y;
-        a1 += t1 * t1 / (double)mv[i / 2].w;
+      for (int i = 0; i < FPL / 4; ++i) {
+        const double t0 = (double)xv[4 * i] - (double)mv[i].x, t1 = (double)xv[4 * i + 1] - (double)mv[i].y;
+        const double t2 = (double)xv[4 * i + 2] - (double)mv[i].z, t3 = (double)xv[4 * i + 3] - (double)mv[i].w;
+        a0 = fma(t0 * t0, iv[2 * i].x, a0);
+        a1 = fma(t1 * t1, iv[2 * i].y, a1);
+        a0 = fma(t2 * t2, iv[2 * i + 1].x, a0);
+        a1 = fma(t3 * t3, iv[2 * i + 1].y, a1);
       }
       double acc = a0 + a1;
       acc += dpp_d<kDppXor1>(acc);
@@ -2437,8 +2560,7 @@ hipError_t launch_precompute(const Plan& p, const float* mu, const float* var, c
   comp_consts_kernel<<<nblocks(p.Kp, 4), 256, 0, stream>>>(mu, var, logw, p.K, p.d, p.Kp, p.Kp16, w.c32,
                                                                w.c64e, w.c64d, w.compmax);
   pack_kernel<<<nblocks((int64_t)p.Kp * p.DP, 256), 256, 0, stream>>>(mu, var, p.K, p.d, p.Kp, p.Kp16, p.DP,
-                                                                        w.W32p, w.W64p, w.iv64, w.mup, w.ivp,
-                                                                        reinterpret_cast<float2*>(w.muvar));
+                                                                        w.W32p, w.W64p, w.iv64, w.mup, w.ivp);
   errc_kernel<<<1, 256, 0, stream>>>(w.compmax, p.K, w.errc);
   return hipGetLastError();
 }
@@ -2449,14 +2571,26 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
   const Workspace& w = p.ws;
   const int nthr = p.waves * 64;
   const int KS = p.waves * 32;
-  const size_t lds = (size_t)(2 * 64 * (32 * DT + 4) + 64 * (KS + 8) + 384) * sizeof(float) +
-                     (size_t)nthr * sizeof(double) + (size_t)(p.waves * kRefCap + 64) * sizeof(uint32_t);
+  // the first pass: one X tile, a 32-row score tile and |x|^2, |x|_1 per row
+  const size_t lds = MODE == 2 ? (size_t)(64 * (32 * DT + 4) + 32 * (KS + 8) + 128) * sizeof(float)
+                               : (size_t)(2 * 64 * (32 * DT + 4) + 64 * (KS + 8) + 384) * sizeof(float) +
+                                     (size_t)nthr * sizeof(double) +
+                                     (size_t)(p.waves * kRefCap + 64) * sizeof(uint32_t);
   auto fn = (p.stats_split && MODE != 2) ? estep_stats_kernel<DT, MODE, XT, true>
                                          : estep_stats_kernel<DT, MODE, XT, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)(p.P * p.kslabs);
+  // The first pass accumulates nothing per chunk, so its chunks are cut for
+  // one round of resident blocks (two per CU, 256 CUs), 8 * floor(64 /
+  // slabs) chunks: a multiple of 8, so that the kernel can keep all slabs of
+  // a chunk on one XCD (blocks are dealt to the 8 XCDs in turn).
+  int64_t chunks = p.P, rpc = p.rows_per_chunk;
+  if (MODE == 2) {
+    chunks = std::min<int64_t>(8 * std::max(1, 64 / p.kslabs), std::max<int64_t>(p.tiles, 1));
+    rpc = (p.tiles + chunks - 1) / chunks * 64;
+  }
+  const unsigned grid = (unsigned)(chunks * p.kslabs);
   // 1: fp32 rows of d % 4 == 0 floats, 2: half-precision rows of d % 8 == 0
   // values, both 16-byte aligned; 0 otherwise
   const bool al16 = reinterpret_cast<uintptr_t>(X) % 16 == 0;
@@ -2464,7 +2598,7 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
   const Pass1Out p1{w.p1h, w.p1v, w.p1k, w.rowE, w.rowSq};
   // the second pass walks the slabs' row lists, except when it also writes R
   const bool lists = MODE == 1 && p.pass1 && !R;
-  fn<<<grid, nthr, lds, stream>>>(X, p.N, p.d, p.K, p.Kp, p.waves, p.kslabs, p.rows_per_chunk,
+  fn<<<grid, nthr, lds, stream>>>(X, p.N, p.d, p.K, p.Kp, p.waves, p.kslabs, rpc,
                                   reinterpret_cast<const float4*>(w.W32p), w.c32, w.mup, w.ivp, w.c64d, w.errc,
                                   w.rowref, w.partials, w.llpart, ll_point, R, p1, p.drop_rho,
                                   lists ? w.slist : nullptr, lists ? w.slen : nullptr, vec);
@@ -2504,9 +2638,12 @@ static hipError_t run_normalisers(const Plan& p, const XT* X, const float* mu, f
   fill_int_kernel<<<1, 64, 0, stream>>>(w.fbcount, 1, 0);
   hipError_t e = run_stats<DT, 2>(p, X, mu, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
+  // the merge reads X rows four values at a time when d % 4 == 0 and the
+  // base is aligned for it (16 bytes for fp32, 8 for half precision)
+  const int mvec = p.d % 4 == 0 && reinterpret_cast<uintptr_t>(X) % (4 * sizeof(XT)) == 0 ? 1 : 0;
   lse_merge_kernel<DT, XT><<<(unsigned)p.tiles, 64, 0, stream>>>(
-      X, p.N, p.d, p.kslabs, 32 * p.waves, w.p1h, w.p1v, w.p1k, w.rowE, w.muvar, w.c64d, w.rowref, w.lrow,
-      w.fblist, w.fbcount);
+      X, p.N, p.d, p.kslabs, 32 * p.waves, w.p1h, w.p1v, w.p1k, w.rowE, w.mup, w.ivp, w.c64d, w.rowref, w.lrow,
+      w.fblist, w.fbcount, mvec);
   e = run_lse<DT, false>(p, X, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
   row_ll_sum_kernel<<<(unsigned)p.tiles, 64, 0, stream>>>(w.lrow, p.N, ll_point, w.llpart);
