@@ -152,6 +152,7 @@ static int make_plan_impl(int64_t N, int d, int K, int regime, void* base, Plan*
   const size_t nst = p.pass1 ? (size_t)p.kslabs * std::max<int64_t>(p.tiles, 1) : 0;
   const size_t o_smask = take(nst * sizeof(uint64_t));
   const size_t o_soff = take(nst * sizeof(int32_t));
+  const size_t o_sseg = take(p.pass1 ? (size_t)p.kslabs * kSlabSegs * sizeof(int32_t) : 0);
   const size_t o_slen = take(p.pass1 ? (size_t)p.kslabs * sizeof(int32_t) : 0);
   const size_t o_part = take((size_t)std::max<int64_t>(p.P, 1) * p.Kp * p.E * sizeof(float));
   const size_t o_ll = take((size_t)std::max<int64_t>(std::max(p.P, p.tiles), 1) * sizeof(double));
@@ -188,6 +189,7 @@ static int make_plan_impl(int64_t N, int d, int K, int regime, void* base, Plan*
     p.ws.slist = p.pass1 ? reinterpret_cast<int32_t*>(b + o_slist) : nullptr;
     p.ws.smask = p.pass1 ? reinterpret_cast<uint64_t*>(b + o_smask) : nullptr;
     p.ws.soff = p.pass1 ? reinterpret_cast<int32_t*>(b + o_soff) : nullptr;
+    p.ws.sseg = p.pass1 ? reinterpret_cast<int32_t*>(b + o_sseg) : nullptr;
     p.ws.slen = p.pass1 ? reinterpret_cast<int32_t*>(b + o_slen) : nullptr;
     p.ws.partials = reinterpret_cast<float*>(b + o_part);
     p.ws.llpart = reinterpret_cast<double*>(b + o_ll);

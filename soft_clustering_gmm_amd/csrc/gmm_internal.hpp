@@ -20,6 +20,8 @@ constexpr int kLseWaves = 4;         // waves per block in the fp64 normaliser p
 constexpr int kSmallWaves = 4;       // waves per block in the small-K kernel
 constexpr int64_t kMaxChunkRows = 32768;  // rows per statistics partial, at most
 constexpr int kCandT = 8;            // candidates kept per (row, slab) by the fp32 first pass
+constexpr int kSlabSegs = 256;       // tile segments per slab in the build of the second pass's row lists
+constexpr int kLlRows = 1024;        // rows per log-likelihood partial in the two-pass regime
 
 // Device pointers into the caller's workspace, filled by gmm::plan().
 struct Workspace {
@@ -46,7 +48,8 @@ struct Workspace {
   float* rowSq;     // [N] |x|^2 of each row (fp32, from the first pass)
   int32_t* slist;   // [kslabs][N] per slab, in increasing order, the rows it keeps
   uint64_t* smask;  // [kslabs][tiles] per 64-row tile, the kept rows as a bit mask
-  int32_t* soff;    // [kslabs][tiles] kept rows per tile, then their exclusive prefix
+  int32_t* soff;    // [kslabs][tiles] kept rows per tile
+  int32_t* sseg;    // [kslabs][kSlabSegs] kept rows per tile segment, then their exclusive prefix
   int32_t* slen;    // [kslabs] length of each slab's list
   float* partials;  // [P][Kp][E] per-chunk statistics
   double* llpart;   // [max(P, tiles)] per-block log-likelihood sums

@@ -1408,21 +1408,29 @@ lse_merge_kernel(const XT* __restrict__ X, int64_t N, int d, int kslabs, int KS,
   if (valid && fallback) fblist[atomicAdd(fbcount, 1)] = (int32_t)n;
 }
 
-// Per 64-row tile: l_n (natural) to ll_point (nullable) and the tile's sum,
-// in row order, to llpart.
-__global__ void __launch_bounds__(64) row_ll_sum_kernel(const double* __restrict__ lrow, int64_t N,
-                                                        float* __restrict__ ll_point, double* __restrict__ llpart) {
-  __shared__ double s[64];
-  const int64_t n = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  const double l = n < N ? lrow[n] : 0.0;
-  if (ll_point && n < N) ll_point[n] = (float)l;
-  s[threadIdx.x] = l;
+// Per kLlRows rows, 256 threads of four consecutive rows each: l_n (natural)
+// to ll_point (nullable) and the block's sum, in a fixed order (each thread's
+// rows in turn, then a pairwise tree over the threads), to llpart.
+__global__ void __launch_bounds__(256) row_ll_sum_kernel(const double* __restrict__ lrow, int64_t N,
+                                                         float* __restrict__ ll_point, double* __restrict__ llpart) {
+  static_assert(kLlRows == 4 * 256, "four rows per thread");
+  __shared__ double s[256];
+  const int64_t r = (int64_t)blockIdx.x * kLlRows + 4 * threadIdx.x;
+  double a = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (r + i < N) {
+      const double l = lrow[r + i];
+      if (ll_point) ll_point[r + i] = (float)l;
+      a += l;
+    }
+  s[threadIdx.x] = a;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double a = 0.0;
-    for (int i = 0; i < 64; ++i) a += s[i];
-    llpart[blockIdx.x] = a;
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
+    __syncthreads();
   }
+  if (threadIdx.x == 0) llpart[blockIdx.x] = s[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -1465,44 +1473,61 @@ __global__ void __launch_bounds__(64) slab_keep_kernel(const float4* __restrict_
   }
 }
 
-// One block of 256 per slab: the tile counts become their exclusive prefix
-// (in place), the total the slab's list length.
-__global__ void __launch_bounds__(256) slab_scan_kernel(int32_t* __restrict__ soff, int64_t tiles,
-                                                        int32_t* __restrict__ slen) {
+// Per (segment, slab), one block of 256: the kept rows of the segment's
+// tiles (kSlabSegs segments of equal tile count per slab, the last ones
+// possibly empty), read with consecutive threads on consecutive tiles.
+__global__ void __launch_bounds__(256) slab_seg_kernel(const int32_t* __restrict__ scnt, int64_t tiles,
+                                                       int32_t* __restrict__ sseg) {
   __shared__ int32_t part[256];
-  int32_t* c = soff + (size_t)blockIdx.x * tiles;
-  const int64_t per = (tiles + 255) / 256;
-  const int64_t lo = min(tiles, threadIdx.x * per), hi = min(tiles, lo + per);
+  const int slab = blockIdx.y, g = blockIdx.x;
+  const int64_t per = (tiles + kSlabSegs - 1) / kSlabSegs;
+  const int64_t lo = min(tiles, g * per), hi = min(tiles, lo + per);
+  const int32_t* c = scnt + (size_t)slab * tiles;
   int32_t a = 0;
-  for (int64_t i = lo; i < hi; ++i) a += c[i];
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 256) a += c[i];
   part[threadIdx.x] = a;
   __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {  // inclusive scan of the 256 segment sums
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sseg[(size_t)slab * kSlabSegs + g] = part[0];
+}
+
+// One block of kSlabSegs per slab: the segment counts become their exclusive
+// prefix (in place), the total the slab's list length.
+__global__ void __launch_bounds__(kSlabSegs) slab_scan_kernel(int32_t* __restrict__ sseg, int32_t* __restrict__ slen) {
+  __shared__ int32_t part[kSlabSegs];
+  int32_t* c = sseg + (size_t)blockIdx.x * kSlabSegs;
+  const int32_t a = c[threadIdx.x];
+  part[threadIdx.x] = a;
+  __syncthreads();
+  for (int o = 1; o < kSlabSegs; o <<= 1) {  // inclusive scan
     const int32_t v = (int)threadIdx.x >= o ? part[threadIdx.x - o] : 0;
     __syncthreads();
     part[threadIdx.x] += v;
     __syncthreads();
   }
-  int32_t run = part[threadIdx.x] - a;
-  for (int64_t i = lo; i < hi; ++i) {
-    const int32_t v = c[i];
-    c[i] = run;
-    run += v;
-  }
-  if (threadIdx.x == 255) slen[blockIdx.x] = part[255];
+  c[threadIdx.x] = part[threadIdx.x] - a;
+  if (threadIdx.x == kSlabSegs - 1) slen[blockIdx.x] = part[kSlabSegs - 1];
 }
 
-// Per (64-row tile, slab): the kept rows to their places in the slab's list.
+// Per (segment, slab), one wave: the segment's tiles in order, each kept row
+// to its place in the slab's list (its tile's base plus its rank among the
+// tile's kept rows).
 __global__ void __launch_bounds__(64) slab_scatter_kernel(const uint64_t* __restrict__ smask,
-                                                          const int32_t* __restrict__ soff, int64_t N,
+                                                          const int32_t* __restrict__ sseg, int64_t N,
                                                           int64_t tiles, int32_t* __restrict__ slist) {
-  const int slab = blockIdx.y;
-  const int64_t t = blockIdx.x;
-  const uint64_t m = smask[(size_t)slab * tiles + t];
-  const int lane = threadIdx.x;
-  if ((m >> lane) & 1u) {
-    const int rank = __builtin_popcountll(m & ((1ull << lane) - 1ull));
-    slist[(size_t)slab * N + soff[(size_t)slab * tiles + t] + rank] = (int32_t)(t * 64 + lane);
+  const int slab = blockIdx.y, g = blockIdx.x, lane = threadIdx.x;
+  const int64_t per = (tiles + kSlabSegs - 1) / kSlabSegs;
+  const int64_t lo = min(tiles, g * per), hi = min(tiles, lo + per);
+  int32_t* out = slist + (size_t)slab * N;
+  int32_t off = sseg[(size_t)slab * kSlabSegs + g];
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int64_t t = lo; t < hi; ++t) {
+    const uint64_t m = smask[(size_t)slab * tiles + t];
+    if ((m >> lane) & 1u) out[off + __builtin_popcountll(m & below)] = (int32_t)(t * 64 + lane);
+    off += __builtin_popcountll(m);
   }
 }
 
@@ -2554,6 +2579,12 @@ __global__ void mstep_kernel(const float* __restrict__ Nk, const float* __restri
 
 static inline unsigned nblocks(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
 
+// Log-likelihood partials of an E-step: one per row chunk, or per kLlRows
+// rows in the two-pass regime.
+static inline int64_t ll_parts(const Plan& p) {
+  return p.regime == 2 ? (p.N + kLlRows - 1) / kLlRows : p.P;
+}
+
 hipError_t launch_precompute(const Plan& p, const float* mu, const float* var, const float* logw,
                              hipStream_t stream) {
   const Workspace& w = p.ws;
@@ -2646,12 +2677,13 @@ static hipError_t run_normalisers(const Plan& p, const XT* X, const float* mu, f
       w.fblist, w.fbcount, mvec);
   e = run_lse<DT, false>(p, X, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
-  row_ll_sum_kernel<<<(unsigned)p.tiles, 64, 0, stream>>>(w.lrow, p.N, ll_point, w.llpart);
+  row_ll_sum_kernel<<<(unsigned)ll_parts(p), 256, 0, stream>>>(w.lrow, p.N, ll_point, w.llpart);
   // the second pass's row lists
-  const dim3 tg((unsigned)p.tiles, (unsigned)p.kslabs);
+  const dim3 tg((unsigned)p.tiles, (unsigned)p.kslabs), sg((unsigned)kSlabSegs, (unsigned)p.kslabs);
   slab_keep_kernel<<<tg, 64, 0, stream>>>(w.p1h, w.rowref, w.rowSq, p.N, p.tiles, p.drop_rho, w.smask, w.soff);
-  slab_scan_kernel<<<(unsigned)p.kslabs, 256, 0, stream>>>(w.soff, p.tiles, w.slen);
-  slab_scatter_kernel<<<tg, 64, 0, stream>>>(w.smask, w.soff, p.N, p.tiles, w.slist);
+  slab_seg_kernel<<<sg, 256, 0, stream>>>(w.soff, p.tiles, w.sseg);
+  slab_scan_kernel<<<(unsigned)p.kslabs, kSlabSegs, 0, stream>>>(w.sseg, w.slen);
+  slab_scatter_kernel<<<sg, 64, 0, stream>>>(w.smask, w.sseg, p.N, p.tiles, w.slist);
   return hipGetLastError();
 }
 
@@ -2737,7 +2769,7 @@ hipError_t launch_estep(const Plan& p, const void* X, int x_dtype, const float* 
     }
   }
   if (loglik_total) {
-    const int64_t nll = p.regime == 2 ? p.tiles : p.P;
+    const int64_t nll = ll_parts(p);
     reduce_ll_kernel<false><<<1, 256, 0, stream>>>(w.llpart, nll, loglik_total, 0);
   }
   return hipGetLastError();
@@ -2751,7 +2783,7 @@ hipError_t launch_estep_accum(const Plan& p, const void* X, int x_dtype, const f
   const Workspace& w = p.ws;
   const int64_t n = (int64_t)p.K * (1 + 2 * p.d);
   accum_stats_kernel<<<nblocks(n, 256), 256, 0, stream>>>(w.partials, p.P, p.Kp, p.E, p.DP, p.K, p.d, acc, first);
-  const int64_t nll = p.regime == 2 ? p.tiles : p.P;
+  const int64_t nll = ll_parts(p);
   reduce_ll_kernel<true><<<1, 256, 0, stream>>>(w.llpart, nll, acc + n, first);
   return hipGetLastError();
 }
