@@ -336,9 +336,10 @@ __global__ void errc_kernel(const float* __restrict__ compmax, int K, float* __r
 // 64 rows of the LDS tile `xs` and the wave's 32 components (operands W from
 // the buffer resource `wrs`), on two 32x32x2 fp32 MFMA accumulators (rows
 // 0-31 in acc0, 32-63 in acc1; score_store adds c_k and writes them to the
-// wave's 32 columns of an LDS score tile); wave 0 also writes |x|^2 and |x|_1
-// of each row to `xq` (inputs of the error bound).
-template <int DT>
+// wave's 32 columns of an LDS score tile); with NORMS wave 0 also writes
+// |x|^2 and |x|_1 of each row to `xq` (inputs of the error bound), from the
+// squares the MFMAs consume.
+template <int DT, bool NORMS>
 __device__ __forceinline__ void score_acc(const float* xs, float* xq, __amdgpu_buffer_rsrc_t wrs, int wave,
                                           int lane, v16f& acc0, v16f& acc1) {
   constexpr int DP = 32 * DT, Q = DP / 4, XS = DP + 4;
@@ -370,10 +371,12 @@ __device__ __forceinline__ void score_acc(const float* xs, float* xq, __amdgpu_b
     acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x1.x, w[2], acc1, 0, 0, 0);
     acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x0.y, w[3], acc0, 0, 0, 0);
     acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x1.y, w[3], acc1, 0, 0, 0);
-    sq0 += s00 + s01;  // rows c and c + 32
-    sq1 += s10 + s11;
-    ab0 += fabsf(x0.x) + fabsf(x0.y);
-    ab1 += fabsf(x1.x) + fabsf(x1.y);
+    if constexpr (NORMS) {
+      sq0 += s00 + s01;  // rows c and c + 32
+      sq1 += s10 + s11;
+      ab0 += fabsf(x0.x) + fabsf(x0.y);
+      ab1 += fabsf(x1.x) + fabsf(x1.y);
+    }
   };
   // The X operands of the next step are read from LDS before this step's
   // MFMAs issue; the scheduling barriers keep every load where it is.
@@ -402,7 +405,7 @@ __device__ __forceinline__ void score_acc(const float* xs, float* xq, __amdgpu_b
     __builtin_amdgcn_sched_barrier(0);
     step(pb0, pb1, wd);
   }
-  if (wave == 0) {
+  if (NORMS && wave == 0) {
     // the two halves of the wave hold the two halves of each row's features
     sq0 += __shfl_xor(sq0, 32, 64);
     sq1 += __shfl_xor(sq1, 32, 64);
@@ -435,14 +438,33 @@ __device__ __forceinline__ void score_store(float* sc, const v16f& acc, int row0
 }
 
 // Scores of a 64-row X tile against the wave's 32 components into the LDS
-// score tile [64][SCS] (see score_acc), |x|^2 and |x|_1 of the rows into xq.
-template <int DT>
+// score tile [64][SCS] (see score_acc), with NORMS |x|^2 and |x|_1 of the
+// rows into xq.
+template <int DT, bool NORMS>
 __device__ __forceinline__ void score_tile(const float* xs, float* sc, float* xq, __amdgpu_buffer_rsrc_t wrs,
                                            float ck, int wave, int lane, int SCS) {
   v16f acc0, acc1;
-  score_acc<DT>(xs, xq, wrs, wave, lane, acc0, acc1);
+  score_acc<DT, NORMS>(xs, xq, wrs, wave, lane, acc0, acc1);
   score_store(sc, acc0, 0, ck, wave, lane, SCS);
   score_store(sc, acc1, 32, ck, wave, lane, SCS);
+}
+
+// |x|^2 and |x|_1 of row `row` of an LDS X tile (row stride XS, features past
+// d not read), summed by the g consecutive lanes of the row's group: lane
+// `sub` takes the 16-byte chunks sub, sub + g, ...; every lane of the group
+// ends with both sums. (A chunk that straddles d is read whole: the element
+// loads of such rows leave zeros past d.)
+template <int DP, int XS>
+__device__ __forceinline__ void row_norms(const float* xs, int row, int sub, int g, int d, float& sq, float& ab) {
+  sq = 0.f;
+  ab = 0.f;
+  for (int q = sub; q < DP / 4 && 4 * q < d; q += g) {
+    const float4 v = *reinterpret_cast<const float4*>(xs + row * XS + 4 * q);
+    sq += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+    ab += (fabsf(v.x) + fabsf(v.y)) + (fabsf(v.z) + fabsf(v.w));
+  }
+  sq = group_sum(sq, g);
+  ab = group_sum(ab, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -510,8 +532,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   float* xsb = smem;               // [kXT][64][XS]: current (and next) X tile
   float* sc = xsb + kXT * 64 * XS; // [kSR][SCS]
   float* rv = sc + kSR * SCS;      // [64][4] per-row references (m, lZ or 1/z, theta)
-  float* xq = rv + (MODE == 2 ? 0 : 256);  // [64][2] |x|^2 and |x|_1 of the tile's rows
-  double* lls = reinterpret_cast<double*>(xq + 128);  // [nthr]
+  double* lls = reinterpret_cast<double*>(rv + (MODE == 2 ? 0 : 256));  // [nthr]
   uint32_t* reflist = reinterpret_cast<uint32_t*>(lls + nthr);  // [waves][kRefCap]
   uint32_t* nzrow = reflist + waves * kRefCap;  // [64]: bit w = row has a nonzero r for wave w
 
@@ -586,8 +607,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   const bool p1pre = MODE == 2 && DT <= 3 && vec != 0 && nthr * kP1Chunks * (sizeof(XT) == 4 ? 4 : 8) >= 64 * DP;
   uint4 p1x[kP1Chunks];
   if (lo < hi) load_x_tile<XS>(xsb, X, lo, hi, d, DP, tid, nthr, vec, rows);
-  // First-pass row phase over 32 rows of the tile (rows rb .. rb + 31, their
-  // |x|^2 and |x|_1 at xq rows xrow0 ..): T2 = 2 * waves threads per row, four
+  // First-pass row phase over 32 rows of the tile (rows rb .. rb + 31, rows
+  // xrow0 .. of the X tile): T2 = 2 * waves threads per row, four
   // 16-byte chunks of the 32 * waves-entry score row each (entries
   // 4 (psub + T2 i) + u).
   auto p1_rows = [&](int64_t rb, int xrow0) {
@@ -603,6 +624,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     const int row = tid / T2, psub = tid - row * T2;
     const int64_t grow = rb + row;
     const bool valid = grow < hi;
+    float sq = 0.f, ab = 0.f;  // |x|^2, |x|_1 (slab 0 records the row's bound)
+    if (slab == 0) row_norms<DP, XS>(xsb, xrow0 + row, psub, T2, d, sq, ab);
     const float4* srow4 = reinterpret_cast<const float4*>(sc + row * SCS);
     float4 ev[NC];
 #pragma unroll
@@ -668,7 +691,6 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       const size_t rec = (size_t)slab * N + grow;
       if (psub == 0) p1.h[rec] = make_float4((float)z, m, th, (float)cnt);
       if (slab == 0 && psub == 0) {
-        const float sq = xq[2 * (xrow0 + row)], ab = xq[2 * (xrow0 + row) + 1];
         p1.rowE[grow] = gam * (a_max * sq + fminf(b_max * ab, b2_max * sqrtf(sq))) + 2.f * kUnitRound * c_max;
         p1.rowSq[grow] = sq;
       }
@@ -704,10 +726,10 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     v16f acc1;
     if constexpr (MODE == 2) {
       v16f acc0;
-      score_acc<DT>(xs, xq, wrs, wave, lane, acc0, acc1);
+      score_acc<DT, false>(xs, nullptr, wrs, wave, lane, acc0, acc1);
       score_store(sc, acc0, 0, ck, wave, lane, SCS);
     } else {
-      score_tile<DT>(xs, sc, xq, wrs, ck, wave, lane, SCS);
+      score_tile<DT, false>(xs, sc, nullptr, wrs, ck, wave, lane, SCS);
     }
     __syncthreads();
 
@@ -739,7 +761,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       const int64_t grow = r0 + row;
       const bool valid = grow < hi;
       float* srow = sc + row * SCS;
-      const float sq = xq[2 * row], ab = xq[2 * row + 1];  // from the score loop
+      float sq, ab;
+      row_norms<DP, XS>(xs, row, psub, tpr, d, sq, ab);
       const float Ebound = gam * (a_max * sq + fminf(b_max * ab, b2_max * sqrtf(sq))) + 2.f * kUnitRound * c_max;
 
       // Each thread owns the 16-byte chunks psub + tpr*i (i < 8) of its row,
@@ -1608,7 +1631,7 @@ kmeans_assign_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int wave
       const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float4*>(W32p) + (size_t)(__builtin_amdgcn_readfirstlane(kw) >> 5) * Q * 64, (short)0,
           Q * 64 * 16, kBufferRsrcWord3);
-      score_tile<DT>(xs, sc, xq, wrs, c32[kw + c], wave, lane, SCS);
+      score_tile<DT, true>(xs, sc, xq, wrs, c32[kw + c], wave, lane, SCS);
       __syncthreads();
       if (slab == 0 && pref && rn < hi) {
         const float* Xf = reinterpret_cast<const float*>(X);
@@ -2602,9 +2625,9 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
   const Workspace& w = p.ws;
   const int nthr = p.waves * 64;
   const int KS = p.waves * 32;
-  // the first pass: one X tile, a 32-row score tile and |x|^2, |x|_1 per row
-  const size_t lds = MODE == 2 ? (size_t)(64 * (32 * DT + 4) + 32 * (KS + 8) + 128) * sizeof(float)
-                               : (size_t)(2 * 64 * (32 * DT + 4) + 64 * (KS + 8) + 384) * sizeof(float) +
+  // the first pass: one X tile and a 32-row score tile
+  const size_t lds = MODE == 2 ? (size_t)(64 * (32 * DT + 4) + 32 * (KS + 8)) * sizeof(float)
+                               : (size_t)(2 * 64 * (32 * DT + 4) + 64 * (KS + 8) + 256) * sizeof(float) +
                                      (size_t)nthr * sizeof(double) +
                                      (size_t)(p.waves * kRefCap + 64) * sizeof(uint32_t);
   auto fn = (p.stats_split && MODE != 2) ? estep_stats_kernel<DT, MODE, XT, true>
