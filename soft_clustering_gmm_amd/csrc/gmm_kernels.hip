@@ -511,19 +511,12 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
   const int nthr = blockDim.x;
   const int KS = waves * 32, SCS = KS + 8;
-  // (chunk, slab) of this block. The first pass's grid is a multiple of
-  // 8 * kslabs: block b runs on XCD b % 8, and the slabs of a chunk are given
-  // to blocks of one XCD, which then read the chunk's X tiles from one L2.
-  int64_t chunk;
-  int slab;
-  if (MODE == 2 && gridDim.x % (8u * (unsigned)kslabs) == 0) {
-    const int j = (int)(blockIdx.x >> 3);
-    chunk = (int64_t)(blockIdx.x & 7) + 8 * (int64_t)(j / kslabs);
-    slab = j % kslabs;
-  } else {
-    chunk = blockIdx.x / kslabs;
-    slab = blockIdx.x - (int)(chunk * kslabs);
-  }
+  // (chunk, slab) of this block, slab fastest. Blocks are dealt to the 8 XCDs
+  // in turn, so with a slab count that is a multiple of 8 (or divides 8) each
+  // XCD serves a fixed subset of the slabs: the score operands its waves
+  // re-read every tile (256 KB per slab at d = 128) then stay in its L2.
+  const int64_t chunk = blockIdx.x / kslabs;
+  const int slab = blockIdx.x - (int)(chunk * kslabs);
   const int k0 = slab * KS;
   const int kw = k0 + wave * 32;
   // The first pass has no rv, lls, reflist or nzrow, one X tile and a score
@@ -2636,9 +2629,8 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   // The first pass accumulates nothing per chunk, so its chunks are cut for
-  // one round of resident blocks (two per CU, 256 CUs), 8 * floor(64 /
-  // slabs) chunks: a multiple of 8, so that the kernel can keep all slabs of
-  // a chunk on one XCD (blocks are dealt to the 8 XCDs in turn).
+  // one round of resident blocks (two per CU, 256 CUs): 8 * floor(64 /
+  // slabs) chunks.
   int64_t chunks = p.P, rpc = p.rows_per_chunk;
   if (MODE == 2) {
     chunks = std::min<int64_t>(8 * std::max(1, 64 / p.kslabs), std::max<int64_t>(p.tiles, 1));
