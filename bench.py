@@ -394,7 +394,8 @@ def main(argv=None):
     sp = str(args.stats_precision == "split-bf16").lower()
     kernel = (f"estep_small_kernel<{-(-d // 16)},{ctype},{sp}> (small K)" if small
               else f"estep_stats_kernel<{-(-d // 32)},0,{ctype},{sp}> (single sweep)" if single
-              else f"estep_lse_kernel + estep_stats_kernel<{-(-d // 32)},1,{ctype},{sp}> (two-pass)")
+              else f"estep_stats_kernel<{-(-d // 32)},2,{ctype},false> + lse_merge_kernel + estep_lse_kernel "
+                   f"(fallback rows) + estep_stats_kernel<{-(-d // 32)},1,{ctype},{sp}> (two-pass)")
     ctr = committed_counters(args.workload, args.stats_precision)
     executed = ctr.get("executed_flops_per_launch")
     roof = {
@@ -409,10 +410,13 @@ def main(argv=None):
         "hbm_algorithmic_bytes_per_launch": xbytes,
         "hbm_achieved_GBps": round(xbytes / (k_avg * 1e-3) / 1e9, 1),
         "hbm_frac": round(xbytes / (k_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-        "credit": ("dense 8NKd flops; the fp32 statistics loop skips points whose responsibilities for a "
-                   "wave's 32 components are all exactly zero (exact, data-dependent), so executed "
-                   "matrix-core work can be below the credited flops" if not small and sp == "false"
-                   else "dense 8NKd flops, all executed"),
+        "credit": "dense 8NKd flops (4NKd scores + 4NKd statistics)"
+                  + ("; the fp32 statistics loop leaves out points whose responsibilities for a wave's 32 "
+                     "components are all at most 2^-20/N/max(1,|x|^2) (at most ~1e-6 of any statistic, "
+                     "data-dependent)" if not small and sp == "false" else ", all statistics executed")
+                  + ("; the first pass scores every pair once more (4NKd, not credited)" if regime == "two-pass"
+                     else "")
+                  + "; executed_flops_per_launch counts what the matrix cores ran",
     }
     out = {
         "metric": METRIC, "value": N * K / (ms_step * 1e-3), "unit": UNIT, "n_gpus": 1,
