@@ -62,7 +62,9 @@ enum gmm_dtype { GMM_F32 = 0, GMM_F16 = 1, GMM_BF16 = 2 };
  *             scores in fp32 on the matrix cores and keeps a few candidates
  *             per row and 256-component slab; a merge re-scores exactly
  *             (fp64) the entries a row's normaliser depends on, and the rare
- *             rows it cannot settle get an fp64 normaliser pass
+ *             rows it cannot settle get an fp64 normaliser pass; the second
+ *             pass then scores, per slab, only the rows that hold a
+ *             responsibility above the statistics threshold there
  *   SMALLK  - single sweep with 16-component tiles, K <= 16 and d <= 64
  * AUTO takes SMALLK when it applies, else SINGLE for K <= 256, else TWOPASS. */
 enum gmm_regime { GMM_REGIME_AUTO = 0, GMM_REGIME_SINGLE = 1, GMM_REGIME_TWOPASS = 2, GMM_REGIME_SMALLK = 3 };
@@ -82,8 +84,9 @@ const char* gmm_error_string(int code);
  * Returns 0 for arguments outside the limits. */
 size_t gmm_workspace_bytes(int64_t N, int32_t d, int32_t K);
 /* (In the two-pass regime the first pass also keeps 56 bytes per row and
- * 256-component slab, so the workspace grows as N K / 256 there: about
- * 3.8 GB at N = 4,194,304, K = 4096.) */
+ * 256-component slab, and the second pass's per-slab row lists 4 more, so the
+ * workspace grows as N K / 256 there: about 4.8 GB in all at N = 4,194,304,
+ * d = 128, K = 4096.) */
 
 /* E-step with sufficient statistics (Turbo-GMM abstract: responsibility
  * normalisation and sufficient-statistic accumulation; Flash-GMM abstract:

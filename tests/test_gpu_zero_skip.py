@@ -151,3 +151,46 @@ def test_normaliser_fallback_on_tied_slab_maximum(G):
     parity.check_total(host(L), ref, what)
     tie = host(R)[:, 10:22]
     assert np.all(tie == tie[:, :1]), "exact copies must get bitwise equal responsibilities"
+
+
+def test_two_pass_row_lists_empty_and_sparse_slabs(G):
+    """K = 1024 (four 256-component slabs) for the second pass's per-slab row
+    lists: slab 0 near blob A (19963 rows), slab 1 far from all data (its
+    list is empty, so every second-pass block of that slab has no rows),
+    slab 2 near blob B (37 rows: one ragged chunk, the other blocks of the
+    slab empty), slab 3 split between both blobs (every row). Against the
+    oracle at the usual bars; l_n bitwise equal to the launch that also
+    writes R (which walks every row of every slab)."""
+    rng = np.random.default_rng(31)
+    N, d, K, nb = 20_000, 16, 1024, 37
+    ca, cb = np.zeros(d), 30.0 * np.eye(d)[0]
+    mu = np.empty((K, d))
+    mu[0:256] = ca + rng.normal(0.0, 1.5, (256, d))
+    mu[256:512] = 200.0 * np.eye(d)[1] + rng.normal(0.0, 1.5, (256, d))
+    mu[512:768] = cb + rng.normal(0.0, 1.5, (256, d))
+    mu[768:896] = ca + rng.normal(0.0, 1.5, (128, d))
+    mu[896:1024] = cb + rng.normal(0.0, 1.5, (128, d))
+    lab = np.zeros(N, np.int64)
+    lab[rng.choice(N, nb, replace=False)] = 1
+    X = (np.where(lab[:, None] == 1, cb, ca) + rng.normal(0.0, 1.0, (N, d))).astype(np.float32)
+    mu = mu.astype(np.float32)
+    var = rng.uniform(0.8, 1.2, (K, d)).astype(np.float32)
+    logw = np.full(K, -np.log(K), np.float32)
+    ref = oracle.estep(X, mu, var, logw, keep_R=True)
+    # the premise, with the statistics skip threshold 2^-20 / N / max(1, |x|^2)
+    thr = 2.0 ** -20 / N / np.maximum(1.0, (X.astype(np.float64) ** 2).sum(1))
+    kept = (ref["R"].reshape(N, 4, 256).max(axis=2) > thr[:, None]).sum(axis=0)
+    assert kept[1] == 0 and kept[2] == nb and kept[0] == N - nb and kept[3] == N, kept
+    args = (dev(X), dev(mu), dev(var), dev(logw))
+    Nk, Sx, Sxx, L, lp = G.estep_stats(*args, regime=2, want_point_loglik=True)
+    R, lr = G.estep_resp(*args, regime=2)
+    torch.cuda.synchronize()
+    X64 = X.astype(np.float64)
+    what = "row lists: empty and 37-row slabs"
+    parity.check_loglik_point(host(lp), ref["l"], what)
+    parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, X64, ref["R"].T @ np.abs(X64), what)
+    parity.check_total(host(L), ref, what)
+    assert np.array_equal(host(lp), host(lr)), f"{what}: l_n differs from the R-writing launch"
+    assert np.all(host(Nk)[256:512] == 0.0) and np.all(host(Sx)[256:512] == 0.0)
+    print(f"{what}: kept rows per slab {kept.tolist()}, Nk of slab 2 {host(Nk)[512:768].sum():.6f} "
+          f"(oracle {ref['Nk'][512:768].sum():.6f})", flush=True)
