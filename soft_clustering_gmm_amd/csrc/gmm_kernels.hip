@@ -193,7 +193,8 @@ __device__ __forceinline__ void async_x_tile(float* xn, const float* X, int64_t 
 }
 
 // Rows [r0, r0 + 64) of X -> LDS tile [64][XS], zero padded to DP features
-// and past `hi`. `vec`: X rows are 16-byte aligned float rows (d % 4 == 0).
+// and past `hi`. `vec`: 1 = 16-byte aligned float rows (d % 4 == 0), 2 =
+// 16-byte aligned half-precision rows (d % 8 == 0).
 // With `rows`, positions name listed rows as in async_x_tile.
 template <int XS, typename XT>
 __device__ __forceinline__ void load_x_tile(float* xs, const XT* X, int64_t r0, int64_t hi, int d, int DP,
@@ -207,6 +208,21 @@ __device__ __forceinline__ void load_x_tile(float* xs, const XT* X, int64_t r0, 
       *reinterpret_cast<float4*>(xs + row * XS + 4 * q) =
           (pos < hi && 4 * q < d) ? *reinterpret_cast<const float4*>(Xf + gr * d + 4 * q)
                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  } else if (vec == 2 && sizeof(XT) == 2) {
+    // half-precision rows of d % 8 == 0 values, 16-byte aligned: eight values
+    // per load, widened into two float4
+    for (int ch = tid; ch < 8 * DP; ch += nthr) {
+      const int row = ch / (DP / 8), q = ch - row * (DP / 8);
+      const int64_t pos = r0 + row;
+      const int64_t gr = pos < hi && rows ? (int64_t)rows[pos] : pos;
+      const uint4 raw = (pos < hi && 8 * q < d) ? *reinterpret_cast<const uint4*>(X + gr * d + 8 * q)
+                                                 : make_uint4(0u, 0u, 0u, 0u);
+      const XT* hv = reinterpret_cast<const XT*>(&raw);
+      *reinterpret_cast<float4*>(xs + row * XS + 8 * q) =
+          make_float4((float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]);
+      *reinterpret_cast<float4*>(xs + row * XS + 8 * q + 4) =
+          make_float4((float)hv[4], (float)hv[5], (float)hv[6], (float)hv[7]);
     }
   } else {
     for (int e = tid; e < 64 * DP; e += nthr) {
