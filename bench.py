@@ -6,8 +6,8 @@ partial reduction and the M-step, on the "ref" blob workload
 (N=1,048,576 points, d=128, K=256 diagonal components, fp32) with X resident
 in HBM. Every step (warm-up and timed) starts from the same initial
 parameters (K data points as means, unit variances, equal weights), restored
-by three small device copies inside the step, so that all steps do identical
-work. `value` = N*K / (wall-clock seconds per step).
+by one device copy of the flat parameter buffer inside the step, so that all
+steps do identical work. `value` = N*K / (wall-clock seconds per step).
 
 Prints one JSON line with, besides the required keys,
   roofline     - the fused E-step kernel's flops per launch / its average
@@ -132,21 +132,29 @@ def measured_peaks(torch, gmm, dev, reps: int = 5):
     return res
 
 
+def param_buffers(torch, mu, var, logw, dev):
+    """The initial parameters P0 and the working parameters P on the device,
+    each one flat buffer [mu | var | logw], and mu, var, logw as views of P:
+    a step resets all three with one device copy."""
+    K, d = mu.shape
+    flat = np.concatenate([mu.ravel(), var.ravel(), logw.ravel()]).astype(np.float32)
+    P0 = torch.from_numpy(flat).to(dev)
+    P = P0.clone()
+    return P0, P, P[:K * d].view(K, d), P[K * d:2 * K * d].view(K, d), P[2 * K * d:]
+
+
 def host_streamed(args, w, X, mu, var, logw, torch, gmm, dev):
     """One step = the row-chunked E-step over X in pinned host memory (copies of
     chunk i+1 overlap the scoring of chunk i) plus the M-step, from the initial
     parameters. Prints one JSON line with the PCIe-inclusive rate."""
     N, d, K = X.shape[0], X.shape[1], mu.shape[0]
     Xh = torch.from_numpy(X).pin_memory()
-    mu0, var0, lw0 = (torch.from_numpy(a.copy()).to(dev) for a in (mu, var, logw))
-    mud, vard, lwd = mu0.clone(), var0.clone(), lw0.clone()
+    P0, P, mud, vard, lwd = param_buffers(torch, mu, var, logw, dev)
     xt = gmm.GMM_F16 if X.dtype == np.float16 else gmm.GMM_F32
     ws = gmm.workspace_chunked(N, d, K, args.chunk_rows, xt, dev)
 
     def step():
-        mud.copy_(mu0)
-        vard.copy_(var0)
-        lwd.copy_(lw0)
+        P.copy_(P0)
         Nk, Sx, Sxx, _, _ = gmm.estep_stats_chunked(Xh, mud, vard, lwd, args.chunk_rows, ws=ws)
         gmm.mstep(Nk, Sx, Sxx, N, VAR_FLOOR, mud, vard, lwd)
 
@@ -354,15 +362,12 @@ def main(argv=None):
         return top2_bench(args, w, X, mu, var, logw, torch, gmm, dev)
     N, d, K = X.shape[0], X.shape[1], mu.shape[0]
     Xd = torch.from_numpy(X).to(dev)
-    mu0, var0, lw0 = (torch.from_numpy(a.copy()).to(dev) for a in (mu, var, logw))
-    mud, vard, lwd = mu0.clone(), var0.clone(), lw0.clone()
+    P0, P, mud, vard, lwd = param_buffers(torch, mu, var, logw, dev)
     ws = gmm.workspace(N, d, K, dev)
     torch.cuda.synchronize()
 
     def step():
-        mud.copy_(mu0)
-        vard.copy_(var0)
-        lwd.copy_(lw0)
+        P.copy_(P0)
         gmm.em_iterate(Xd, mud, vard, lwd, 1, VAR_FLOOR, ws=ws)
 
     for _ in range(args.warmup):
