@@ -85,6 +85,9 @@ constexpr float kCapWin = 32.f;
 constexpr int kCapLevels = 13;
 __constant__ float kCapLadder[kCapLevels] = {kCapWin, 26.f, 22.f, 19.f, 17.f, 15.f, 13.f, 11.f, 9.f,
                                              7.f, 5.f, 3.f, 0.f};
+// 2^-W for each level W of kCapLadder (compile-time constants).
+constexpr float kCapQ[kCapLevels] = {0x1p-32f, 0x1p-26f, 0x1p-22f, 0x1p-19f, 0x1p-17f, 0x1p-15f, 0x1p-13f,
+                                     0x1p-11f, 0x1p-9f,  0x1p-7f,  0x1p-5f,  0x1p-3f,  1.f};
 // Word 3 of a raw buffer resource on CDNA (32-bit data format, no swizzle):
 // loads at offsets past the record count return zero.
 constexpr int kBufferRsrcWord3 = 0x00020000;
@@ -664,30 +667,56 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     float th = -INFINITY;
     int mine = 0, cnt = 0;
     if (m != -INFINITY) {
-      th = m - kCapLadder[0];
-      mine = count_ge(th);
-      cnt = (int)group_sum((float)mine, T2);
-      if (cnt > kCandT) {
-        // the loosest level that admits at most kCandT: counts only fall
-        // along the ladder, so bisect levels [1, kCapLevels); kCapLevels
-        // stands for none
-        int lo = 1, hi = kCapLevels;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if ((int)group_sum((float)count_ge(m - kCapLadder[mid]), T2) <= kCandT)
-            hi = mid;
-          else
-            lo = mid + 1;
+      // The loosest level that admits at most kCandT entries. Counts only
+      // fall along the ladder, so: level 0, then a bisection of the levels
+      // [lo, kCapLevels), kCapLevels standing for none. Levels that z alone
+      // shows to admit more are not counted: an entry below a level's
+      // threshold has e < q = 2^-W (times qm, a margin for the fp32 rounding
+      // of m - W) and an entry at or above it e <= 1, so
+      // z < count + (KS - count) q, i.e. count > (z - KS q) / (1 - q); z is
+      // taken 1e-6 low for its own rounding and the test (in fp32) carries
+      // 1e-3 of slack. A level proven to admit more implies as much of every
+      // looser one, so lo = 1 + the tightest proven level. Dense slabs thus
+      // go straight to the tight levels.
+      const float zl = (float)z * (1.f - 1e-6f);
+      const float qm = __builtin_amdgcn_exp2f((fabsf(m) + kCapWin) * 2.4e-7f);
+      int lo = 0;
+      if (zl > (float)kCandT)  // (no level can be proven otherwise)
+#pragma unroll
+        for (int i = 0; i < kCapLevels - 1; ++i) {
+          const float q = kCapQ[i] * qm;
+          lo = zl - (float)KS * q > (float)kCandT * (1.f - q) + 1e-3f ? i + 1 : lo;
         }
-        if (lo < kCapLevels) {
-          th = m - kCapLadder[lo];
-          mine = count_ge(th);
-          cnt = (int)group_sum((float)mine, T2);
+      int hi = kCapLevels, mine_hi = 0, cnt_hi = 0;  // the last level found to admit <= kCandT
+      if (lo == 0) {
+        const int c0 = count_ge(m - kCapLadder[0]);
+        const int g0 = (int)group_sum((float)c0, T2);
+        if (g0 <= kCandT) {
+          hi = 0;
+          mine_hi = c0;
+          cnt_hi = g0;
         } else {
-          th = next_up(m);
-          mine = 0;
-          cnt = 0;
+          lo = 1;
         }
+      }
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const int cm = count_ge(m - kCapLadder[mid]);
+        const int gm = (int)group_sum((float)cm, T2);
+        if (gm <= kCandT) {
+          hi = mid;
+          mine_hi = cm;
+          cnt_hi = gm;
+        } else {
+          lo = mid + 1;
+        }
+      }
+      if (hi < kCapLevels) {
+        th = m - kCapLadder[hi];
+        mine = mine_hi;
+        cnt = cnt_hi;
+      } else {
+        th = next_up(m);
       }
     }
     // this thread's first slot: exclusive prefix of the counts over the row's lanes
