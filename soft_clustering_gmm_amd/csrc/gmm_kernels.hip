@@ -725,6 +725,28 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       const int t = __shfl_up(incl, o, T2);
       if (psub >= o) incl += t;
     }
+    // The candidates are staged in the row's own score-tile row (its scores
+    // are in registers by now; the row's threads are lanes of one wave):
+    // candidate j's score at float j, its component at word 8 + j. The
+    // record is then written by consecutive lanes: the scores as floats, the
+    // components packed four to a word (slots past the count hold stale
+    // words, masked to a byte; the merge reads only the first `count`).
+    float* stg = sc + row * SCS;
+    if (mine) {
+      int slot = incl - mine;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const float vv[4] = {ev[i].x, ev[i].y, ev[i].z, ev[i].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (vv[u] >= th) {
+            stg[slot] = vv[u];
+            reinterpret_cast<uint32_t*>(stg)[8 + slot] = (uint32_t)(4 * (psub + T2 * i) + u);
+            ++slot;
+          }
+      }
+    }
+    wave_lds_sync();
     if (valid) {
       const size_t rec = (size_t)slab * N + grow;
       if (psub == 0) p1.h[rec] = make_float4((float)z, m, th, (float)cnt);
@@ -732,19 +754,11 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         p1.rowE[grow] = gam * (a_max * sq + fminf(b_max * ab, b2_max * sqrtf(sq))) + 2.f * kUnitRound * c_max;
         p1.rowSq[grow] = sq;
       }
-      if (mine) {
-        size_t slot = rec * kCandT + (size_t)(incl - mine);
-#pragma unroll
-        for (int i = 0; i < NC; ++i) {
-          const float vv[4] = {ev[i].x, ev[i].y, ev[i].z, ev[i].w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (vv[u] >= th) {
-              p1.v[slot] = vv[u];
-              p1.k[slot] = (uint8_t)(4 * (psub + T2 * i) + u);
-              ++slot;
-            }
-        }
+      for (int j = psub; j < cnt; j += T2) p1.v[rec * kCandT + j] = stg[j];
+      for (int j = psub; 4 * j < cnt; j += T2) {
+        const uint32_t* kk = reinterpret_cast<const uint32_t*>(stg) + 8 + 4 * j;
+        *reinterpret_cast<uint32_t*>(p1.k + rec * kCandT + 4 * j) =
+            (kk[0] & 0xffu) | ((kk[1] & 0xffu) << 8) | ((kk[2] & 0xffu) << 16) | ((kk[3] & 0xffu) << 24);
       }
     }
   };
