@@ -487,20 +487,26 @@ __device__ __forceinline__ void row_norms(const float* xs, int row, int sub, int
 }
 
 // ---------------------------------------------------------------------------
-// Statistics kernel: single sweep (MODE 0) or the second pass (MODE 1)
+// Fused score kernel: the single sweep (MODE 0), and the first (MODE 2) and
+// second (MODE 1) passes of the two-pass regime
 // ---------------------------------------------------------------------------
 //
 // Block = `waves` waves; wave w owns components kw = k0 + 32w .. kw + 31 of
-// its slab. The block walks the 64-point tiles of its row chunk:
-//   1. X tile -> LDS (zero padded to DP features and 64 rows)
+// its slab. The block walks the 64-point tiles of its row chunk (MODE 1: of
+// its slab's row list):
+//   1. X tile -> LDS (padded to DP features and 64 rows)
 //   2. scores: two 32x32 fp32 MFMA accumulators per wave -> LDS score tile
 //   3. row phase (`waves` threads per row): max, log-sum-exp (MODE 0) or the
-//      first pass's (m, lZ) (MODE 1), gated exact re-score; the tile then
-//      holds e = exp(s - m) and a per-row 1/z (MODE 0) or r itself (MODE 1)
+//      row references (m, lZ, theta) of the merge (MODE 1), gated exact
+//      re-score; the tile then holds e = exp(s - m) and a per-row 1/z
+//      (MODE 0) or r itself (MODE 1). MODE 2 instead writes per (row, slab)
+//      the slab's maximum, normaliser and candidates (p1_rows), a half tile
+//      at a time, and stops there.
 //   4. statistics, one point per step: r of the wave's 32 components is the
 //      A operand and x (block 0) or x^2 (block 1) the B operand of two-block
 //      32x32x1 MFMAs that accumulate Sx and Sxx in registers; a point whose
-//      32 responsibilities are all exactly zero is skipped.
+//      32 responsibilities are all at or below rho / max(1, |x|^2) is
+//      skipped.
 // At the end each block writes its statistics partial; a separate kernel
 // sums the partials in a fixed order (no atomics anywhere).
 // Outputs of the fp32 first pass (MODE 2), per (row, slab): see Pass1Out.
