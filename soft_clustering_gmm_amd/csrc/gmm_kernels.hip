@@ -549,7 +549,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   constexpr int kXT = MODE == 2 ? 1 : 2, kSR = MODE == 2 ? 32 : 64;
   float* xsb = smem;               // [kXT][64][XS]: current (and next) X tile
   float* sc = xsb + kXT * 64 * XS; // [kSR][SCS]
-  float* rv = sc + kSR * SCS;      // [64][4] per-row references (m, lZ or 1/z, theta)
+  float* rv = sc + kSR * SCS;      // [64][4] per-row references (m, lZ or 1/z, theta, MODE 1: |x|^2)
   double* lls = reinterpret_cast<double*>(rv + (MODE == 2 ? 0 : 256));  // [nthr]
   uint32_t* reflist = reinterpret_cast<uint32_t*>(lls + nthr);  // [waves][kRefCap]
   uint32_t* nzrow = reflist + waves * kRefCap;  // [64]: bit w = row has a nonzero r for wave w
@@ -774,10 +774,12 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     __syncthreads();
     if (MODE == 1 && tid < 64) {
       const int64_t pos = r0 + tid;
-      const float4 mr = pos < hi ? rowref[row_at(pos)] : make_float4(0.f, 0.f, INFINITY, 0.f);
+      const int64_t gr = pos < hi ? row_at(pos) : 0;
+      const float4 mr = pos < hi ? rowref[gr] : make_float4(0.f, 0.f, INFINITY, 0.f);
       rv[4 * tid] = mr.x;
       rv[4 * tid + 1] = mr.y;
       rv[4 * tid + 2] = mr.z;
+      rv[4 * tid + 3] = pos < hi ? p1.rowSq[gr] : 0.f;  // |x|^2 from the first pass
     }
 
     // 2. scores (the first pass stores them a half tile at a time)
@@ -819,8 +821,13 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       const int64_t grow = r0 + row;
       const bool valid = grow < hi;
       float* srow = sc + row * SCS;
-      float sq, ab;
-      row_norms<DP, XS>(xs, row, psub, tpr, d, sq, ab);
+      // |x|^2 and |x|_1 (the second pass has |x|^2 from the first and needs
+      // no bound)
+      float sq, ab = 0.f;
+      if (MODE == 1)
+        sq = rv[4 * row + 3];
+      else
+        row_norms<DP, XS>(xs, row, psub, tpr, d, sq, ab);
       const float Ebound = gam * (a_max * sq + fminf(b_max * ab, b2_max * sqrtf(sq))) + 2.f * kUnitRound * c_max;
 
       // Each thread owns the 16-byte chunks psub + tpr*i (i < 8) of its row,
