@@ -162,6 +162,31 @@ __device__ __forceinline__ float group_sum(float v, int tpr) {
   if (tpr > 8) v += dpp_f<kDppMirror>(v);
   return v;
 }
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t group_or(uint32_t v, int tpr) {
+  if (tpr > 1) v |= dpp_u<kDppXor1>(v);
+  if (tpr > 2) v |= dpp_u<kDppXor2>(v);
+  if (tpr > 4) v |= dpp_u<kDppHalfMirror>(v);
+  if (tpr > 8) v |= dpp_u<kDppMirror>(v);
+  return v;
+}
+// Inclusive prefix sum over aligned groups of tpr consecutive lanes (tpr a
+// power of two <= 16): DPP row shifts by 1, 2, 4, 8; a lane adds the shifted
+// value only when its source lies in its own group.
+__device__ __forceinline__ int group_incl_scan(int v, int sub, int tpr) {
+  int t = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  if (tpr > 1 && sub >= 1) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  if (tpr > 2 && sub >= 2) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  if (tpr > 4 && sub >= 4) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  if (tpr > 8 && sub >= 8) v += t;
+  return v;
+}
 __device__ __forceinline__ double group_sum_d(double v, int tpr) {
   if (tpr > 1) v += dpp_d<kDppXor1>(v);
   if (tpr > 2) v += dpp_d<kDppXor2>(v);
@@ -726,11 +751,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       }
     }
     // this thread's first slot: exclusive prefix of the counts over the row's lanes
-    int incl = mine;
-    for (int o = 1; o < T2; o <<= 1) {
-      const int t = __shfl_up(incl, o, T2);
-      if (psub >= o) incl += t;
-    }
+    const int incl = group_incl_scan(mine, psub, T2);
     // The candidates are staged in the row's own score-tile row (its scores
     // are in registers by now; the row's threads are lanes of one wave):
     // candidate j's score at float j, its component at word 8 + j. The
@@ -899,7 +920,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           const bool nz = (v.x > wthr) | (v.y > wthr) | (v.z > wthr) | (v.w > wthr);
           nzb |= (nz ? 1u : 0u) << ((i * waves) >> 3);
         }
-        for (int o = 1; o < tpr; o <<= 1) nzb |= (uint32_t)__shfl_xor((int)nzb, o, 64);
+        nzb = group_or(nzb, tpr);
         if (psub == 0) nzrow[row] = valid ? nzb : 0u;
       }
       // Which entries need the exact re-score (E = Ebound, r_k = e_k / z)?
