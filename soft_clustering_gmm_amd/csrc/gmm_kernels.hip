@@ -937,7 +937,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       uint32_t mask = 0;
       if (MODE == 0) {
         const float zf = (float)z;
-        const float thr2 = kGateTau * zf * zf / (2.f * Ebound);  // on e (z - e)
+        const float thr2 = kGateTau * zf * zf * __builtin_amdgcn_rcpf(2.f * Ebound);  // on e (z - e)
         const float maxq = zf >= 2.f ? zf - 1.f : 0.25f * zf * zf;
         const bool refine = valid && maxq > thr2;
         float flagged = 0.f;
@@ -1049,9 +1049,11 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         z2 = group_sum_d(z2, tpr);
         if (redo) z = z2;
         // z is in [1, K]: the fp32 hardware log2 is good to ~1e-7 absolute, far
-        // inside the 1e-4 relative bar of l_n; r itself uses 1/z.
+        // inside the 1e-4 relative bar of l_n; r = e / z uses the hardware
+        // reciprocal of z in fp32 (1 ulp: with z's own 2 u, r is within
+        // 4e-7 relative).
         const double lZd = (double)__builtin_amdgcn_logf((float)z);  // log2
-        const float invz = valid ? (float)(1.0 / z) : 0.f;
+        const float invz = valid ? __builtin_amdgcn_rcpf((float)z) : 0.f;
         if (valid && psub == 0) {
           const double l = ((double)m + lZd) * kLn2;
           ll_acc += l;
