@@ -2321,7 +2321,9 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
 // Scores come from 16x16x4 f64 MFMAs (layout: D[comp][point]),
 // so each lane holds four components of one point per accumulator and keeps
 // an online (max, sum of exp) per point; lanes and waves are merged at the
-// end in a fixed order. Output per row: (m_ref, lZ) with m_ref = fp32 of the
+// end in a fixed order. The sum takes fp32 exponentials of the fp64
+// differences (each within about one fp32 ulp), so l carries about 1e-7
+// relative error on top of fp64 scores. Output per row: (m_ref, lZ) with m_ref = fp32 of the
 // row max and lZ = l - m_ref, the per-point l, and optionally the top-2.
 __device__ __forceinline__ bool better(double v, int i, double w, int j) {
   return v > w || (v == w && i < j);
