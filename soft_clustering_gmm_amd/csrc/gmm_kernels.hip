@@ -527,11 +527,12 @@ __device__ __forceinline__ void row_norms(const float* xs, int row, int sub, int
 //      (MODE 0) or r itself (MODE 1). MODE 2 instead writes per (row, slab)
 //      the slab's maximum, normaliser and candidates (p1_rows), a half tile
 //      at a time, and stops there.
-//   4. statistics, one point per step: r of the wave's 32 components is the
-//      A operand and x (block 0) or x^2 (block 1) the B operand of two-block
-//      32x32x1 MFMAs that accumulate Sx and Sxx in registers; a point whose
-//      32 responsibilities are all at or below rho / max(1, |x|^2) is
-//      skipped.
+//   4. statistics: r of the wave's 32 components is the A operand, x and
+//      x^2 the B operands of MFMAs that accumulate Sx and Sxx in registers:
+//      in the single sweep one point per two-block 32x32x1 MFMA, skipping a
+//      point whose 32 responsibilities are all at or below
+//      rho / max(1, |x|^2); in the second pass every point of the listed
+//      rows, two per 32x32x2 MFMA.
 // At the end each block writes its statistics partial; a separate kernel
 // sums the partials in a fixed order (no atomics anywhere).
 // Outputs of the fp32 first pass (MODE 2), per (row, slab): see Pass1Out.
@@ -574,7 +575,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   constexpr int kXT = MODE == 2 ? 1 : 2, kSR = MODE == 2 ? 32 : 64;
   float* xsb = smem;               // [kXT][64][XS]: current (and next) X tile
   float* sc = xsb + kXT * 64 * XS; // [kSR][SCS]
-  float* rv = sc + kSR * SCS;      // [64][4] per-row references (m, lZ or 1/z, theta, MODE 1: |x|^2)
+  float* rv = sc + kSR * SCS;      // [64][4] per-row references (m, lZ or 1/z, theta)
   double* lls = reinterpret_cast<double*>(rv + (MODE == 2 ? 0 : 256));  // [nthr]
   uint32_t* reflist = reinterpret_cast<uint32_t*>(lls + nthr);  // [waves][kRefCap]
   uint32_t* nzrow = reflist + waves * kRefCap;  // [64]: bit w = row has a nonzero r for wave w
@@ -800,7 +801,6 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       rv[4 * tid] = mr.x;
       rv[4 * tid + 1] = mr.y;
       rv[4 * tid + 2] = mr.z;
-      rv[4 * tid + 3] = pos < hi ? p1.rowSq[gr] : 0.f;  // |x|^2 from the first pass
     }
 
     // 2. scores (the first pass stores them a half tile at a time)
@@ -842,13 +842,10 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       const int64_t grow = r0 + row;
       const bool valid = grow < hi;
       float* srow = sc + row * SCS;
-      // |x|^2 and |x|_1 (the second pass has |x|^2 from the first and needs
-      // no bound)
-      float sq, ab = 0.f;
-      if (MODE == 1)
-        sq = rv[4 * row + 3];
-      else
-        row_norms<DP, XS>(xs, row, psub, tpr, d, sq, ab);
+      // |x|^2 and |x|_1 for the bound and the skip threshold (the second pass
+      // needs neither)
+      float sq = 0.f, ab = 0.f;
+      if (MODE == 0) row_norms<DP, XS>(xs, row, psub, tpr, d, sq, ab);
       const float Ebound = gam * (a_max * sq + fminf(b_max * ab, b2_max * sqrtf(sq))) + 2.f * kUnitRound * c_max;
 
       // Each thread owns the 16-byte chunks psub + tpr*i (i < 8) of its row,
@@ -901,8 +898,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           srow4[psub + tpr * i] = v;
         }
       }
-      // Which waves' component slices hold a responsibility above
-      // rho / max(1, |x|^2) in this row (r = e / z in MODE 0); a point whose
+      // (Single sweep) Which waves' component slices hold a responsibility
+      // above rho / max(1, |x|^2) in this row (r = e / z); a point whose
       // 32 responsibilities for a wave are all at or below that threshold is
       // left out of that wave's statistics. Over all N points this drops at
       // most N rho (1 + 2E) from any Nk, and, as |x_j| <= |x|^2 for |x|^2 >= 1,
@@ -911,9 +908,9 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       // belongs to wave (i * waves) / 8. The bits are taken from the fp32
       // responsibilities, before the re-score (which moves an entry by a
       // factor within 1 +- 2E); rows past the end take none (their r is zero).
-      if constexpr (!SPLIT) {
+      if constexpr (!SPLIT && MODE == 0) {
         uint32_t nzb = 0;
-        const float wthr = rho / fmaxf(1.f, sq) * (MODE == 0 ? (float)z : 1.f);
+        const float wthr = rho / fmaxf(1.f, sq) * (float)z;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float4 v = ev[i];
@@ -1135,6 +1132,28 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           SXX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rl, qh, SXX[t2], 0, 0, 0);
         }
       }
+    } else if constexpr (MODE == 1) {
+      // Second pass: two points per step on the 32x32x2 MFMA, lanes h = 0 and
+      // h = 1 holding r and x of points p0 and p0 + 1 (the A and B operands),
+      // Sx and Sxx in separate instructions whose accumulators have the
+      // layout of the two-block form's blocks. Every point is taken: the row
+      // lists already left out the (row, slab) pairs without a responsibility
+      // above the threshold, and on the pairs they keep this plain loop runs
+      // faster than the one-point form with its per-point skip (ivf 71.6 ->
+      // 67.4 ms; largek 68.0 -> 68.9 ms).
+#pragma unroll 2
+      for (int p0 = 0; p0 < 64; p0 += 2) {
+        const int p = p0 + h;
+        const float r = sc[p * SCS + wave * 32 + c];
+        nk += r;
+        const float* xr = xs + p * XS + DT * c;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          const float xv = xr[t];
+          SX[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(r, xv, SX[t], 0, 0, 0);
+          SXX[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(r, xv * xv, SXX[t], 0, 0, 0);
+        }
+      }
     } else {
       // One point per step on the two-block 32x32x1 MFMA: both halves of the
       // wave hold r of component c of point p (the A operand of either block),
@@ -1164,8 +1183,10 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
         for (int t = 0; t < DT; ++t) S2[t] = __builtin_amdgcn_mfma_f32_32x32x1f32(r, bv[t], S2[t], 0, 0, 0);
       };
       // Active points in increasing order, two per iteration (no register
-      // rotation). An odd count is padded with the lowest inactive point,
-      // whose r is exactly zero; past the end the loads read point 0, unused.
+      // rotation). An odd count is padded with the lowest inactive point
+      // (its responsibilities are at most the threshold, or zero past the
+      // last row: taking it only adds what the skip would leave out); past
+      // the end the loads read point 0, unused.
       uint64_t am = __builtin_amdgcn_ballot_w64((nzrow[lane] >> wave) & 1u);
       const int na = __builtin_popcountll(am);
       if (na & 1) am |= ~am & (am + 1);
@@ -1254,11 +1275,12 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     for (int j = 0; j < 16; ++j) {
       const int comp = kw + acc_row(h, j);
       const int f = DT * c + t;
-      part[(size_t)comp * E + 1 + f] = SPLIT ? SX[t][j] : S2[t][j];
-      part[(size_t)comp * E + 1 + DP + f] = SPLIT ? SXX[t][j] : S2[t][16 + j];
+      part[(size_t)comp * E + 1 + f] = (SPLIT || MODE == 1) ? SX[t][j] : S2[t][j];
+      part[(size_t)comp * E + 1 + DP + f] = (SPLIT || MODE == 1) ? SXX[t][j] : S2[t][16 + j];
     }
-  // the split path's halves saw different points; the fp32 path's the same ones
-  if (SPLIT) nk += __shfl_xor(nk, 32, 64);
+  // the halves of the split path and of the second pass saw different points;
+  // those of the single sweep's one-point form the same ones
+  if (SPLIT || MODE == 1) nk += __shfl_xor(nk, 32, 64);
   if (h == 0) part[(size_t)(kw + c) * E] = nk;
 
   if (MODE == 0) {
