@@ -1,16 +1,19 @@
 """GPU parity where most responsibilities are zero or negligible.
 
-The fp32 statistics loop of the fused kernels visits, per wave, only the
-points with a responsibility above rho / max(1, |x|^2) (rho = 2^-20 / N)
-among the wave's 32 components; the points it leaves out move any statistic
-by at most about rho N = 2^-20. These cases make that skip extreme: components come in
-groups of 32 (one wave's slice each) whose centres are so far apart that a
-point's responsibilities outside its own group underflow to exactly zero.
-With rows sorted by group whole tiles belong to one group, so seven of eight
-waves skip every point; shuffled rows give every wave a few points per tile
-(odd counts included); K = 200 leaves the last wave with padding only.
-Everything is compared with the float64 oracle at the usual bars, in the
-single sweep and in the second pass of the two-pass regime.
+The statistics leave out responsibilities at or below rho / max(1, |x|^2)
+(rho = 2^-20 / N): the single sweep per wave (a point whose responsibilities
+for the wave's 32 components are all below it), the two-pass regime per
+256-component slab (the second pass walks only the rows listed for each
+slab). What is left out moves any statistic by at most about rho N = 2^-20.
+These cases make that skip extreme: components come in groups of 32 (one
+wave's slice each) whose centres are so far apart that a point's
+responsibilities outside its own group underflow to exactly zero. With rows
+sorted by group whole tiles belong to one group, so seven of eight waves skip
+every point; shuffled rows give every wave a few points per tile (odd counts
+included); K = 200 leaves the last wave with padding only. Everything is
+compared with the float64 oracle at the usual bars, in both regimes; the
+row lists' extremes (an empty slab, a slab of 37 rows) have a case of their
+own.
 """
 import numpy as np
 import pytest
