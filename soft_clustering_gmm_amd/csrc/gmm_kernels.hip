@@ -547,9 +547,13 @@ struct Pass1Out {
 // The first pass (MODE 2) keeps one X tile and half a score tile in LDS and
 // fits in 128 registers, so that two blocks share a CU and one block's row
 // phase overlaps the other's score MFMAs.
-template <int DT, int MODE, typename XT, bool SPLIT>
+// WV: the block's wave count when fixed at compile time (8, for slabs of 256
+// components), 0 when it comes from `waves_rt`. With it fixed, the row
+// phase's cross-lane reductions over a row's threads compile to straight DPP
+// sequences instead of branches on the thread count.
+template <int DT, int MODE, typename XT, bool SPLIT, int WV>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 4 : 1)))
-estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, int waves, int kslabs,
+estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, int waves_rt, int kslabs,
                    int64_t rows_per_chunk, const float4* __restrict__ W32p, const float* __restrict__ c32,
                    const float* __restrict__ mup, const double* __restrict__ ivp,
                    const double* __restrict__ c64d, const float* __restrict__ errc,
@@ -560,7 +564,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
   constexpr int DP = 32 * DT, Q = DP / 4, XS = DP + 4, E = 1 + 2 * DP;
   extern __shared__ __align__(16) float smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
-  const int nthr = blockDim.x;
+  const int waves = WV ? WV : waves_rt;
+  const int nthr = WV ? WV * 64 : (int)blockDim.x;
   const int KS = waves * 32, SCS = KS + 8;
   // (chunk, slab) of this block, slab fastest. Blocks are dealt to the 8 XCDs
   // in turn, so with a slab count that is a multiple of 8 (or divides 8) each
@@ -2742,8 +2747,9 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
                                : (size_t)(2 * 64 * (32 * DT + 4) + 64 * (KS + 8) + 256) * sizeof(float) +
                                      (size_t)nthr * sizeof(double) +
                                      (size_t)(p.waves * kRefCap + 64) * sizeof(uint32_t);
-  auto fn = (p.stats_split && MODE != 2) ? estep_stats_kernel<DT, MODE, XT, true>
-                                         : estep_stats_kernel<DT, MODE, XT, false>;
+  const bool split = p.stats_split && MODE != 2;
+  auto fn = p.waves == 8 ? (split ? estep_stats_kernel<DT, MODE, XT, true, 8> : estep_stats_kernel<DT, MODE, XT, false, 8>)
+                         : (split ? estep_stats_kernel<DT, MODE, XT, true, 0> : estep_stats_kernel<DT, MODE, XT, false, 0>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
