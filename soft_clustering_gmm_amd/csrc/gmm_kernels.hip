@@ -2094,28 +2094,49 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
     //    four lanes g of a point, lane (g = b, c) keeps |x|^2 of point
     //    16b + c, the point it takes in the row phase.
     float sq = 0.f;
+    {
+      // the four blocks' operands first (one LDS round trip), then their four
+      // MFMA chains interleaved
+      float xa[4][DP / 4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      float sqb = 0.f;
-      const float* xrow = xs + (16 * b + c) * XS + g * (DP / 4);
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int q = 0; q < DP / 16; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(xrow + 4 * q);
-        const float xv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float x2 = xv[u] * xv[u];
-          sqb += x2;
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x2, w[8 * q + 2 * u], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[u], w[8 * q + 2 * u + 1], acc, 0, 0, 0);
+        for (int q = 0; q < DP / 16; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(xs + (16 * b + c) * XS + g * (DP / 4) + 4 * q);
+          xa[b][4 * q] = v.x;
+          xa[b][4 * q + 1] = v.y;
+          xa[b][4 * q + 2] = v.z;
+          xa[b][4 * q + 3] = v.w;
         }
-      }
-      sqb += __shfl_xor(sqb, 16, 64);
-      sqb += __shfl_xor(sqb, 32, 64);
-      if (g == b) sq = sqb;
+      __builtin_amdgcn_sched_barrier(0);
+      v4f acc[4];
+      float sqb[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sc[(16 * b + 4 * g + j) * SS + c] = acc[j];
+      for (int b = 0; b < 4; ++b) {
+        acc[b] = (v4f){0.f, 0.f, 0.f, 0.f};
+        sqb[b] = 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < DP / 4; ++u) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float x2 = xa[b][u] * xa[b][u];
+          sqb[b] += x2;
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(x2, w[2 * u], acc[b], 0, 0, 0);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[b][u], w[2 * u + 1], acc[b], 0, 0, 0);
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        float v = sqb[b];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        if (g == b) sq = v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[(16 * b + 4 * g + j) * SS + c] = acc[b][j];
+      }
     }
     __builtin_amdgcn_s_setprio(0);
     wave_lds_sync();
@@ -2251,20 +2272,25 @@ estep_small_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int64_t wa
     __builtin_amdgcn_s_setprio(1);
     if constexpr (!SPLIT) {
       // 4. statistics: step j of block b uses r of point 16b + 4g + j (component c)
+      // operands of all 16 steps first (one LDS round trip), then the MFMAs
+      float rr[16], xx[16][DS];
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int q = 0; q < 16; ++q) {
+        const int p = 16 * (q >> 2) + 4 * g + (q & 3);
+        rr[q] = sc[p * SS + c];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int p = 16 * b + 4 * g + j;
-          const float r = sc[p * SS + c];
-          nk += r;
+        for (int t = 0; t < DS; ++t) xx[q][t] = xs[p * XS + 16 * t + c];
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int t = 0; t < DS; ++t) {
-            const float xv = xs[p * XS + 16 * t + c];
-            SX[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(r, xv, SX[t], 0, 0, 0);
-            SXX[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(r, xv * xv, SXX[t], 0, 0, 0);
-          }
+      for (int q = 0; q < 16; ++q) {
+        nk += rr[q];
+#pragma unroll
+        for (int t = 0; t < DS; ++t) {
+          SX[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(rr[q], xx[q][t], SX[t], 0, 0, 0);
+          SXX[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(rr[q], xx[q][t] * xx[q][t], SXX[t], 0, 0, 0);
         }
+      }
     } else {
       // 4. statistics as split-bf16 products on the bf16 MFMA (16x16x32): each
       //    fp32 operand v = hi + lo + d with hi = bf16(v), lo = bf16(v - hi),
