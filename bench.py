@@ -8,6 +8,9 @@ in HBM. Every step (warm-up and timed) starts from the same initial
 parameters (K data points as means, unit variances, equal weights), restored
 by one device copy of the flat parameter buffer inside the step, so that all
 steps do identical work. `value` = N*K / (wall-clock seconds per step).
+Unless --warmup is given, the untimed warm-up runs at least 3 steps and
+200 ms, past the GPU's clock ramp (the first ~30 ms of back-to-back E-steps
+run up to ~12% slower); the line reports how many warm-up steps ran.
 
 Prints one JSON line with, besides the required keys,
   roofline     - the fused E-step kernel's flops per launch / its average
@@ -49,6 +52,30 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 # host core (two GEMMs of 2d per point x component, plus the exponentials):
 # only used to choose the row sample so that the baseline takes ~20 s.
 CPU_BUDGET_POINT_COMP_D = 2.5e10
+
+
+WARMUP_MIN_STEPS = 3
+WARMUP_MIN_MS = 200.0
+
+
+def warm_up(step, args, torch) -> int:
+    """Untimed steps before the timed ones; returns how many ran. With --warmup W exactly W.
+    By default at least WARMUP_MIN_STEPS steps and WARMUP_MIN_MS of wall time, each step
+    synchronised: on a GPU that has just become busy the first ~30 ms of back-to-back E-steps
+    run up to ~12% slower while its clock ramps up (rocprofv3 traces of 300 launches), and the
+    timed steps should measure the steady state."""
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        return args.warmup
+    n = 0
+    t0 = time.perf_counter()
+    while n < WARMUP_MIN_STEPS or 1e3 * (time.perf_counter() - t0) < WARMUP_MIN_MS:
+        step()
+        torch.cuda.synchronize()
+        n += 1
+    return n
 
 
 def kernel_source_hash() -> str:
@@ -158,8 +185,7 @@ def host_streamed(args, w, X, mu, var, logw, torch, gmm, dev):
         Nk, Sx, Sxx, _, _ = gmm.estep_stats_chunked(Xh, mud, vard, lwd, args.chunk_rows, ws=ws)
         gmm.mstep(Nk, Sx, Sxx, N, VAR_FLOOR, mud, vard, lwd)
 
-    for _ in range(args.warmup):
-        step()
+    warmup = warm_up(step, args, torch)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -169,7 +195,7 @@ def host_streamed(args, w, X, mu, var, logw, torch, gmm, dev):
     xbytes = X.nbytes
     out = {
         "metric": METRIC + " [X streamed from pinned host memory]", "value": N * K / (ms * 1e-3), "unit": UNIT,
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "n_gpus": 1, "steps": args.steps, "warmup": warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{w.name}: N={N} d={d} K={K} {w.x_dtype}; X in pinned host memory, "
                                f"{args.chunk_rows} rows per chunk; step = chunked E-step + M-step",
@@ -191,9 +217,8 @@ def border_lists_bench(args, w, torch, gmm, dev):
     idx_d, resp_d = torch.from_numpy(idx).to(dev), torch.from_numpy(resp).to(dev)
     members = torch.empty(2 * N, dtype=torch.int32, device=dev)
     ws = torch.empty(int(gmm.lib().gmm_border_lists_workspace_bytes(N, K)), dtype=torch.uint8, device=dev)
-    for _ in range(args.warmup):
-        off, _ = gmm.border_lists(idx_d, resp_d, K, args.border_threshold, ws=ws, members=members)
-    torch.cuda.synchronize()
+    warmup = warm_up(lambda: gmm.border_lists(idx_d, resp_d, K, args.border_threshold, ws=ws, members=members),
+                     args, torch)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for a, b in evs:
@@ -208,7 +233,7 @@ def border_lists_bench(args, w, torch, gmm, dev):
     gbps = alg / (k_ms * 1e-3) / 1e9
     out = {
         "metric": "border-vector inverted-list build, points/s", "value": N / (ms * 1e-3), "unit": "points/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "n_gpus": 1, "steps": args.steps, "warmup": warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
         "config": {"workload": f"{w.name} shape: N={N} K={K}, synthetic top-2 (seed 11), threshold "
                                f"{args.border_threshold}, {entries} list entries", "N": N, "K": K},
@@ -229,9 +254,7 @@ def top2_bench(args, w, X, mu, var, logw, torch, gmm, dev):
     Xd = torch.from_numpy(X).to(dev)
     mud, vard, lwd = (torch.from_numpy(a.copy()).to(dev) for a in (mu, var, logw))
     ws = gmm.workspace(N, d, K, dev)
-    for _ in range(args.warmup):
-        gmm.assign_top2(Xd, mud, vard, lwd, ws=ws)
-    torch.cuda.synchronize()
+    warmup = warm_up(lambda: gmm.assign_top2(Xd, mud, vard, lwd, ws=ws), args, torch)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for a, b in evs:
@@ -245,7 +268,7 @@ def top2_bench(args, w, X, mu, var, logw, torch, gmm, dev):
     ach = flops / (k_ms * 1e-3) / 1e12
     out = {
         "metric": "top-2 assignment, points x components/s", "value": N * K / (ms * 1e-3),
-        "unit": "points×components/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "unit": "points×components/s", "n_gpus": 1, "steps": args.steps, "warmup": warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f64", "data": "synthetic",
         "config": {"workload": f"{w.name} recipe: N={N} d={d} K={K} {w.x_dtype}; initial parameters; "
@@ -287,8 +310,7 @@ def kmeans_bench(args, w, torch, gmm, dev):
             ev[1].record()
         gmm.kmeans_update(Xd, assign, C, ws=ws)
 
-    for _ in range(args.warmup):
-        step()
+    warmup = warm_up(step, args, torch)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -301,7 +323,7 @@ def kmeans_bench(args, w, torch, gmm, dev):
     ach = flops / (a_ms * 1e-3) / 1e12
     out = {
         "metric": "k-means Lloyd iteration, points x centres/s", "value": N * K / (ms * 1e-3),
-        "unit": "points×centres/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "unit": "points×centres/s", "n_gpus": 1, "steps": args.steps, "warmup": warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32+f64", "data": "synthetic",
         "config": {"workload": f"{w.name} recipe: N={N} d={d} K={K} {w.x_dtype}; centres = the K initial means; "
@@ -319,7 +341,8 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 3 and at least 200 ms of them)")
     ap.add_argument("--workload", default="ref", choices=["tiny", "ref", "smallk", "largek", "ivf"])
     ap.add_argument("--cpu-rows", type=int, default=-1,
                     help="row cap for the oracle baseline (-1: as many as fit ~20 s, full N where possible; 0: skip)")
@@ -370,8 +393,7 @@ def main(argv=None):
         P.copy_(P0)
         gmm.em_iterate(Xd, mud, vard, lwd, 1, VAR_FLOOR, ws=ws)
 
-    for _ in range(args.warmup):
-        step()
+    warmup = warm_up(step, args, torch)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     for a, b in evs:  # materialise the events
@@ -425,7 +447,7 @@ def main(argv=None):
     }
     out = {
         "metric": METRIC, "value": N * K / (ms_step * 1e-3), "unit": UNIT, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "steps": args.steps, "warmup": warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32+bf16x3" if args.stats_precision == "split-bf16" else "f32",
         "data": "synthetic",
