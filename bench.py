@@ -154,6 +154,24 @@ def measured_peaks(torch, gmm, dev, reps: int = 5):
             best = max(best, rate)
         res[name] = round(best / (1e12 if "tflops" in name else 1e9), 1)
     del buf
+    # fp32 matrix and vector work alone, together in each wave, and in separate waves of one SIMD
+    co = torch.empty(1024 * 512, dtype=torch.float32, device=dev)
+    t = []
+    for mode in range(4):
+        gmm.peak_coissue(mode, 2000, 1024, co)  # warm-up
+        best = float("inf")
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            gmm.peak_coissue(mode, 20000, 1024, co)
+            b.record()
+            b.synchronize()
+            best = min(best, a.elapsed_time(b))
+        t.append(best)
+    res["coissue_ms"] = {"mfma_only": round(t[0], 3), "valu_only": round(t[1], 3), "both_per_wave": round(t[2], 3),
+                         "split_waves": round(t[3], 3),
+                         "both_per_wave_over_sum": round(t[2] / (t[0] + t[1]), 3),
+                         "split_waves_over_half_sum": round(t[3] / ((t[0] + t[1]) / 2), 3)}
     res["probes"] = ("gmm_peak_mfma: 2048 blocks x 4 waves, 8 independent MFMAs per trip (32x32x2 fp32 / "
                      "16x16x4 fp64); gmm_peak_hbm_read: 4 GiB read once, 16-byte loads, 2048 blocks x 256")
     return res

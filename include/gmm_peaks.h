@@ -42,6 +42,19 @@ double gmm_peak_mfma_flops(int32_t precision, int64_t trips, int32_t blocks);
  * written only in a case that does not arise in practice. */
 int gmm_peak_hbm_read(const void* buf, size_t bytes, int32_t blocks, uint32_t* out, void* stream);
 
+/* Co-issue probe: whether fp32 vector (VALU) work runs beside fp32
+ * matrix-core (MFMA) work on one SIMD, which decides whether the E-step
+ * kernels' row phases (max, exponentials, error bounds: VALU) can hide under
+ * their contractions (MFMA). `blocks` blocks of 512 threads (eight waves;
+ * with one block per CU, waves w and w + 4 share SIMD w % 4), each wave
+ * running `trips` trips. Per trip a matrix wave issues eight independent
+ * 32x32x2 fp32 MFMAs and a vector wave 128 independent fp32 FMAs. mode 0:
+ * matrix only; 1: vector only; 2: both in every wave; 3: waves 0-3 matrix,
+ * waves 4-7 vector. If the two kinds of work overlapped, modes 2 and 3
+ * would take about max(t0, t1) and max(t0, t1) / 2; serialised, t0 + t1 and
+ * (t0 + t1) / 2. out: device, blocks * 512 floats (written). */
+int gmm_peak_coissue(int32_t mode, int64_t trips, int32_t blocks, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -86,6 +86,51 @@ __global__ void __launch_bounds__(256) peak_hbm_read_kernel(const uint4* __restr
   if (acc == 0x9e3779b9u) out[blockIdx.x * (int64_t)blockDim.x + threadIdx.x] = acc;
 }
 
+// Co-issue probe: whether fp32 vector work runs beside fp32 matrix-core work
+// on a SIMD. Blocks of eight waves; with one block per CU (the registers
+// allow no more) waves w and w + 4 share SIMD w % 4. Per trip a wave that
+// does matrix work issues eight independent 32x32x2 fp32 MFMAs (eight
+// chains), and a wave that does vector work issues 128 independent fp32
+// FMAs (32 chains, four each), about the same SIMD time each. Modes: 0
+// matrix only, 1 vector only, 2 both in every wave (interleaved), 3 waves
+// 0-3 matrix only and waves 4-7 vector only.
+template <int MODE>
+__global__ void __launch_bounds__(512) peak_coissue_kernel(int64_t trips, float* __restrict__ out) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const bool mat = MODE == 0 || MODE == 2 || (MODE == 3 && wave < 4);
+  const bool vec = MODE == 1 || MODE == 2 || (MODE == 3 && wave >= 4);
+  v16f acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = 1.0f + 1e-3f * (float)i + 1e-7f * (float)tid;
+  const float a = 0.999f, b = 1e-6f;
+  float x = 1.0f + 1e-7f * (float)(tid & 63), y = 1.0f;
+#pragma unroll 1
+  for (int64_t t = 0; t < trips; ++t) {
+    if (mat) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, acc[i], 0, 0, 0);
+    }
+    if (vec) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(v[i], a, b);
+    }
+    x += 1e-9f;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][15];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) s += v[i];
+  out[blockIdx.x * (int64_t)blockDim.x + tid] = s;
+}
+
 }  // namespace gmm
 
 using namespace gmm;
@@ -113,6 +158,18 @@ int gmm_peak_hbm_read(const void* buf, size_t bytes, int32_t blocks, uint32_t* o
   if (!buf || !out || blocks < 1 || bytes < 16 || reinterpret_cast<uintptr_t>(buf) % 16 != 0) return -1;
   peak_hbm_read_kernel<<<blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const uint4*>(buf), (int64_t)(bytes / 16), out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int gmm_peak_coissue(int32_t mode, int64_t trips, int32_t blocks, float* out, void* stream) {
+  if (mode < 0 || mode > 3 || trips < 1 || blocks < 1 || !out) return -1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (mode) {
+    case 0: peak_coissue_kernel<0><<<blocks, 512, 0, s>>>(trips, out); break;
+    case 1: peak_coissue_kernel<1><<<blocks, 512, 0, s>>>(trips, out); break;
+    case 2: peak_coissue_kernel<2><<<blocks, 512, 0, s>>>(trips, out); break;
+    default: peak_coissue_kernel<3><<<blocks, 512, 0, s>>>(trips, out); break;
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -27,7 +27,7 @@ EXPORTS = (
     "gmm_border_lists", "gmm_border_lists_workspace_bytes",
     "gmm_kmeans_assign", "gmm_kmeans_update", "gmm_kmeans_iterate", "gmm_kmeans_workspace_bytes",
     "gmm_plan_info", "gmm_estep_stats_static",
-    "gmm_peak_mfma", "gmm_peak_mfma_flops", "gmm_peak_hbm_read",
+    "gmm_peak_mfma", "gmm_peak_mfma_flops", "gmm_peak_hbm_read", "gmm_peak_coissue",
 )
 PEAK_FP32, PEAK_FP64 = 0, 1
 
@@ -90,6 +90,8 @@ def _load() -> ctypes.CDLL:
     L.gmm_peak_mfma_flops.argtypes = [I32, I64, I32]
     L.gmm_peak_hbm_read.restype = ctypes.c_int
     L.gmm_peak_hbm_read.argtypes = [P, SZ, I32, P, P]
+    L.gmm_peak_coissue.restype = ctypes.c_int
+    L.gmm_peak_coissue.argtypes = [I32, I64, I32, P, P]
     L.gmm_estep_stats_static.restype = ctypes.c_int
     L.gmm_estep_stats_static.argtypes = [P, I32, I64, I32, P, P, P, I32, P, P, P, P, P, P]
     return L
@@ -389,3 +391,8 @@ def peak_hbm_read(buf: torch.Tensor, blocks: int, out: torch.Tensor) -> int:
     nbytes = buf.numel() * buf.element_size() // 16 * 16
     _check("gmm_peak_hbm_read", lib().gmm_peak_hbm_read(_ptr(buf), nbytes, blocks, _ptr(out), _stream(buf.device)))
     return nbytes
+
+
+def peak_coissue(mode: int, trips: int, blocks: int, out: torch.Tensor) -> None:
+    """Enqueues the co-issue probe (0 matrix only, 1 vector only, 2 both per wave, 3 split waves)."""
+    _check("gmm_peak_coissue", lib().gmm_peak_coissue(mode, trips, blocks, _ptr(out), _stream(out.device)))
