@@ -46,6 +46,8 @@ def test_peak_probes_validate_on_the_host(L):
     assert L.gmm_peak_hbm_read(None, 1 << 20, 4, FAKE, None) == -1
     assert L.gmm_peak_hbm_read(ctypes.c_void_p(0x100004), 1 << 20, 4, FAKE, None) == -1  # misaligned
     assert L.gmm_peak_hbm_read(FAKE, 8, 4, FAKE, None) == -1
+    for bad in ((-1, 10, 4, FAKE), (4, 10, 4, FAKE), (0, 0, 4, FAKE), (0, 10, 0, FAKE), (3, 10, 4, None)):
+        assert L.gmm_peak_coissue(*bad, None) == -1
 
 
 def test_version_and_error_strings(L):
