@@ -377,8 +377,9 @@ def main(argv=None):
                     help="time gmm_assign_top2 on the workload's X and initial parameters")
     ap.add_argument("--kmeans", action="store_true",
                     help="time Lloyd iterations of k-means on the workload's X with its K initial means as centres")
-    ap.add_argument("--stats-precision", default="fp32", choices=["fp32", "split-bf16"],
-                    help="statistics contraction (split-bf16: split products on the bf16 matrix cores)")
+    ap.add_argument("--stats-precision", default="auto", choices=["auto", "fp32", "split-bf16"],
+                    help="statistics contraction: auto (the library's default: fp32 products, exact fp16 "
+                         "splits in the second pass over half-precision X), fp32, or split-bf16 products")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this E-step build runs on a "
@@ -389,7 +390,8 @@ def main(argv=None):
     from soft_clustering_gmm_amd import datagen, gmm
     gmm.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
-    gmm.set_stats_precision(gmm.STATS_SPLIT_BF16 if args.stats_precision == "split-bf16" else gmm.STATS_FP32)
+    gmm.set_stats_precision({"auto": gmm.STATS_AUTO, "fp32": gmm.STATS_FP32,
+                             "split-bf16": gmm.STATS_SPLIT_BF16}[args.stats_precision])
 
     w = datagen.WORKLOADS[args.workload]
     if args.border_lists:
@@ -437,10 +439,13 @@ def main(argv=None):
     regime = "small-K" if small else "single-sweep" if single else "two-pass"
     ctype = {"f32": "float", "f16": "_Float16"}[w.x_dtype]
     sp = str(args.stats_precision == "split-bf16").lower()
+    # the second pass over half-precision X in the default mode: exact fp16 splits (rows with |x| < 15)
+    f16split = args.stats_precision == "auto" and regime == "two-pass" and w.x_dtype == "f16"
+    s2 = "2" if f16split else ("1" if sp == "true" else "0")
     kernel = (f"estep_small_kernel<{-(-d // 16)},{ctype},{sp}> (small K)" if small
-              else f"estep_stats_kernel<{-(-d // 32)},0,{ctype},{sp}> (single sweep)" if single
-              else f"estep_stats_kernel<{-(-d // 32)},2,{ctype},false> + lse_merge_kernel + estep_lse_kernel "
-                   f"(fallback rows) + estep_stats_kernel<{-(-d // 32)},1,{ctype},{sp}> (two-pass)")
+              else f"estep_stats_kernel<{-(-d // 32)},0,{ctype},{int(sp == 'true')}> (single sweep)" if single
+              else f"estep_stats_kernel<{-(-d // 32)},2,{ctype},0> + lse_merge_kernel + estep_lse_kernel "
+                   f"(fallback rows) + estep_stats_kernel<{-(-d // 32)},1,{ctype},{s2}> (two-pass)")
     ctr = committed_counters(args.workload, args.stats_precision)
     executed = ctr.get("executed_flops_per_launch")
     roof = {
@@ -467,7 +472,8 @@ def main(argv=None):
         "metric": METRIC, "value": N * K / (ms_step * 1e-3), "unit": UNIT, "n_gpus": 1,
         "steps": args.steps, "warmup": warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32+bf16x3" if args.stats_precision == "split-bf16" else "f32",
+        "dtype": ("f32+bf16x3" if args.stats_precision == "split-bf16" else
+                  "f32+f16x2" if f16split else "f32"),
         "data": "synthetic",
         "config": {"workload": f"{w.name}: N={N} d={d} K={K} {w.x_dtype} Gaussian blobs (seed {w.seed}); "
                                f"step = one EM iteration from the initial parameters (precompute, fused E-step+stats, "

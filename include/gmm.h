@@ -179,23 +179,36 @@ int gmm_plan_info(int64_t N, int32_t d, int32_t K, int32_t regime, int64_t* info
 int gmm_set_timing_events(void* start, void* stop);
 
 /* Precision of the statistics contraction (Nk, Sx, Sxx = sums of r * [1, x,
- * x^2]) of the fused E-step kernels, in every regime. The pages measure their
- * kernels with half-precision data ("Flash-KMeans" article, test setup); this
- * option moves that contraction onto the bf16 matrix cores instead:
- *   GMM_STATS_FP32      - fp32 MFMA products (default);
+ * x^2]) of the fused E-step kernels. The pages measure their kernels with
+ * half-precision data ("Flash-KMeans" article, test setup); these modes move
+ * that contraction onto the bf16 or fp16 matrix cores where it pays:
+ *   GMM_STATS_AUTO      - (default) as GMM_STATS_FP32, except that the second
+ *                          pass of the two-pass regime takes exact fp16
+ *                          splits when X is IEEE half: x is exact in fp16,
+ *                          (16 x)^2 splits exactly into two fp16 values, and
+ *                          2^10 r = hi + lo + d with |d| <= 2^-22 of it, so
+ *                          each product is off by <= 2^-21 relative (plus
+ *                          2^-35 |x| or x^2 absolute for r < 2^-13) before
+ *                          the fp32 accumulation, close to fp32 products. A
+ *                          16-point block with any |x| >= 15 takes fp32
+ *                          products instead;
+ *   GMM_STATS_FP32      - fp32 MFMA products everywhere;
  *   GMM_STATS_SPLIT_BF16 - every fp32 operand v is split as v = hi + lo + d
  *                          with hi = bf16(v), lo = bf16(v - hi), |d| <=
  *                          2^-16 |v|, and a*b is taken as hi*hi + hi*lo +
  *                          lo*hi, exact products accumulated in fp32: each
  *                          product is off by <= 3.0001 * 2^-16 |a b| (4.6e-5
  *                          relative) before the accumulation's rounding,
- *                          inside the 1e-4 bar on the statistics.
- * Scores, responsibilities, l_n and L are unchanged (fp32 MFMA scores with the
- * exact re-score). The setting is process-wide and read when an E-step is
- * enqueued (gmm_estep_stats*, gmm_estep_resp, gmm_em_iterate). Returns GMM_OK,
- * or GMM_EINVAL for an unknown mode (setting unchanged). Not synchronised with
- * calls enqueued concurrently from other threads. */
-enum gmm_stats_precision { GMM_STATS_FP32 = 0, GMM_STATS_SPLIT_BF16 = 1 };
+ *                          inside the 1e-4 bar on the statistics. The
+ *                          variance an M-step forms from them, Sxx/Nk - mu^2,
+ *                          then carries up to 4.6e-5 (mu^2 + var) of absolute
+ *                          error.
+ * Scores, responsibilities, l_n and L are the same in every mode (fp32 MFMA
+ * scores with the exact re-score). The setting is process-wide and read when
+ * an E-step is enqueued (gmm_estep_stats*, gmm_estep_resp, gmm_em_iterate).
+ * Returns GMM_OK, or GMM_EINVAL for an unknown mode (setting unchanged). Not
+ * synchronised with calls enqueued concurrently from other threads. */
+enum gmm_stats_precision { GMM_STATS_FP32 = 0, GMM_STATS_SPLIT_BF16 = 1, GMM_STATS_AUTO = 2 };
 int gmm_set_stats_precision(int32_t mode);
 
 /* Top-2 assignment for border-vector multi-assignment (Flash-GMM abstract:

@@ -16,8 +16,8 @@
 
 namespace gmm {
 
-// Statistics contraction of the small-K kernel (gmm_set_stats_precision).
-static std::atomic<int> g_stats_precision{GMM_STATS_FP32};
+// Statistics contraction of the fused kernels (gmm_set_stats_precision).
+static std::atomic<int> g_stats_precision{GMM_STATS_AUTO};
 
 // Scratch of the allocation-free E-step (gmm_estep_stats_static): one array
 // per GPU, allocated with the code object and held until the process ends.
@@ -113,7 +113,9 @@ static int make_plan_impl(int64_t N, int d, int K, int regime, void* base, Plan*
   }
   p.Kp16 = (int)ceil_div(K, 16) * 16;
   p.E = 1 + 2 * p.DP;
-  p.stats_split = g_stats_precision.load(std::memory_order_relaxed) == GMM_STATS_SPLIT_BF16;
+  const int sp = g_stats_precision.load(std::memory_order_relaxed);
+  p.stats_split = sp == GMM_STATS_SPLIT_BF16;
+  p.stats_f16 = sp == GMM_STATS_AUTO;
   p.pass1 = regime == GMM_REGIME_TWOPASS && records;
   p.drop_rho = (float)(std::ldexp(1.0, -20) / (double)std::max<int64_t>(N, 1));
 
@@ -146,7 +148,7 @@ static int make_plan_impl(int64_t N, int d, int K, int regime, void* base, Plan*
   const size_t o_rowE = take(p.pass1 ? n1 * sizeof(float) : 0);
   const size_t o_lrow = take(p.pass1 ? n1 * sizeof(double) : 0);
   const size_t o_fbl = take(p.pass1 ? n1 * sizeof(int32_t) : 0);
-  const size_t o_fbc = take(p.pass1 ? sizeof(int32_t) : 0);
+  const size_t o_fbc = take(p.pass1 ? 2 * sizeof(int32_t) : 0);  // fbcount, xflag
   const size_t o_rsq = take(p.pass1 ? n1 * sizeof(float) : 0);
   const size_t o_slist = take(nrec * sizeof(int32_t));
   const size_t nst = p.pass1 ? (size_t)p.kslabs * std::max<int64_t>(p.tiles, 1) : 0;
@@ -185,6 +187,7 @@ static int make_plan_impl(int64_t N, int d, int K, int regime, void* base, Plan*
     p.ws.lrow = p.pass1 ? reinterpret_cast<double*>(b + o_lrow) : nullptr;
     p.ws.fblist = p.pass1 ? reinterpret_cast<int32_t*>(b + o_fbl) : nullptr;
     p.ws.fbcount = p.pass1 ? reinterpret_cast<int32_t*>(b + o_fbc) : nullptr;
+    p.ws.xflag = p.pass1 ? reinterpret_cast<int32_t*>(b + o_fbc) + 1 : nullptr;
     p.ws.rowSq = p.pass1 ? reinterpret_cast<float*>(b + o_rsq) : nullptr;
     p.ws.slist = p.pass1 ? reinterpret_cast<int32_t*>(b + o_slist) : nullptr;
     p.ws.smask = p.pass1 ? reinterpret_cast<uint64_t*>(b + o_smask) : nullptr;
@@ -622,7 +625,7 @@ int gmm_plan_info(int64_t N, int32_t d, int32_t K, int32_t regime, int64_t* info
 }
 
 int gmm_set_stats_precision(int32_t mode) {
-  if (mode != GMM_STATS_FP32 && mode != GMM_STATS_SPLIT_BF16) return GMM_EINVAL;
+  if (mode != GMM_STATS_FP32 && mode != GMM_STATS_SPLIT_BF16 && mode != GMM_STATS_AUTO) return GMM_EINVAL;
   g_stats_precision.store(mode, std::memory_order_relaxed);
   return GMM_OK;
 }

@@ -44,6 +44,7 @@ struct Workspace {
   double* lrow;     // [N] per-row l_n (natural), before the block sums
   int32_t* fblist;  // [N] rows whose normaliser needs the fp64 pass
   int32_t* fbcount; // [1] number of such rows
+  int32_t* xflag;   // [1] (beside fbcount) set when some row's |x|^2 >= 225 (xrange_kernel)
   // row lists of the second pass (two-pass regime, Plan::pass1):
   float* rowSq;     // [N] |x|^2 of each row (fp32, from the first pass)
   int32_t* slist;   // [kslabs][N] per slab, in increasing order, the rows it keeps
@@ -72,6 +73,7 @@ struct Plan {
   int64_t tiles;    // ceil(N / 64)
   int E;            // 1 + 2*DP floats per component in a partial
   int stats_split;  // statistics contraction as split-bf16 products on the bf16 MFMA
+  int stats_f16;    // half-precision X: the second pass's statistics as exact fp16 splits
   int pass1;        // two-pass regime with the fp32 first pass (its record regions are laid out)
   float drop_rho;   // statistics skip threshold rho = 2^-20 / (rows of the whole E-step)
   size_t bytes;     // workspace bytes this plan uses

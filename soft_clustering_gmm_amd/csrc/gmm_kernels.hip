@@ -46,6 +46,7 @@
 #include "gmm_internal.hpp"
 
 #include <atomic>
+#include <type_traits>
 #include <algorithm>
 #include <limits.h>
 #include <math.h>
@@ -56,6 +57,7 @@ typedef float v32f __attribute__((ext_vector_type(32)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 constexpr double kLog2Pi = 1.83787706640934548356065947281;
@@ -551,7 +553,7 @@ struct Pass1Out {
 // components), 0 when it comes from `waves_rt`. With it fixed, the row
 // phase's cross-lane reductions over a row's threads compile to straight DPP
 // sequences instead of branches on the thread count.
-template <int DT, int MODE, typename XT, bool SPLIT, int WV>
+template <int DT, int MODE, typename XT, int SPLIT, int WV>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 4 : 1)))
 estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, int waves_rt, int kslabs,
                    int64_t rows_per_chunk, const float4* __restrict__ W32p, const float* __restrict__ c32,
@@ -560,8 +562,11 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
                    const float4* __restrict__ rowref, float* __restrict__ partials,
                    double* __restrict__ llpart, float* __restrict__ ll_point, float* __restrict__ R,
                    Pass1Out p1, float rho, const int32_t* __restrict__ slab_rows,
-                   const int32_t* __restrict__ slab_len, int vec) {
+                   const int32_t* __restrict__ slab_len, const int32_t* __restrict__ xflag, int vec) {
   constexpr int DP = 32 * DT, Q = DP / 4, XS = DP + 4, E = 1 + 2 * DP;
+  // The fp16-split second pass (SPLIT 2) and its fp32 twin are launched
+  // together; *xflag (xrange_kernel) decides which one does the work.
+  if (xflag && ((SPLIT == 2) == (*xflag != 0))) return;
   extern __shared__ __align__(16) float smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
   const int waves = WV ? WV : waves_rt;
@@ -913,7 +918,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       // belongs to wave (i * waves) / 8. The bits are taken from the fp32
       // responsibilities, before the re-score (which moves an entry by a
       // factor within 1 +- 2E); rows past the end take none (their r is zero).
-      if constexpr (!SPLIT && MODE == 0) {
+      if constexpr (SPLIT == 0 && MODE == 0) {
         uint32_t nzb = 0;
         const float wthr = rho / fmaxf(1.f, sq) * (float)z;
 #pragma unroll
@@ -1097,7 +1102,7 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       }
     if constexpr (MODE == 2) {
       // the first pass accumulates no statistics
-    } else if constexpr (SPLIT) {
+    } else if constexpr (SPLIT == 1) {
       // Split-bf16 products on the 32x32x16 bf16 MFMA (see the small-K
       // kernel for the error of a product): block pb covers points
       // 16 pb + 8 h + t (t < 8) of lane (h, c), r of component c as the A
@@ -1135,6 +1140,50 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
           SXX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rh, ql, SXX[t2], 0, 0, 0);
           SX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rl, xh, SX[t2], 0, 0, 0);
           SXX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rl, qh, SXX[t2], 0, 0, 0);
+        }
+      }
+    } else if constexpr (SPLIT == 2) {
+      // Half-precision X (second pass): exact fp16 splits on the 32x32x16 f16
+      // MFMA, in the lane layout of the bf16 path. x is exact in fp16; q =
+      // (16 x)^2 is exact in fp32 (22 significant bits) and is q_hi + q_lo
+      // with two fp16 values, exactly while q_lo is a normal fp16 (|x| >=
+      // 0.022; below, q_lo is within 2^-25 of its part); r' = 2^10 r is r_hi
+      // + r_lo + d with |d| <= 2^-22 r' (2^-25 absolute where r_lo is
+      // subnormal, r < 2^-13). Sx takes r_hi x + r_lo x and Sxx r_hi q_hi +
+      // r_hi q_lo + r_lo q_hi, products exact in fp32: per term at most 2^-22
+      // (Sx) and 2^-21 (Sxx) relative, plus 2^-35 |x| and 2^-35 x^2
+      // absolute, before the fp32 accumulation. The partial is scaled back by
+      // 2^-10 and 2^-18 (exact). This variant runs only when every listed
+      // row has |x|^2 < 225 (so |x| < 15 and q stays in the fp16 range); the
+      // plain fp32 second pass is launched beside it and runs otherwise
+      // (`xflag`).
+#pragma unroll 1
+      for (int pb = 0; pb < 4; ++pb) {
+        v8h rh, rl;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float e = sc[(16 * pb + 8 * h + t) * SCS + wave * 32 + c];
+          nk += e;
+          const float rs = e * 1024.f;
+          rh[t] = (_Float16)rs;
+          rl[t] = (_Float16)(rs - (float)rh[t]);
+        }
+#pragma unroll
+        for (int t2 = 0; t2 < DT; ++t2) {
+          v8h xh, qh, ql;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float x = xs[(16 * pb + 8 * h + t) * XS + DT * c + t2];
+            const float q = (16.f * x) * (16.f * x);
+            xh[t] = (_Float16)x;
+            qh[t] = (_Float16)q;
+            ql[t] = (_Float16)(q - (float)qh[t]);
+          }
+          SX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rh, xh, SX[t2], 0, 0, 0);
+          SXX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rh, qh, SXX[t2], 0, 0, 0);
+          SX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rl, xh, SX[t2], 0, 0, 0);
+          SXX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rh, ql, SXX[t2], 0, 0, 0);
+          SXX[t2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rl, qh, SXX[t2], 0, 0, 0);
         }
       }
     } else if constexpr (MODE == 1) {
@@ -1280,8 +1329,11 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
     for (int j = 0; j < 16; ++j) {
       const int comp = kw + acc_row(h, j);
       const int f = DT * c + t;
-      part[(size_t)comp * E + 1 + f] = (SPLIT || MODE == 1) ? SX[t][j] : S2[t][j];
-      part[(size_t)comp * E + 1 + DP + f] = (SPLIT || MODE == 1) ? SXX[t][j] : S2[t][16 + j];
+      // (the fp16 split path accumulated 2^10 r x and 2^18 r x^2)
+      part[(size_t)comp * E + 1 + f] =
+          SPLIT == 2 ? SX[t][j] * 0x1p-10f : (SPLIT || MODE == 1) ? SX[t][j] : S2[t][j];
+      part[(size_t)comp * E + 1 + DP + f] =
+          SPLIT == 2 ? SXX[t][j] * 0x1p-18f : (SPLIT || MODE == 1) ? SXX[t][j] : S2[t][16 + j];
     }
   // the halves of the split path and of the second pass saw different points;
   // those of the single sweep's one-point form the same ones
@@ -2783,11 +2835,21 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
                                      (size_t)nthr * sizeof(double) +
                                      (size_t)(p.waves * kRefCap + 64) * sizeof(uint32_t);
   const bool split = p.stats_split && MODE != 2;
-  auto fn = p.waves == 8 ? (split ? estep_stats_kernel<DT, MODE, XT, true, 8> : estep_stats_kernel<DT, MODE, XT, false, 8>)
-                         : (split ? estep_stats_kernel<DT, MODE, XT, true, 0> : estep_stats_kernel<DT, MODE, XT, false, 0>);
+  // exact fp16 splits of the second pass's statistics for half-precision X
+  constexpr bool kF16 = MODE == 1 && std::is_same<XT, _Float16>::value;
+  const bool f16 = kF16 && p.stats_f16 && !split;
+  auto fn = p.waves == 8 ? (split ? estep_stats_kernel<DT, MODE, XT, 1, 8> : estep_stats_kernel<DT, MODE, XT, 0, 8>)
+                         : (split ? estep_stats_kernel<DT, MODE, XT, 1, 0> : estep_stats_kernel<DT, MODE, XT, 0, 0>);
+  auto fn16 = fn;
+  if constexpr (kF16)
+    fn16 = p.waves == 8 ? estep_stats_kernel<DT, MODE, XT, 2, 8> : estep_stats_kernel<DT, MODE, XT, 2, 0>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
+  if (f16) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn16), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   // The first pass accumulates nothing per chunk, so its chunks are cut for
   // one round of resident blocks (two per CU, 256 CUs): 8 * floor(64 /
   // slabs) chunks.
@@ -2804,10 +2866,18 @@ static hipError_t run_stats(const Plan& p, const XT* X, const float* mu, float* 
   const Pass1Out p1{w.p1h, w.p1v, w.p1k, w.rowE, w.rowSq};
   // the second pass walks the slabs' row lists, except when it also writes R
   const bool lists = MODE == 1 && p.pass1 && !R;
+  // with f16: the fp16-split variant, then the fp32 one; each returns at
+  // once unless the first pass's |x|^2 records select it
+  const int32_t* xf = f16 ? w.xflag : nullptr;
+  if (f16)
+    fn16<<<grid, nthr, lds, stream>>>(X, p.N, p.d, p.K, p.Kp, p.waves, p.kslabs, rpc,
+                                      reinterpret_cast<const float4*>(w.W32p), w.c32, w.mup, w.ivp, w.c64d, w.errc,
+                                      w.rowref, w.partials, w.llpart, ll_point, R, p1, p.drop_rho,
+                                      lists ? w.slist : nullptr, lists ? w.slen : nullptr, xf, vec);
   fn<<<grid, nthr, lds, stream>>>(X, p.N, p.d, p.K, p.Kp, p.waves, p.kslabs, rpc,
                                   reinterpret_cast<const float4*>(w.W32p), w.c32, w.mup, w.ivp, w.c64d, w.errc,
                                   w.rowref, w.partials, w.llpart, ll_point, R, p1, p.drop_rho,
-                                  lists ? w.slist : nullptr, lists ? w.slen : nullptr, vec);
+                                  lists ? w.slist : nullptr, lists ? w.slen : nullptr, xf, vec);
   return hipGetLastError();
 }
 
@@ -2834,6 +2904,18 @@ static hipError_t run_lse(const Plan& p, const XT* X, int32_t* idx, float* resp,
   return hipGetLastError();
 }
 
+// Sets *flag when some row's |x|^2, as the fp32 first pass recorded it, is at
+// least 225 (or not a number): then some |x_j| may reach 15, where the fp16
+// split of (16 x)^2 would leave the fp16 range. (Each record is a sum of
+// nonnegative rounded squares, so it is at least every x_j^2 of its row.)
+__global__ void __launch_bounds__(256) xrange_kernel(const float* __restrict__ rowSq, int64_t N,
+                                                     int32_t* __restrict__ flag) {
+  int out = 0;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < N; i += (int64_t)gridDim.x * blockDim.x)
+    out |= !(rowSq[i] < 225.f);
+  if (__syncthreads_or(out) && threadIdx.x == 0) atomicOr(flag, 1);
+}
+
 // Normalisers of the two-pass regime: the fp32 first pass, the merge of its
 // records per row, the fp64 fallback for the rows the merge lists, and the
 // per-tile log-likelihood sums.
@@ -2841,7 +2923,7 @@ template <int DT, typename XT>
 static hipError_t run_normalisers(const Plan& p, const XT* X, const float* mu, float* ll_point,
                                   hipStream_t stream) {
   const Workspace& w = p.ws;
-  fill_int_kernel<<<1, 64, 0, stream>>>(w.fbcount, 1, 0);
+  fill_int_kernel<<<1, 64, 0, stream>>>(w.fbcount, 2, 0);  // fbcount and xflag
   hipError_t e = run_stats<DT, 2>(p, X, mu, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
   // the merge reads X rows four values at a time when d % 4 == 0 and the
@@ -2853,6 +2935,9 @@ static hipError_t run_normalisers(const Plan& p, const XT* X, const float* mu, f
   e = run_lse<DT, false>(p, X, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
   row_ll_sum_kernel<<<(unsigned)ll_parts(p), 256, 0, stream>>>(w.lrow, p.N, ll_point, w.llpart);
+  // whether half-precision X stays in the fp16 split's range (every |x| < 15)
+  if (sizeof(XT) == 2 && p.stats_f16 && !p.stats_split)
+    xrange_kernel<<<256, 256, 0, stream>>>(w.rowSq, p.N, w.xflag);
   // the second pass's row lists
   const dim3 tg((unsigned)p.tiles, (unsigned)p.kslabs), sg((unsigned)kSlabSegs, (unsigned)p.kslabs);
   slab_keep_kernel<<<tg, 64, 0, stream>>>(w.p1h, w.rowref, w.rowSq, p.N, p.tiles, p.drop_rho, w.smask, w.soff);

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libgmm_mi355x.so")
 
 GMM_F32, GMM_F16, GMM_BF16 = 0, 1, 2
 REGIME_AUTO, REGIME_SINGLE, REGIME_TWOPASS, REGIME_SMALLK = 0, 1, 2, 3
-STATS_FP32, STATS_SPLIT_BF16 = 0, 1
+STATS_FP32, STATS_SPLIT_BF16, STATS_AUTO = 0, 1, 2  # STATS_AUTO is the default
 
 EXPORTS = (
     "gmm_version", "gmm_error_string", "gmm_workspace_bytes", "gmm_estep_stats",
@@ -292,7 +292,8 @@ def set_timing_events(start, stop) -> None:
 
 def set_stats_precision(mode: int) -> None:
     """Statistics contraction of the fused E-step kernels, process-wide:
-    STATS_FP32 (default) or STATS_SPLIT_BF16 (split-bf16 products)."""
+    STATS_AUTO (default: fp32 products, exact fp16 splits in the second pass over half-precision X),
+    STATS_FP32 or STATS_SPLIT_BF16 (split-bf16 products)."""
     _check("gmm_set_stats_precision", lib().gmm_set_stats_precision(int(mode)))
 
 

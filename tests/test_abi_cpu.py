@@ -63,6 +63,7 @@ def test_stats_precision_setting(L):
     assert L.gmm_set_stats_precision(-1) == -1
     assert L.gmm_set_stats_precision(1) == 0
     assert L.gmm_set_stats_precision(0) == 0
+    assert L.gmm_set_stats_precision(2) == 0  # the default (auto) mode
 
 
 def test_workspace_bytes(L):

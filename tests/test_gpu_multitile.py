@@ -35,9 +35,9 @@ torch = pytest.importorskip("torch")
 def G():
     from soft_clustering_gmm_amd import gmm
     gmm.lib()
-    gmm.set_stats_precision(gmm.STATS_FP32)
+    gmm.set_stats_precision(gmm.STATS_AUTO)  # the library's default
     yield gmm
-    gmm.set_stats_precision(gmm.STATS_FP32)
+    gmm.set_stats_precision(gmm.STATS_AUTO)
 
 
 def dev(a):
@@ -71,9 +71,9 @@ def _check_case(G, Xd, Xv, mu, var, logw, regime, what, min_tiles, split=(False,
     l_rows, R_rows = oracle.estep_rows(Xv, mu, var, logw, rows)
     args = (Xd, dev(mu), dev(var), dev(logw))
     l_fp32 = None
-    for sp in split:
-        G.set_stats_precision(G.STATS_SPLIT_BF16 if sp else G.STATS_FP32)
-        tag = f"{what} {'split-bf16' if sp else 'fp32'}"
+    for sp in split:  # False: fp32 products, True: split-bf16, "auto": the default mode
+        G.set_stats_precision({False: G.STATS_FP32, True: G.STATS_SPLIT_BF16, "auto": G.STATS_AUTO}[sp])
+        tag = f"{what} {'split-bf16' if sp is True else 'auto' if sp == 'auto' else 'fp32'}"
         Nk, Sx, Sxx, L, lp = G.estep_stats(*args, regime=regime, want_point_loglik=True)
         torch.cuda.synchronize()
         es = parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, None, ref["absx"], tag)
@@ -92,7 +92,7 @@ def _check_case(G, Xd, Xv, mu, var, logw, regime, what, min_tiles, split=(False,
             er = float("nan")
         print(f"{tag}: stats {es[0]:.1e}/{es[1]:.1e}/{es[2]:.1e}  l_n {el:.1e}  sampled |dr| {er:.1e}",
               flush=True)
-        G.set_stats_precision(G.STATS_FP32)
+        G.set_stats_precision(G.STATS_AUTO)
     return ref
 
 
@@ -107,10 +107,11 @@ def test_two_pass_fp32_many_tiles(G, scale):
 
 def test_two_pass_fp16_prefetch_many_tiles(G):
     """ivf recipe at N = 131072, X in fp16: 4 slabs, 32 tiles per block, the
-    half-precision register prefetch of the next tile."""
+    half-precision register prefetch of the next tile; statistics as fp32
+    products, split-bf16 products and (the default) exact fp16 splits."""
     X, mu, var, logw = datagen.make_workload("ivf", N=131072)
     Xd, Xv = _xdev(X, "f16")
-    _check_case(G, Xd, Xv, mu, var, logw, 2, "ivf fp16", 16, split=(False, True))
+    _check_case(G, Xd, Xv, mu, var, logw, 2, "ivf fp16", 16, split=(False, True, "auto"))
 
 
 @pytest.mark.parametrize("xkind", ["bf16", "f16", "f32"])

@@ -24,7 +24,7 @@ def G():
     from soft_clustering_gmm_amd import gmm
     gmm.lib()
     yield gmm
-    gmm.set_stats_precision(gmm.STATS_FP32)
+    gmm.set_stats_precision(gmm.STATS_AUTO)  # back to the library's default
 
 
 def dev(a):
