@@ -189,9 +189,11 @@ int gmm_set_timing_events(void* start, void* stop);
  *                          2^10 r = hi + lo + d with |d| <= 2^-22 of it, so
  *                          each product is off by <= 2^-21 relative (plus
  *                          2^-35 |x| or x^2 absolute for r < 2^-13) before
- *                          the fp32 accumulation, close to fp32 products. A
- *                          16-point block with any |x| >= 15 takes fp32
- *                          products instead;
+ *                          the fp32 accumulation, close to fp32 products.
+ *                          When some row has |x|^2 >= 225 (as the first pass
+ *                          records it; then some |x_j| may reach 15 and
+ *                          (16 x)^2 leave the fp16 range), the whole second
+ *                          pass takes fp32 products instead;
  *   GMM_STATS_FP32      - fp32 MFMA products everywhere;
  *   GMM_STATS_SPLIT_BF16 - every fp32 operand v is split as v = hi + lo + d
  *                          with hi = bf16(v), lo = bf16(v - hi), |d| <=

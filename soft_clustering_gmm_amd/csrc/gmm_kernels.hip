@@ -1153,8 +1153,8 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       // r_hi q_lo + r_lo q_hi, products exact in fp32: per term at most 2^-22
       // (Sx) and 2^-21 (Sxx) relative, plus 2^-35 |x| and 2^-35 x^2
       // absolute, before the fp32 accumulation. The partial is scaled back by
-      // 2^-10 and 2^-18 (exact). This variant runs only when every listed
-      // row has |x|^2 < 225 (so |x| < 15 and q stays in the fp16 range); the
+      // 2^-10 and 2^-18 (exact). This variant runs only when every row has
+      // |x|^2 < 225 (so every |x| < 15 and q stays in the fp16 range); the
       // plain fp32 second pass is launched beside it and runs otherwise
       // (`xflag`).
 #pragma unroll 1

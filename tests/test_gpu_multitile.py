@@ -168,3 +168,27 @@ def test_ivf_em_teacher_forced_many_tiles(G):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(h2), hist)
     assert torch.equal(mu2, mud) and torch.equal(var2, vard) and torch.equal(lw2, lwd)
+
+
+def test_two_pass_fp16_out_of_range_takes_fp32_products(G):
+    """Half-precision X with rows of |x|^2 >= 225, where the fp16 split of (16 x)^2
+    is not known to stay in the fp16 range: the default mode's second pass must hand
+    the statistics to its fp32 twin, so that everything is bitwise what
+    GMM_STATS_FP32 gives, and meets the oracle. (ivf recipe at N = 32768 scaled by
+    20, so |x|^2 = 400 on every row; variances by 400.)"""
+    X, mu, var, logw = datagen.make_workload("ivf", N=32768)
+    X20 = (X.astype(np.float32) * 20.0).astype(np.float16)
+    assert (X20.astype(np.float64) ** 2).sum(axis=1).max() >= 225.0
+    mu20, var20 = (mu * 20.0).astype(np.float32), (var * 400.0).astype(np.float32)
+    Xd, Xv = dev(X20), X20.astype(np.float32)
+    args = (Xd, dev(mu20), dev(var20), dev(logw))
+    G.set_stats_precision(G.STATS_AUTO)
+    a = G.estep_stats(*args, regime=2, want_point_loglik=True)
+    G.set_stats_precision(G.STATS_FP32)
+    b = G.estep_stats(*args, regime=2, want_point_loglik=True)
+    torch.cuda.synchronize()
+    for i, key in enumerate(("Nk", "Sx", "Sxx", "L", "l_n")):
+        assert torch.equal(a[i], b[i]), f"out-of-range fp16 X: {key} differs from the fp32 products"
+    ref = oracle.estep(Xv, mu20, var20, logw, form="expanded", row_chunk=4096, abs_x=True)
+    parity.check_stats((host(a[0]), host(a[1]), host(a[2])), ref, None, ref["absx"], "out-of-range fp16 X")
+    parity.check_total(host(a[3]), ref, "out-of-range fp16 X")
