@@ -185,11 +185,14 @@ int gmm_set_timing_events(void* start, void* stop);
  *   GMM_STATS_AUTO      - (default) as GMM_STATS_FP32, except that the second
  *                          pass of the two-pass regime takes exact fp16
  *                          splits when X is IEEE half: x is exact in fp16,
- *                          (16 x)^2 splits exactly into two fp16 values, and
- *                          2^10 r = hi + lo + d with |d| <= 2^-22 of it, so
- *                          each product is off by <= 2^-21 relative (plus
- *                          2^-35 |x| or x^2 absolute for r < 2^-13) before
- *                          the fp32 accumulation, close to fp32 products.
+ *                          (16 x)^2 splits exactly into two fp16 values for
+ *                          |x| >= 2^-6 (within 2^-25 below), and 2^10 r =
+ *                          hi + lo + d with |d| <= max(2^-22 of it, 2^-25),
+ *                          so each product is off by <= 2^-21 relative, plus
+ *                          2^-35 |x| or 2^-35 x^2 + 2^-68 absolute, plus
+ *                          2^-33 r on an Sxx term with |x| < 2^-6, before
+ *                          the fp32 accumulation: close to fp32 products
+ *                          except for the absolute floor on tiny features.
  *                          When some row has |x|^2 >= 225 (as the first pass
  *                          records it; then some |x_j| may reach 15 and
  *                          (16 x)^2 leave the fp16 range), the whole second

@@ -1144,16 +1144,15 @@ estep_stats_kernel(const XT* __restrict__ X, int64_t N, int d, int K, int Kp, in
       }
     } else if constexpr (SPLIT == 2) {
       // Half-precision X (second pass): exact fp16 splits on the 32x32x16 f16
-      // MFMA, in the lane layout of the bf16 path. x is exact in fp16; q =
-      // (16 x)^2 is exact in fp32 (22 significant bits) and is q_hi + q_lo
-      // with two fp16 values, exactly while q_lo is a normal fp16 (|x| >=
-      // 0.022; below, q_lo is within 2^-25 of its part); r' = 2^10 r is r_hi
-      // + r_lo + d with |d| <= 2^-22 r' (2^-25 absolute where r_lo is
-      // subnormal, r < 2^-13). Sx takes r_hi x + r_lo x and Sxx r_hi q_hi +
-      // r_hi q_lo + r_lo q_hi, products exact in fp32: per term at most 2^-22
-      // (Sx) and 2^-21 (Sxx) relative, plus 2^-35 |x| and 2^-35 x^2
-      // absolute, before the fp32 accumulation. The partial is scaled back by
-      // 2^-10 and 2^-18 (exact). This variant runs only when every row has
+      // MFMA (which keeps fp16 subnormal inputs), in the lane layout of the
+      // bf16 path. x is exact in fp16; q = (16 x)^2 is exact in fp32 (22
+      // significant bits) and equals q_hi + q_lo, two fp16 values, for |x| >=
+      // 2^-6 (below, within 2^-25); r' = 2^10 r is r_hi + r_lo + d with |d|
+      // <= max(2^-22 r', 2^-25). Sx takes r_hi x + r_lo x and Sxx r_hi q_hi +
+      // r_hi q_lo + r_lo q_hi, products exact in fp32: per term Sx is off by
+      // at most 2^-22 r|x| + 2^-35 |x| and Sxx by 2^-21 r x^2 + 2^-35 x^2 +
+      // 2^-68, plus 2^-33 r where |x| < 2^-6, before the fp32 accumulation.
+      // The partial is scaled back by 2^-10 and 2^-18 (exact). This variant runs only when every row has
       // |x|^2 < 225 (so every |x| < 15 and q stays in the fp16 range); the
       // plain fp32 second pass is launched beside it and runs otherwise
       // (`xflag`).
