@@ -2934,8 +2934,9 @@ static hipError_t run_normalisers(const Plan& p, const XT* X, const float* mu, f
   e = run_lse<DT, false>(p, X, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
   row_ll_sum_kernel<<<(unsigned)ll_parts(p), 256, 0, stream>>>(w.lrow, p.N, ll_point, w.llpart);
-  // whether half-precision X stays in the fp16 split's range (every |x| < 15)
-  if (sizeof(XT) == 2 && p.stats_f16 && !p.stats_split)
+  // whether IEEE-half X stays in the fp16 split's range (every |x| < 15);
+  // bfloat16 X never takes the fp16 split
+  if (std::is_same<XT, _Float16>::value && p.stats_f16 && !p.stats_split)
     xrange_kernel<<<256, 256, 0, stream>>>(w.rowSq, p.N, w.xflag);
   // the second pass's row lists
   const dim3 tg((unsigned)p.tiles, (unsigned)p.kslabs), sg((unsigned)kSlabSegs, (unsigned)p.kslabs);
