@@ -192,3 +192,33 @@ def test_two_pass_fp16_out_of_range_takes_fp32_products(G):
     ref = oracle.estep(Xv, mu20, var20, logw, form="expanded", row_chunk=4096, abs_x=True)
     parity.check_stats((host(a[0]), host(a[1]), host(a[2])), ref, None, ref["absx"], "out-of-range fp16 X")
     parity.check_total(host(a[3]), ref, "out-of-range fp16 X")
+
+
+@pytest.mark.parametrize("N,d,K,scale", [(1001, 37, 300, 0.25), (65, 1, 257, 1.0), (700, 64, 520, 0.25),
+                                         (129, 96, 1024, 0.25), (2000, 40, 300, 2.0 ** -8)])
+def test_two_pass_fp16_edge_shapes(G, N, d, K, scale):
+    """Half-precision X through the two-pass regime at ragged shapes (N not a
+    tile multiple, d not a multiple of the feature tile, K just past a
+    256-component slab), with fp32 products and with the default fp16 splits:
+    statistics, L and every l_n against the oracle, sampled r, and l_n bitwise
+    equal between the two modes. Every row has |x|^2 < 225, so the default
+    mode takes the fp16 splits. The 2^-8 case puts most |x| below 2^-6, where
+    (16 x)^2 no longer splits exactly into two fp16 values."""
+    X, mu, var, logw = datagen.random_problem(7000 + N + d + K, N, d, K)
+    X = (X * scale).astype(np.float32)
+    mu = (mu * scale).astype(np.float32)
+    var = (var * scale * scale).astype(np.float32)
+    Xd, Xv = _xdev(X, "f16")
+    assert (Xv.astype(np.float64) ** 2).sum(axis=1).max() < 225.0
+    if scale < 0.01:
+        assert (np.abs(Xv) < 2.0 ** -6).mean() > 0.5
+    _check_case(G, Xd, Xv, mu, var, logw, 2, f"fp16 two-pass N={N} d={d} K={K} scale={scale}", 0,
+                split=(False, "auto"))
+    # the default mode took the fp16 splits (not its fp32 twin): its products differ
+    args = (Xd, dev(mu), dev(var), dev(logw))
+    G.set_stats_precision(G.STATS_AUTO)
+    a = G.estep_stats(*args, regime=2)
+    G.set_stats_precision(G.STATS_FP32)
+    b = G.estep_stats(*args, regime=2)
+    torch.cuda.synchronize()
+    assert not torch.equal(a[2], b[2]), "fp16 X in range: the default mode gave the fp32 products"
