@@ -32,9 +32,15 @@ def _same(a, b, what):
         assert torch.equal(a[i], b[i]), f"{what}: {key} differs from gmm_estep_stats"
 
 
-def test_static_matches_workspace_entry_point_on_successive_calls():
-    from soft_clustering_gmm_amd import gmm
-    gmm.lib()
+@pytest.fixture()
+def gmm():
+    from soft_clustering_gmm_amd import gmm as g
+    g.lib()
+    yield g
+    g.set_stats_precision(g.STATS_AUTO)  # the library's default
+
+
+def test_static_matches_workspace_entry_point_on_successive_calls(gmm):
     gmm.set_stats_precision(gmm.STATS_FP32)
     cases = [("ref", 300_000), ("ref", 70_001), ("smallk", 100_003)]
     for i, (name, N) in enumerate(cases):
@@ -58,3 +64,30 @@ def test_static_matches_workspace_entry_point_on_successive_calls():
     w = gmm.estep_stats(*args, want_point_loglik=True)
     torch.cuda.synchronize()
     _same(s, w, "tiny after the larger calls")
+
+
+def test_static_half_precision_two_pass_range_flag_is_reset(gmm):
+    """Half-precision X in the two-pass regime, default statistics mode: the
+    device flag that picks the fp16-split or the fp32 second pass lives in the
+    static scratch. A first call whose rows reach |x|^2 >= 225 sets it; the
+    second, smaller call is in range and must clear it, so that both match
+    gmm_estep_stats (which takes its own flag) bit for bit."""
+    gmm.set_stats_precision(gmm.STATS_AUTO)
+    X, mu, var, logw = datagen.make_workload("ivf", N=20_000)
+    big = ((X.astype(np.float32) * 20.0).astype(np.float16), (mu * 20.0).astype(np.float32),
+           (var * 400.0).astype(np.float32))
+    assert (big[0].astype(np.float64) ** 2).sum(axis=1).max() >= 225.0
+    Xs = X[:9_001]
+    assert (Xs.astype(np.float64) ** 2).sum(axis=1).max() < 225.0
+    for what, (Xc, muc, varc) in (("out of range", big), ("in range", (Xs, mu, var))):
+        info = gmm.plan_info(*Xc.shape, muc.shape[0])
+        print(f"{what}: fp16 N={Xc.shape[0]} plan {info}", flush=True)
+        assert info["regime"] == 2
+        args = (dev(Xc), dev(muc), dev(varc), dev(logw))
+        s = gmm.estep_stats_static(*args, want_point_loglik=True)
+        w = gmm.estep_stats(*args, want_point_loglik=True)
+        torch.cuda.synchronize()
+        _same(s, w, f"fp16 two-pass, {what}")
+    ref = oracle.estep(Xs.astype(np.float32), mu, var, logw, form="expanded", abs_x=True)
+    parity.check_stats((host(s[0]), host(s[1]), host(s[2])), ref, None, ref["absx"], "static fp16 in range")
+    parity.check_loglik_point(host(s[4]), ref["l"], "static fp16 in range")
