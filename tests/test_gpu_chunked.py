@@ -111,3 +111,17 @@ def test_chunked_bfloat16_host_x(G):
     X64 = Xv.astype(np.float64)
     parity.check_stats((host(Nk), host(Sx), host(Sxx)), ref, X64, ref["R"].T @ np.abs(X64), "chunked bf16")
     parity.check_total(host(L), ref, "chunked bf16")
+
+
+def test_chunked_half_x_mixed_range_chunks(G):
+    """Half-precision X whose last chunk leaves the fp16 split's range (rows
+    scaled by 20, |x|^2 = 400): the chunks in range take the fp16-split
+    statistics, the last one the fp32 products. l_n still matches the
+    device-resident call (which takes fp32 products for every row) bit for
+    bit, and the statistics meet the oracle."""
+    X, mu, var, logw = datagen.make_workload("ivf", N=3000)
+    X = X.copy()
+    X[2000:] = (X[2000:].astype(np.float32) * 20.0).astype(np.float16)
+    sq = (X.astype(np.float64) ** 2).sum(axis=1)
+    assert sq[:2000].max() < 225.0 <= sq[2000:].min()
+    _check(G, X, mu, var, logw, 1000, True, "ivf fp16 mixed-range chunks")
