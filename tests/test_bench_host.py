@@ -1,5 +1,5 @@
-"""Host logic of bench.py that needs no GPU: the warm-up rule and the refusal
-of more than one GPU."""
+"""Host logic of bench.py that needs no GPU: the warm-up rule, the refusal
+of more than one GPU and the check of --rows."""
 import argparse
 import types
 
@@ -57,3 +57,9 @@ def test_default_warmup_runs_at_least_three_long_steps(monkeypatch):
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_rows_below_the_component_count_are_refused(capsys):
+    # the recipes draw their initial means from K distinct rows
+    assert bench.main(["--rows", "5", "--workload", "ref"]) == 2
+    assert "--rows" in capsys.readouterr().err
